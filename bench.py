@@ -1,0 +1,299 @@
+"""Benchmark of the fused reduce + norm boundary on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--all] [--no-cpu]
+
+One step is one call of the whole fused path on the headline workload: the
+sandwich boundary (FP32 sum of R=4 BF16 partials -> RMSNorm(gamma1) ->
++residual -> RMSNorm(gamma2)) at H=5120, T=4096 tokens, inputs resident in
+HBM.  Consecutive steps rotate over input/output sets totalling more than
+1 GiB so that the 256 MB Infinity Cache cannot serve them.
+
+Printed: ONE JSON line with the contract fields plus
+  * ``roofline``: the fused kernel's achieved algorithmic GB/s (bytes per
+    launch / average launch time from HIP events on the launch stream)
+    against MI355X's 8 TB/s HBM peak, and the HBM traffic measured with
+    rocprofv3 counters when the stored counter summary matches the current
+    kernel source;
+  * ``sweep``: µs/call and GB/s over T = 1..4096 at H=5120 (R=4) and H=8192
+    (R=8), each the median of 5 replays of a HIP graph holding 20 calls (the
+    measuring method of the pages' microbenchmark table, vLLM PR #62366);
+  * ``cpu_baseline``: the CPU oracle timed on the host cores on a bounded
+    sample of the same workload.
+
+The GPU runs one process on one device; ``--gpus N`` with N > 1 exits with a
+message (this build runs on one GPU only).
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "µs/call and achieved HBM GB/s (% of peak) vs tokens T at H=5120/8192"
+PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+HEADLINE = (2, 4096)       # sandwich H=5120 R=4, T=4096
+SWEEP_T = (1, 8, 64, 256, 1024, 4096)
+COLD_BYTES = 1 << 30       # rotate inputs over > 1 GiB where bandwidth is measured
+
+
+def kernel_source_digest() -> str:
+    """SHA-256 over the kernel sources and build flags: counter data taken
+    for another version of the kernels is not reported."""
+    from tp_reduction_rmsnorm_amd import build as B
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(B.CSRC, "*"))):
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode())
+            h.update(fh.read())
+    with open(os.path.join(ROOT, "include", "fused_reduce_norm.h"), "rb") as fh:
+        h.update(fh.read())
+    h.update(" ".join(B.FLAGS).encode())
+    return h.hexdigest()
+
+
+def stored_traffic(workload: str, T: int, digest: str):
+    """HBM bytes per launch from profiles/traffic_<workload>_T<T>.md, or None
+    when the file is missing or was measured on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}_T{T}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    f = re.search(r"fetch_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    w = re.search(r"write_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not (m and f and w) or m.group(1) != digest:
+        return None
+    return float(f.group(1)) + float(w.group(1))
+
+
+class Runner:
+    """Rotating input/output sets of one workload and the fused call on them."""
+
+    def __init__(self, cid, T, dev, cold=True, split=False):
+        import torch
+        import tp_reduction_rmsnorm_amd as frn
+        import workloads
+        self.frn, self.torch = frn, torch
+        self.w = workloads.WORKLOADS[cid]
+        self.T = T
+        self.split = split
+        w = self.w
+        self.bytes = workloads.algorithmic_bytes(w.R, T, w.H, epilogue=w.epilogue, k=w.k,
+                                                 shared=w.shared)
+        n = max(1, min(32, -(-COLD_BYTES // self.bytes))) if cold else 1
+        self.sets = [workloads.make_workload(cid, T, device=dev, salt=i) for i in range(n)]
+        self.outs = [(torch.empty(T, w.H, dtype=torch.bfloat16, device=dev),
+                      torch.empty(T, w.H, dtype=torch.bfloat16, device=dev)) for _ in range(n)]
+        self.scratch = torch.empty(T, w.H, dtype=torch.bfloat16, device=dev) if split else None
+        self.epi = frn.EPI_SANDWICH if w.epilogue == "sandwich" else frn.EPI_RMSNORM
+
+    def call(self, i):
+        d = self.sets[i % len(self.sets)]
+        o, r = self.outs[i % len(self.outs)]
+        f = self.frn
+        if self.split:
+            return f.split_reduce_norm(d.sources, d.residual, d.gamma1, d.gamma2, d.eps,
+                                       topk_weights=d.topk_w if d.k else None,
+                                       topk_rows=d.topk_idx if d.k else None,
+                                       shared=d.shared if d.k else None, epilogue=self.epi,
+                                       scratch=self.scratch, out=o, residual_out=r)
+        if d.k:
+            return f.moe_finalize_reduce_norm(d.expert_rows, d.topk_w, d.topk_idx, d.residual,
+                                              d.gamma1, d.gamma2, d.eps, shared=d.shared,
+                                              epilogue=self.epi, out=o, residual_out=r)
+        if self.epi == f.EPI_SANDWICH:
+            return f.reduce_sandwich_norm(d.partials, d.residual, d.gamma1, d.gamma2, d.eps,
+                                          out=o, residual_out=r)
+        return f.reduce_residual_rmsnorm(d.partials, d.residual, d.gamma1, d.eps,
+                                         out=o, residual_out=r)
+
+    def graph_us(self, calls=20, replays=5, warm=3):
+        """µs per call: a HIP graph of `calls` calls, median over replays."""
+        torch = self.torch
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for i in range(3):
+                self.call(i)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(calls):
+                self.call(i)
+        for _ in range(warm):
+            g.replay()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(replays):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3 / calls)
+        del g
+        return sorted(ts)[len(ts) // 2]
+
+
+def sweep(dev, cids=(2, 3), Ts=SWEEP_T):
+    rows = []
+    for cid in cids:
+        for T in Ts:
+            r = Runner(cid, T, dev, cold=T >= 256)
+            us = r.graph_us()
+            gbs = r.bytes / us / 1e3
+            rows.append(dict(workload=r.w.name, T=T, us_per_call=round(us, 3),
+                             GBps=round(gbs, 1), frac_of_peak=round(gbs / PEAK_GBS, 4),
+                             cold=len(r.sets) > 1))
+            print(json.dumps(dict(sweep=rows[-1])), file=sys.stderr, flush=True)
+            del r
+    return rows
+
+
+def extra_configs(dev):
+    rows = []
+    for cid, Ts, split in ((1, (8,), False), (4, (1, 2, 4, 8, 16, 32, 64), False),
+                           (5, (4096, 16384), False), (5, (4096, 16384), True)):
+        for T in Ts:
+            r = Runner(cid, T, dev, cold=T >= 256, split=split)
+            us = r.graph_us()
+            rows.append(dict(workload=r.w.name + ("_split" if split else ""), T=T,
+                             us_per_call=round(us, 3), GBps=round(r.bytes / us / 1e3, 1),
+                             frac_of_peak=round(r.bytes / us / 1e3 / PEAK_GBS, 4)))
+            print(json.dumps(dict(extra=rows[-1])), file=sys.stderr, flush=True)
+            del r
+    return rows
+
+
+def cpu_baseline(runner, seconds=10.0):
+    """The CPU oracle, as it is, on a bounded sample of the headline
+    workload (its first 256 token rows), repeated for ~`seconds`."""
+    import oracle
+    import workloads
+    d = runner.sets[0]
+    rows = min(256, runner.T)
+    w = runner.w
+    args = [workloads.bits(p[:rows]) for p in d.partials]
+    kw = dict(residual=workloads.bits(d.residual[:rows]), gamma1=workloads.f32(d.gamma1),
+              gamma2=workloads.f32(d.gamma2), eps=d.eps, epilogue=oracle.EPI_SANDWICH)
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    byts = workloads.algorithmic_bytes(w.R, rows, w.H, epilogue=w.epilogue)
+    oracle.boundary(args, nthreads=cores, **kw)  # warm
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.boundary(args, nthreads=cores, **kw)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    gbs = byts * reps / el / 1e9
+    return dict(value=round(gbs, 3), unit="GB/s", cores=cores, kind="oracle",
+                sample=f"{rows} of {runner.T} token rows of {w.name} (R={w.R}, H={w.H}), "
+                       f"{reps} repetitions in {el:.1f} s, {cores} threads; "
+                       f"{el / reps * 1e6 / rows:.1f} us per row")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--all", action="store_true", help="also time the MoE and split workloads")
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 512 MiB device copy (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    lib = os.path.join(ROOT, "tp_reduction_rmsnorm_amd", "libfused_reduce_norm.so")
+    if not os.path.exists(lib):
+        from tp_reduction_rmsnorm_amd import build as B
+        B.build()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    cid, T = HEADLINE
+    run = Runner(cid, T, dev, cold=True)
+    for i in range(args.warmup):
+        run.call(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        run.call(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_us = e0.elapsed_time(e1) * 1e3 / args.steps  # average launch duration, µs
+    ms_per_step = wall * 1e3 / args.steps
+    value = run.bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = run.bytes / (ev_us * 1e-6) / 1e9
+
+    if args.copy_calibration:
+        n = 512 << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    digest = kernel_source_digest()
+    traffic = stored_traffic(run.w.name, T, digest)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_call": round(ms_per_step * 1e3, 2),
+        "frac_of_peak": round(value / PEAK_GBS, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": run.w.name, "T": T, "H": run.w.H, "R": run.w.R,
+                   "epilogue": run.w.epilogue, "storage": "bf16",
+                   "algorithmic_bytes_per_call": run.bytes,
+                   "rotating_sets": len(run.sets), "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4),
+                     "traffic": traffic, "kernel_us": round(ev_us, 3),
+                     "kernel_source_sha256": digest},
+    }
+    del run
+    torch.cuda.empty_cache()
+    if not args.no_sweep:
+        out["sweep"] = sweep(dev)
+    if args.all:
+        out["other_configs"] = extra_configs(dev)
+    if not args.no_cpu:
+        base = Runner(cid, T, dev, cold=False)
+        out["cpu_baseline"] = cpu_baseline(base)
+        del base
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,205 @@
+/*
+ * fused_reduce_norm.h -- C ABI of the fused reduce + norm boundary for one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the layer boundary of a tensor-parallel transformer: R
+ * BF16 partial-sum tensors [T,H] (one per TP rank) are summed in FP32 and
+ * followed by residual add + RMSNorm, or by the FP32 norm -> residual add ->
+ * norm "sandwich" (vLLM PR #62366, "Overview" and "Claims"; SGLang PR
+ * #34134, first commit message, first fusion pattern).  An optional MoE
+ * top-k finalize -- the weighted sum of each token's k expert output rows
+ * plus a shared-expert row, rounded to BF16 on each rank -- runs ahead of
+ * the reduction (vLLM PR #62366 "Claims"; SGLang PR #34134, second fusion
+ * pattern).  For large batches a two-pass path first reduces to a BF16
+ * tensor and then runs the boundary on it (vLLM PR #62366 "Claims").  All
+ * FP32 arithmetic is uncontracted: no multiply-add is fused into an FMA
+ * (vLLM PR #62366 "Details").
+ *
+ * Here the R rank shares are R buffers resident in the one GPU's HBM.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - BF16 tensors are passed as raw device pointers to row-major [rows, H]
+ *   arrays of 16-bit bfloat16 values, row stride H elements.  FP32 vectors
+ *   (gamma) and top-k weights are float; top-k rows are int32.
+ * - Pointer arrays (partials, expert_rows, shared) are HOST arrays of R
+ *   device pointers; the library copies them into the kernel arguments, so
+ *   the host array may be freed as soon as the call returns.
+ * - Every device pointer must be 16-byte aligned and H must be a multiple
+ *   of 8 (one 128-bit vector holds 8 BF16 values); otherwise the call
+ *   returns FRN_ERR_UNSUPPORTED.  1 <= R <= FRN_MAX_R, 1 <= k <= FRN_MAX_K,
+ *   8 <= H <= FRN_MAX_H.
+ * - stream is a hipStream_t passed as void*; NULL is the null stream.  Calls
+ *   are asynchronous: they enqueue kernels and return.  They never
+ *   synchronize, never read device memory from the host and never allocate,
+ *   so they may be captured into a HIP graph.
+ * - The caller owns every buffer.  The library keeps no per-call state.
+ * - Aliasing: residual_out may be the same pointer as residual_in (the
+ *   residual stream updated in place).  Any other overlap between an
+ *   output and any input or other output is FRN_ERR_INVALID.
+ * - Errors are return codes; nothing is thrown across the ABI.  All
+ *   arguments are checked before anything is launched, so on any error the
+ *   outputs are untouched.  T == 0 returns FRN_OK once the sizes are
+ *   valid, without looking at the pointers and without a launch.
+ *   FRN_ERR_HIP means the launch itself failed; frn_last_error() has text.
+ * - Numerics: per element, the finalize accumulates j = 0..k-1 in order
+ *   (each product and sum one FP32 rounding), adds the shared row last and
+ *   rounds to BF16 (nearest-even); the reduction adds ranks r = 0..R-1 in
+ *   order in FP32; the inverse RMS uses an FP64 sum of the squares, divides
+ *   by H, rounds to FP32, adds eps in FP32 and takes a correctly rounded
+ *   square root and reciprocal; the normalized value is (x * rinv) * gamma.
+ *   Outputs are rounded to BF16, nearest-even.
+ */
+#ifndef FUSED_REDUCE_NORM_H
+#define FUSED_REDUCE_NORM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FRN_VERSION_STRING "0.1.0"
+
+#define FRN_MAX_R 16     /* partials (TP ranks) per call */
+#define FRN_MAX_K 16     /* top-k slots per token */
+#define FRN_MAX_H 16384  /* hidden size */
+
+typedef enum frn_status {
+    FRN_OK = 0,
+    FRN_ERR_INVALID = 1,     /* malformed arguments (null pointer, R < 1, ...) */
+    FRN_ERR_UNSUPPORTED = 2, /* well-formed, but outside what this build serves */
+    FRN_ERR_HIP = 3          /* the HIP launch failed */
+} frn_status;
+
+typedef enum frn_epilogue {
+    FRN_EPI_RMSNORM = 0,  /* residual add + RMSNorm(gamma1) */
+    FRN_EPI_SANDWICH = 1  /* RMSNorm(gamma1) -> residual add -> RMSNorm(gamma2) */
+} frn_epilogue;
+
+/*
+ * Reduce + residual add + RMSNorm (vLLM PR #62366, kernel microbenchmark
+ * table; SGLang PR #34134, first fusion pattern).  Per token row t:
+ *   s = sum_r partials[r][t]          (FP32, r ascending)
+ *   h = s + residual_in[t]            (FP32)
+ *   residual_out[t] = bf16(h)
+ *   out[t] = bf16((h * rinv(h)) * gamma)
+ * partials: R device pointers to [T,H] BF16.  residual_in/out, out: [T,H]
+ * BF16.  gamma: [H] FP32.  eps >= 0, finite.  workspace/workspace_bytes:
+ * optional scratch (NULL/0 allowed); see frn_workspace_bytes.
+ */
+frn_status frn_reduce_residual_rmsnorm(const void* const* partials, int32_t R,
+                                       const void* residual_in, const float* gamma,
+                                       float eps, int64_t T, int64_t H, void* out,
+                                       void* residual_out, void* workspace,
+                                       size_t workspace_bytes, void* stream);
+
+/*
+ * Reduce + Beam's FP32 sandwich norm (vLLM PR #62366, "Overview", "Claims").
+ * Per token row t:
+ *   s = sum_r partials[r][t]           (FP32)
+ *   a = (s * rinv(s)) * gamma1         (FP32, never rounded to BF16)
+ *   h = a + residual_in[t]             (FP32)
+ *   residual_out[t] = bf16(h)
+ *   out[t] = bf16((h * rinv(h)) * gamma2)
+ * Arguments as for frn_reduce_residual_rmsnorm; gamma1, gamma2: [H] FP32.
+ */
+frn_status frn_reduce_sandwich_norm(const void* const* partials, int32_t R,
+                                    const void* residual_in, const float* gamma1,
+                                    const float* gamma2, float eps, int64_t T, int64_t H,
+                                    void* out, void* residual_out, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
+/*
+ * MoE top-k finalize (+ shared expert) folded ahead of the reduction, then
+ * the chosen epilogue (vLLM PR #62366 "Claims": the finalize is deferred
+ * into the fused all-reduce and keeps its per-rank BF16 rounding; SGLang PR
+ * #34134, second fusion pattern: finalize + shared-expert add + all-reduce
+ * + residual + RMSNorm).  Per rank r, token t, element i:
+ *   acc = 0; for j = 0..k-1: acc = acc + topk_w[t,j] * E_r[topk_row[t,j], i]
+ *   if shared: acc = acc + S_r[t, i]
+ *   P_r[t, i] = bf16(acc)
+ * then the epilogue runs on s = sum_r P_r exactly as in the calls above.
+ * expert_rows: R device pointers to [num_rows,H] BF16 (each rank's expert
+ * outputs, one row per (token, slot) in any order).  shared: NULL, or R
+ * device pointers to [T,H] BF16.  topk_w: [T,k] FP32; topk_row: [T,k]
+ * int32, the row of E_r holding token t's j-th expert output; routing is
+ * the same on every rank.  A row index outside [0, num_rows) is never
+ * dereferenced: that slot reads as NaN, so the token's whole output row
+ * becomes NaN (visible, and no memory fault).  epilogue: FRN_EPI_RMSNORM
+ * (gamma1 used, gamma2 ignored and may be NULL) or FRN_EPI_SANDWICH.
+ */
+frn_status frn_moe_finalize_reduce_norm(const void* const* expert_rows,
+                                        const void* const* shared, int32_t R,
+                                        const float* topk_w, const int32_t* topk_row,
+                                        int32_t k, int64_t num_rows, int32_t epilogue,
+                                        const void* residual_in, const float* gamma1,
+                                        const float* gamma2, float eps, int64_t T,
+                                        int64_t H, void* out, void* residual_out,
+                                        void* workspace, size_t workspace_bytes,
+                                        void* stream);
+
+/*
+ * Split path, pass 1 (vLLM PR #62366 "Claims": for large batches the
+ * all-reduce alone produces a BF16 tensor): sum_out[t] = bf16(sum_r
+ * partials[r][t]).  sum_out: [T,H] BF16.  Pass 2 is
+ * frn_reduce_residual_rmsnorm / frn_reduce_sandwich_norm with R = 1 and
+ * partials = {sum_out}.
+ */
+frn_status frn_reduce_bf16(const void* const* partials, int32_t R, int64_t T, int64_t H,
+                           void* sum_out, void* stream);
+
+/* Split path, pass 1 with the finalize folded in: sum_out[t] =
+ * bf16(sum_r P_r[t]), P_r as in frn_moe_finalize_reduce_norm. */
+frn_status frn_moe_finalize_reduce_bf16(const void* const* expert_rows,
+                                        const void* const* shared, int32_t R,
+                                        const float* topk_w, const int32_t* topk_row,
+                                        int32_t k, int64_t num_rows, int64_t T, int64_t H,
+                                        void* sum_out, void* stream);
+
+/*
+ * Both passes of the split path on one stream (vLLM PR #62366 "Claims":
+ * two-shot reduction to BF16, then the boundary kernel).  k == 0: src holds
+ * R partials [T,H] and shared/topk_w/topk_row are ignored; k > 0: src holds
+ * R expert-row buffers [num_rows,H] as in frn_moe_finalize_reduce_norm.
+ * scratch: caller-owned [T,H] BF16 device buffer for the pass-1 tensor; it
+ * must not overlap any other argument.
+ */
+frn_status frn_split_reduce_norm(const void* const* src, const void* const* shared,
+                                 int32_t R, const float* topk_w, const int32_t* topk_row,
+                                 int32_t k, int64_t num_rows, int32_t epilogue,
+                                 const void* residual_in, const float* gamma1,
+                                 const float* gamma2, float eps, int64_t T, int64_t H,
+                                 void* scratch, void* out, void* residual_out, void* stream);
+
+/*
+ * Capability check without launching anything: FRN_OK if a call with these
+ * sizes is served, FRN_ERR_UNSUPPORTED if it would be declined, and
+ * FRN_ERR_INVALID for malformed sizes (the analogue of a workspace factory
+ * that returns nothing for unsupported shapes, vLLM PR #62366 "Details").
+ * k == 0 means no finalize.  Setting the environment variable
+ * FRN_FORCE_DECLINE=1 before the first call makes every entry point return
+ * FRN_ERR_UNSUPPORTED (for testing callers' fallback paths).
+ */
+frn_status frn_query(int32_t R, int32_t k, int64_t T, int64_t H, int32_t epilogue);
+
+/* Bytes of optional workspace that lets calls up to max_T tokens use the
+ * split-row kernels for small T.  0 means no workspace is ever used. */
+size_t frn_workspace_bytes(int64_t max_T, int64_t H, int32_t R, int32_t k);
+
+/* Static text for a status code. */
+const char* frn_status_string(frn_status s);
+
+/* Text describing the last error returned on the calling thread ("" if
+ * none).  Valid until the next call on that thread. */
+const char* frn_last_error(void);
+
+/* Library version, FRN_VERSION_STRING. */
+const char* frn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FUSED_REDUCE_NORM_H */

@@ -19,3 +19,17 @@ def pytest_runtest_setup(item):
         import torch
         if not torch.cuda.is_available():
             pytest.fail("GPU test selected but no GPU is visible", pytrace=False)
+
+
+def pytest_terminal_summary(terminalreporter):
+    try:
+        from tests import parity
+    except Exception:
+        return
+    if not parity.REPORT:
+        return
+    terminalreporter.section("GPU vs oracle parity (BF16 ulp)")
+    for s in parity.REPORT:
+        terminalreporter.write_line(
+            f"{s['case']:<58} n={s['n']:>10} max_ulp={s['max_ulp']} "
+            f"1ulp={s['n_1ulp']} >1ulp={s['n_over']} max_abs={s['max_abs']:.3g}")

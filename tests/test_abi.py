@@ -1,0 +1,262 @@
+"""The C ABI on the CPU: the library loads, exports every entry point the
+header declares, and rejects bad arguments before launching anything.
+
+No call here reaches a kernel launch: every call is either rejected by the
+argument checks or has T == 0 (which returns before any HIP call).  The
+pointers are fake, 16-byte-aligned integers; the library never dereferences
+host-side device pointers.
+"""
+import ctypes
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fused_reduce_norm.h")
+LIB = os.path.join(ROOT, "tp_reduction_rmsnorm_amd", "libfused_reduce_norm.so")
+
+OK, INVALID, UNSUPPORTED, HIP = 0, 1, 2, 3
+P = ctypes.c_void_p
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from tp_reduction_rmsnorm_amd import build
+        build.build()
+    L = ctypes.CDLL(LIB)
+    L.frn_reduce_residual_rmsnorm.argtypes = [P, ctypes.c_int32, P, P, ctypes.c_float,
+                                              ctypes.c_int64, ctypes.c_int64, P, P, P,
+                                              ctypes.c_size_t, P]
+    L.frn_reduce_sandwich_norm.argtypes = [P, ctypes.c_int32, P, P, P, ctypes.c_float,
+                                           ctypes.c_int64, ctypes.c_int64, P, P, P,
+                                           ctypes.c_size_t, P]
+    L.frn_moe_finalize_reduce_norm.argtypes = [P, P, ctypes.c_int32, P, P, ctypes.c_int32,
+                                               ctypes.c_int64, ctypes.c_int32, P, P, P,
+                                               ctypes.c_float, ctypes.c_int64, ctypes.c_int64,
+                                               P, P, P, ctypes.c_size_t, P]
+    L.frn_reduce_bf16.argtypes = [P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, P, P]
+    L.frn_split_reduce_norm.argtypes = [P, P, ctypes.c_int32, P, P, ctypes.c_int32,
+                                        ctypes.c_int64, ctypes.c_int32, P, P, P, ctypes.c_float,
+                                        ctypes.c_int64, ctypes.c_int64, P, P, P, P]
+    L.frn_query.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
+                            ctypes.c_int32]
+    L.frn_status_string.restype = ctypes.c_char_p
+    L.frn_last_error.restype = ctypes.c_char_p
+    L.frn_version.restype = ctypes.c_char_p
+    L.frn_workspace_bytes.restype = ctypes.c_size_t
+    L.frn_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                                      ctypes.c_int32]
+    return L
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const char\*|frn_status|size_t)\s+(frn_\w+)\(",
+                                 text, re.M)))
+
+
+def test_header_declares_the_boundary_calls():
+    names = declared_functions()
+    for want in ("frn_reduce_residual_rmsnorm", "frn_reduce_sandwich_norm",
+                 "frn_moe_finalize_reduce_norm", "frn_reduce_bf16",
+                 "frn_moe_finalize_reduce_bf16", "frn_split_reduce_norm", "frn_query",
+                 "frn_workspace_bytes", "frn_status_string", "frn_last_error", "frn_version"):
+        assert want in names
+
+
+def test_library_exports_exactly_the_declared_symbols():
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True,
+                         check=True).stdout
+    exported = sorted({l.split()[-1] for l in out.splitlines() if " T " in l and
+                       l.split()[-1].startswith("frn_")})
+    assert exported == declared_functions()
+
+
+def test_every_declared_symbol_resolves(lib):
+    for name in declared_functions():
+        assert getattr(lib, name) is not None
+
+
+def test_python_binding_names_match_the_c_entry_points():
+    import tp_reduction_rmsnorm_amd as frn
+    assert sorted(frn.C_FUNCTIONS) == declared_functions()
+    for name in frn.C_FUNCTIONS:
+        if name not in ("frn_status_string", "frn_last_error"):
+            assert hasattr(frn, name[len("frn_"):]), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.frn_version() == b"0.1.0"
+    for s in (OK, INVALID, UNSUPPORTED, HIP):
+        assert lib.frn_status_string(s).startswith(b"FRN_")
+
+
+# fake device addresses, 16-byte aligned and far apart
+BASE = 1 << 40
+def addr(i, off=0):
+    return BASE + i * (1 << 32) + off
+
+
+def ptrs(*xs):
+    return ctypes.cast((ctypes.c_void_p * len(xs))(*xs), P)
+
+
+def call_rms(lib, R=2, T=4, H=64, eps=1e-6, parts=None, residual=None, gamma=None,
+             out=None, rout=None):
+    parts = ptrs(*[addr(10 + r) for r in range(R)]) if parts is None else parts
+    return lib.frn_reduce_residual_rmsnorm(
+        parts, R, addr(1) if residual is None else residual, addr(2) if gamma is None else gamma,
+        eps, T, H, addr(3) if out is None else out, addr(4) if rout is None else rout,
+        None, 0, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(R=0), INVALID),
+    (dict(R=17), UNSUPPORTED),
+    (dict(T=-1), INVALID),
+    (dict(H=0), INVALID),
+    (dict(H=12), UNSUPPORTED),
+    (dict(H=16392), UNSUPPORTED),
+    (dict(eps=float("nan")), INVALID),
+    (dict(eps=-1e-6), INVALID),
+    (dict(eps=float("inf")), INVALID),
+    (dict(residual=0), INVALID),
+    (dict(gamma=0), INVALID),
+    (dict(out=0), INVALID),
+    (dict(rout=0), INVALID),
+    (dict(out=addr(3, 8)), UNSUPPORTED),          # 8-byte aligned only
+    (dict(gamma=addr(2, 4)), UNSUPPORTED),
+    (dict(out=addr(10, 64)), INVALID),            # out overlaps partial 0
+    (dict(rout=addr(3, 128)), INVALID),           # residual_out overlaps out
+    (dict(out=addr(1)), INVALID),                 # out aliases residual_in
+])
+def test_rmsnorm_rejects(lib, kw, status):
+    assert call_rms(lib, **kw) == status
+    assert lib.frn_last_error() != b""
+
+
+def test_null_partial_and_misaligned_partial(lib):
+    assert call_rms(lib, parts=ptrs(addr(10), 0)) == INVALID
+    assert call_rms(lib, parts=ptrs(addr(10), addr(11, 2))) == UNSUPPORTED
+    assert lib.frn_reduce_residual_rmsnorm(None, 2, addr(1), addr(2), 1e-6, 4, 64, addr(3),
+                                           addr(4), None, 0, None) == INVALID
+
+
+def test_zero_tokens_is_a_no_op(lib):
+    # T == 0 returns before any HIP call, so this is safe without a GPU
+    assert call_rms(lib, T=0) == OK
+    assert lib.frn_last_error() == b""
+
+
+def test_sandwich_needs_gamma2(lib):
+    parts = ptrs(addr(10), addr(11))
+    st = lib.frn_reduce_sandwich_norm(parts, 2, addr(1), addr(2), None, 1e-6, 4, 64, addr(3),
+                                      addr(4), None, 0, None)
+    assert st == INVALID
+
+
+def call_moe(lib, R=2, k=3, T=4, H=64, num_rows=12, epilogue=0, shared=True, w=None, rows=None):
+    src = ptrs(*[addr(10 + r) for r in range(R)])
+    sh = ptrs(*[addr(30 + r) for r in range(R)]) if shared else None
+    return lib.frn_moe_finalize_reduce_norm(
+        src, sh, R, addr(5) if w is None else w, addr(6) if rows is None else rows, k, num_rows,
+        epilogue, addr(1), addr(2), addr(7), 1e-6, T, H, addr(3), addr(4), None, 0, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=0), INVALID),
+    (dict(k=17), UNSUPPORTED),
+    (dict(num_rows=0), INVALID),
+    (dict(epilogue=7), INVALID),
+    (dict(w=0), INVALID),
+    (dict(rows=0), INVALID),
+    (dict(rows=addr(6, 2)), UNSUPPORTED),
+    (dict(w=addr(3)), INVALID),   # out overlaps the weights
+])
+def test_moe_rejects(lib, kw, status):
+    assert call_moe(lib, **kw) == status
+
+
+def test_moe_zero_tokens_is_a_no_op(lib):
+    assert call_moe(lib, T=0) == OK
+
+
+def test_split_scratch_must_not_alias(lib):
+    src = ptrs(addr(10), addr(11))
+    st = lib.frn_split_reduce_norm(src, None, 2, None, None, 0, 0, 0, addr(1), addr(2), None,
+                                   1e-6, 4, 64, addr(3), addr(3), addr(4), None)
+    assert st == INVALID
+    st = lib.frn_split_reduce_norm(src, None, 2, None, None, 0, 0, 0, addr(1), addr(2), None,
+                                   1e-6, 4, 64, addr(11), addr(3), addr(4), None)
+    assert st == INVALID
+    st = lib.frn_split_reduce_norm(src, None, 2, None, None, 0, 0, 0, addr(1), addr(2), None,
+                                   1e-6, 0, 64, addr(20), addr(3), addr(4), None)
+    assert st == OK
+
+
+def test_pass1_rejects(lib):
+    src = ptrs(addr(10), addr(11))
+    assert lib.frn_reduce_bf16(src, 2, 4, 64, 0, None) == INVALID
+    assert lib.frn_reduce_bf16(src, 2, 4, 64, addr(10, 16), None) == INVALID
+    assert lib.frn_reduce_bf16(src, 2, 0, 64, addr(20), None) == OK
+
+
+def test_query(lib):
+    assert lib.frn_query(4, 0, 1024, 5120, 1) == OK
+    assert lib.frn_query(8, 10, 64, 6144, 0) == OK
+    assert lib.frn_query(2, 8, 16384, 7168, 0) == OK
+    assert lib.frn_query(4, 0, 1024, 5124, 1) == UNSUPPORTED
+    assert lib.frn_query(0, 0, 1024, 5120, 1) == INVALID
+    assert lib.frn_query(20, 0, 1024, 5120, 1) == UNSUPPORTED
+    assert lib.frn_query(4, 0, 1 << 31, 5120, 1) == UNSUPPORTED
+
+
+DECLINE_SCRIPT = r"""
+import ctypes, sys
+sys.path.insert(0, {root!r})
+L = ctypes.CDLL({lib!r})
+L.frn_query.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32]
+assert L.frn_query(4, 0, 1024, 5120, 1) == 2
+import tp_reduction_rmsnorm_amd as frn
+assert frn.query(4, 0, 1024, 5120, 1) is False
+print("declined")
+"""
+
+
+def test_forced_decline_env():
+    code = DECLINE_SCRIPT.format(root=ROOT, lib=LIB)
+    env = dict(os.environ, FRN_FORCE_DECLINE="1")
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 0, r.stderr
+    assert "declined" in r.stdout
+
+
+def test_python_layer_raises_on_decline_and_never_returns_inputs(monkeypatch):
+    """The binding turns FRN_ERR_UNSUPPORTED into an exception (it cannot
+    hand back unreduced data), using a stand-in for the C call."""
+    import tp_reduction_rmsnorm_amd as frn
+    with pytest.raises(frn.FusedReduceNormUnsupported):
+        frn._check(UNSUPPORTED)
+    with pytest.raises(ValueError):
+        frn._check(INVALID)
+    with pytest.raises(frn.FusedReduceNormError):
+        frn._check(HIP)
+    frn._check(OK)
+
+
+def test_python_layer_requires_gpu_tensors():
+    import torch
+    import tp_reduction_rmsnorm_amd as frn
+    p = torch.zeros(4, 64, dtype=torch.bfloat16)
+    g = torch.ones(64)
+    with pytest.raises(ValueError, match="GPU"):
+        frn.reduce_residual_rmsnorm([p, p], p, g)
+    with pytest.raises(ValueError, match="residual is required"):
+        frn.reduce_residual_rmsnorm([p, p], None, g)
+    with pytest.raises(TypeError):
+        frn.reduce_residual_rmsnorm([p.float()], p, g)

@@ -1,0 +1,371 @@
+"""Python binding of the fused reduce + norm boundary for MI355X (gfx950).
+
+A thin ctypes layer over ``libfused_reduce_norm.so`` (the C ABI declared in
+``include/fused_reduce_norm.h``).  It only checks tensor dtypes, devices and
+layouts, passes raw device pointers and the current HIP stream, and turns
+status codes into exceptions.  Every step of the computation runs in the
+library's HIP kernels; there is no CPU or PyTorch fallback.  If the library
+is missing the import fails.
+
+Function names are the C entry points without their ``frn_`` prefix:
+
+* ``reduce_residual_rmsnorm``    FP32 sum of R BF16 partials + residual + RMSNorm
+* ``reduce_sandwich_norm``       FP32 sum + norm(gamma1) + residual + norm(gamma2)
+* ``moe_finalize_reduce_norm``   top-k finalize (+ shared expert) per rank,
+                                 rounded to BF16, then either epilogue
+* ``reduce_bf16``, ``moe_finalize_reduce_bf16``  split path, pass 1
+* ``split_reduce_norm``          both passes of the split path
+* ``query``, ``workspace_bytes``, ``version``
+
+Every call returns its outputs.  A declined call raises
+``FusedReduceNormUnsupported``; it never returns unreduced data.  (The pages
+record a bug where a declined fused call silently skipped the owed
+reduction: SGLang PR #34134, second commit message.)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple, Union
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfused_reduce_norm.so")
+
+FRN_OK = 0
+FRN_ERR_INVALID = 1
+FRN_ERR_UNSUPPORTED = 2
+FRN_ERR_HIP = 3
+EPI_RMSNORM = 0
+EPI_SANDWICH = 1
+MAX_R = 16
+MAX_K = 16
+MAX_H = 16384
+
+
+class FusedReduceNormError(RuntimeError):
+    """The library returned FRN_ERR_HIP."""
+
+
+class FusedReduceNormUnsupported(RuntimeError):
+    """The call is outside what the library serves (FRN_ERR_UNSUPPORTED).
+    The caller must take another path that still performs the reduction."""
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -m tp_reduction_rmsnorm_amd.build` "
+        "(or __graft_entry__.build()); there is no fallback path")
+
+_lib = ctypes.CDLL(LIB_PATH)
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_F32 = ctypes.c_float
+_SZ = ctypes.c_size_t
+
+
+def _sig(name, res, args):
+    f = getattr(_lib, name)
+    f.restype = res
+    f.argtypes = args
+    return f
+
+
+_c_rms = _sig("frn_reduce_residual_rmsnorm", ctypes.c_int,
+              [_P, _I32, _P, _P, _F32, _I64, _I64, _P, _P, _P, _SZ, _P])
+_c_sandwich = _sig("frn_reduce_sandwich_norm", ctypes.c_int,
+                   [_P, _I32, _P, _P, _P, _F32, _I64, _I64, _P, _P, _P, _SZ, _P])
+_c_moe = _sig("frn_moe_finalize_reduce_norm", ctypes.c_int,
+              [_P, _P, _I32, _P, _P, _I32, _I64, _I32, _P, _P, _P, _F32, _I64, _I64,
+               _P, _P, _P, _SZ, _P])
+_c_reduce_bf16 = _sig("frn_reduce_bf16", ctypes.c_int, [_P, _I32, _I64, _I64, _P, _P])
+_c_moe_bf16 = _sig("frn_moe_finalize_reduce_bf16", ctypes.c_int,
+                   [_P, _P, _I32, _P, _P, _I32, _I64, _I64, _I64, _P, _P])
+_c_split = _sig("frn_split_reduce_norm", ctypes.c_int,
+                [_P, _P, _I32, _P, _P, _I32, _I64, _I32, _P, _P, _P, _F32, _I64, _I64,
+                 _P, _P, _P, _P])
+_c_query = _sig("frn_query", ctypes.c_int, [_I32, _I32, _I64, _I64, _I32])
+_c_ws = _sig("frn_workspace_bytes", _SZ, [_I64, _I64, _I32, _I32])
+_c_status = _sig("frn_status_string", ctypes.c_char_p, [ctypes.c_int])
+_c_last = _sig("frn_last_error", ctypes.c_char_p, [])
+_c_version = _sig("frn_version", ctypes.c_char_p, [])
+
+C_FUNCTIONS = ("frn_reduce_residual_rmsnorm", "frn_reduce_sandwich_norm",
+               "frn_moe_finalize_reduce_norm", "frn_reduce_bf16",
+               "frn_moe_finalize_reduce_bf16", "frn_split_reduce_norm", "frn_query",
+               "frn_workspace_bytes", "frn_status_string", "frn_last_error", "frn_version")
+
+
+def version() -> str:
+    return _c_version().decode()
+
+
+def _check(status: int) -> None:
+    if status == FRN_OK:
+        return
+    text = _c_last().decode() or _c_status(status).decode()
+    if status == FRN_ERR_UNSUPPORTED:
+        raise FusedReduceNormUnsupported(text)
+    if status == FRN_ERR_INVALID:
+        raise ValueError(text)
+    raise FusedReduceNormError(text)
+
+
+def query(R: int, k: int, T: int, H: int, epilogue: int = EPI_RMSNORM) -> bool:
+    """True if a call with these sizes is served (no launch)."""
+    st = _c_query(R, k, T, H, epilogue)
+    if st == FRN_ERR_INVALID:
+        _check(st)
+    return st == FRN_OK
+
+
+def workspace_bytes(max_T: int, H: int, R: int, k: int = 0) -> int:
+    return int(_c_ws(max_T, H, R, k))
+
+
+# ---------------------------------------------------------------- helpers --- #
+
+TensorList = Union[torch.Tensor, Sequence[torch.Tensor]]
+
+
+def _as_list(x: TensorList, what: str):
+    if isinstance(x, torch.Tensor):
+        if x.dim() != 3:
+            raise ValueError(f"{what}: a stacked tensor must be [R, rows, H]")
+        return list(x.unbind(0))
+    return list(x)
+
+
+def _need(t: torch.Tensor, what: str, dtype, dim: int, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{what} must be {dtype} (got {t.dtype})")
+    if t.dim() != dim:
+        raise ValueError(f"{what} must have {dim} dims (got {tuple(t.shape)})")
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be on the GPU")
+    if device is not None and t.device != device:
+        raise ValueError(f"{what} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+
+
+def _ptr_array(ts):
+    return (ctypes.c_void_p * len(ts))(*[t.data_ptr() for t in ts])
+
+
+def _stream(stream, device) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _outputs(T, H, device, out, residual_out):
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=device)
+    else:
+        _need(out, "out", torch.bfloat16, 2, device)
+    if residual_out is None:
+        residual_out = torch.empty((T, H), dtype=torch.bfloat16, device=device)
+    else:
+        _need(residual_out, "residual_out", torch.bfloat16, 2, device)
+    if tuple(out.shape) != (T, H) or tuple(residual_out.shape) != (T, H):
+        raise ValueError("out and residual_out must be [T, H]")
+    return out, residual_out
+
+
+def _workspace(workspace):
+    if workspace is None:
+        return None, 0
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
+def _check_partials(partials: TensorList, residual: Optional[torch.Tensor]):
+    ps = _as_list(partials, "partials")
+    if not ps:
+        raise ValueError("need at least one partial")
+    device = ps[0].device
+    for i, p in enumerate(ps):
+        _need(p, f"partials[{i}]", torch.bfloat16, 2, device)
+        if p.shape != ps[0].shape:
+            raise ValueError("all partials must have the same [T, H] shape")
+    T, H = ps[0].shape
+    if residual is not None:
+        _need(residual, "residual", torch.bfloat16, 2, device)
+        if tuple(residual.shape) != (T, H):
+            raise ValueError("residual must be [T, H] like the partials")
+    return ps, T, H, device
+
+
+def _check_gamma(g, H, device, what):
+    _need(g, what, torch.float32, 1, device)
+    if g.shape[0] != H:
+        raise ValueError(f"{what} must have H={H} entries")
+
+
+def _check_finalize(expert_rows, topk_weights, topk_rows, shared):
+    es = _as_list(expert_rows, "expert_rows")
+    if not es:
+        raise ValueError("need at least one expert-row buffer")
+    device = es[0].device
+    for i, e in enumerate(es):
+        _need(e, f"expert_rows[{i}]", torch.bfloat16, 2, device)
+        if e.shape != es[0].shape:
+            raise ValueError("all expert-row buffers must have the same shape")
+    num_rows, H = es[0].shape
+    _need(topk_weights, "topk_weights", torch.float32, 2, device)
+    _need(topk_rows, "topk_rows", torch.int32, 2, device)
+    T, k = topk_weights.shape
+    if tuple(topk_rows.shape) != (T, k):
+        raise ValueError("topk_rows must have the shape of topk_weights [T, k]")
+    sh = None
+    if shared is not None:
+        sh = _as_list(shared, "shared")
+        if len(sh) != len(es):
+            raise ValueError("shared must give one [T, H] tensor per rank")
+        for i, s in enumerate(sh):
+            _need(s, f"shared[{i}]", torch.bfloat16, 2, device)
+            if tuple(s.shape) != (T, H):
+                raise ValueError("shared tensors must be [T, H]")
+    return es, sh, T, H, k, num_rows, device
+
+
+# ------------------------------------------------------------- entry points --- #
+
+def reduce_residual_rmsnorm(partials: TensorList, residual: torch.Tensor, gamma: torch.Tensor,
+                            eps: float = 1e-6, *, out=None, residual_out=None,
+                            workspace=None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """h = sum(partials) + residual (FP32); returns (bf16(norm(h) * gamma), bf16(h)).
+    Pass ``residual_out=residual`` to update the residual stream in place."""
+    if residual is None:
+        raise ValueError("residual is required: this boundary always adds the residual")
+    ps, T, H, device = _check_partials(partials, residual)
+    _check_gamma(gamma, H, device, "gamma")
+    out, residual_out = _outputs(T, H, device, out, residual_out)
+    ws, wsb = _workspace(workspace)
+    arr = _ptr_array(ps)
+    _check(_c_rms(ctypes.cast(arr, _P), len(ps), residual.data_ptr(), gamma.data_ptr(), eps,
+                  T, H, out.data_ptr(), residual_out.data_ptr(), ws, wsb, _stream(stream, device)))
+    return out, residual_out
+
+
+def reduce_sandwich_norm(partials: TensorList, residual: torch.Tensor, gamma1: torch.Tensor,
+                         gamma2: torch.Tensor, eps: float = 1e-6, *, out=None,
+                         residual_out=None, workspace=None,
+                         stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """a = norm(sum(partials)) * gamma1; h = a + residual (FP32);
+    returns (bf16(norm(h) * gamma2), bf16(h))."""
+    if residual is None:
+        raise ValueError("residual is required: this boundary always adds the residual")
+    ps, T, H, device = _check_partials(partials, residual)
+    _check_gamma(gamma1, H, device, "gamma1")
+    _check_gamma(gamma2, H, device, "gamma2")
+    out, residual_out = _outputs(T, H, device, out, residual_out)
+    ws, wsb = _workspace(workspace)
+    arr = _ptr_array(ps)
+    _check(_c_sandwich(ctypes.cast(arr, _P), len(ps), residual.data_ptr(), gamma1.data_ptr(),
+                       gamma2.data_ptr(), eps, T, H, out.data_ptr(), residual_out.data_ptr(),
+                       ws, wsb, _stream(stream, device)))
+    return out, residual_out
+
+
+def moe_finalize_reduce_norm(expert_rows: TensorList, topk_weights: torch.Tensor,
+                             topk_rows: torch.Tensor, residual: torch.Tensor,
+                             gamma1: torch.Tensor, gamma2: Optional[torch.Tensor] = None,
+                             eps: float = 1e-6, *, shared: Optional[TensorList] = None,
+                             epilogue: int = EPI_RMSNORM, out=None, residual_out=None,
+                             workspace=None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Per rank r: P_r = bf16(sum_j w[t,j] * E_r[rows[t,j]] (+ shared_r[t])); then
+    the epilogue on sum_r P_r.  Returns (out, residual_out)."""
+    if residual is None:
+        raise ValueError("residual is required: this boundary always adds the residual")
+    es, sh, T, H, k, num_rows, device = _check_finalize(expert_rows, topk_weights, topk_rows,
+                                                        shared)
+    _need(residual, "residual", torch.bfloat16, 2, device)
+    if tuple(residual.shape) != (T, H):
+        raise ValueError("residual must be [T, H]")
+    _check_gamma(gamma1, H, device, "gamma1")
+    if epilogue == EPI_SANDWICH:
+        if gamma2 is None:
+            raise ValueError("the sandwich epilogue needs gamma2")
+        _check_gamma(gamma2, H, device, "gamma2")
+    out, residual_out = _outputs(T, H, device, out, residual_out)
+    ws, wsb = _workspace(workspace)
+    earr = _ptr_array(es)
+    sarr = _ptr_array(sh) if sh is not None else None
+    _check(_c_moe(ctypes.cast(earr, _P), ctypes.cast(sarr, _P) if sarr is not None else None,
+                  len(es), topk_weights.data_ptr(), topk_rows.data_ptr(), k, num_rows, epilogue,
+                  residual.data_ptr(), gamma1.data_ptr(),
+                  gamma2.data_ptr() if gamma2 is not None else None, eps, T, H,
+                  out.data_ptr(), residual_out.data_ptr(), ws, wsb, _stream(stream, device)))
+    return out, residual_out
+
+
+def reduce_bf16(partials: TensorList, *, out=None, stream=None) -> torch.Tensor:
+    """Split path, pass 1: bf16(sum_r partials[r]) (FP32 sum)."""
+    ps, T, H, device = _check_partials(partials, None)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=device)
+    else:
+        _need(out, "out", torch.bfloat16, 2, device)
+    arr = _ptr_array(ps)
+    _check(_c_reduce_bf16(ctypes.cast(arr, _P), len(ps), T, H, out.data_ptr(),
+                          _stream(stream, device)))
+    return out
+
+
+def moe_finalize_reduce_bf16(expert_rows: TensorList, topk_weights: torch.Tensor,
+                             topk_rows: torch.Tensor, *, shared: Optional[TensorList] = None,
+                             out=None, stream=None) -> torch.Tensor:
+    """Split path, pass 1 with the finalize: bf16(sum_r P_r)."""
+    es, sh, T, H, k, num_rows, device = _check_finalize(expert_rows, topk_weights, topk_rows,
+                                                        shared)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=device)
+    else:
+        _need(out, "out", torch.bfloat16, 2, device)
+    earr = _ptr_array(es)
+    sarr = _ptr_array(sh) if sh is not None else None
+    _check(_c_moe_bf16(ctypes.cast(earr, _P), ctypes.cast(sarr, _P) if sarr is not None else None,
+                       len(es), topk_weights.data_ptr(), topk_rows.data_ptr(), k, num_rows, T, H,
+                       out.data_ptr(), _stream(stream, device)))
+    return out
+
+
+def split_reduce_norm(src: TensorList, residual: torch.Tensor, gamma1: torch.Tensor,
+                      gamma2: Optional[torch.Tensor] = None, eps: float = 1e-6, *,
+                      topk_weights=None, topk_rows=None, shared=None,
+                      epilogue: int = EPI_RMSNORM, scratch=None, out=None, residual_out=None,
+                      stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Both passes of the split path.  Without topk_weights, src are the
+    partials; with them, src are the expert-row buffers."""
+    if residual is None:
+        raise ValueError("residual is required: this boundary always adds the residual")
+    if topk_weights is not None:
+        es, sh, T, H, k, num_rows, device = _check_finalize(src, topk_weights, topk_rows, shared)
+        w_ptr, r_ptr = topk_weights.data_ptr(), topk_rows.data_ptr()
+    else:
+        es, T, H, device = _check_partials(src, residual)
+        sh, k, num_rows, w_ptr, r_ptr = None, 0, 0, None, None
+    _need(residual, "residual", torch.bfloat16, 2, device)
+    _check_gamma(gamma1, H, device, "gamma1")
+    if epilogue == EPI_SANDWICH:
+        if gamma2 is None:
+            raise ValueError("the sandwich epilogue needs gamma2")
+        _check_gamma(gamma2, H, device, "gamma2")
+    if scratch is None:
+        scratch = torch.empty((T, H), dtype=torch.bfloat16, device=device)
+    else:
+        _need(scratch, "scratch", torch.bfloat16, 2, device)
+    out, residual_out = _outputs(T, H, device, out, residual_out)
+    earr = _ptr_array(es)
+    sarr = _ptr_array(sh) if sh is not None else None
+    _check(_c_split(ctypes.cast(earr, _P), ctypes.cast(sarr, _P) if sarr is not None else None,
+                    len(es), w_ptr, r_ptr, k, num_rows, epilogue, residual.data_ptr(),
+                    gamma1.data_ptr(), gamma2.data_ptr() if gamma2 is not None else None, eps,
+                    T, H, scratch.data_ptr(), out.data_ptr(), residual_out.data_ptr(),
+                    _stream(stream, device)))
+    return out, residual_out

@@ -1,0 +1,346 @@
+// frn_api.hip -- the extern "C" entry points of include/fused_reduce_norm.h:
+// argument checks, the decline rule and kernel launches.  Every check runs
+// before the first launch, so a rejected call leaves every output untouched
+// (the fail-closed contract of vLLM PR #62366 "Details" and SGLang PR
+// #34134: a call that cannot be served says so instead of silently skipping
+// the reduction).
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "frn_internal.h"
+
+#define FRN_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+frn_status fail(frn_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+bool force_decline() {
+    static const bool forced = [] {
+        const char* e = getenv("FRN_FORCE_DECLINE");
+        return e != nullptr && e[0] == '1';
+    }();
+    return forced;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Span {
+    const char* name;
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+Span span(const char* name, const void* p, size_t bytes) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Span{name, lo, lo + bytes};
+}
+
+bool overlap(const Span& a, const Span& b) {
+    return a.lo < b.hi && b.lo < a.hi && a.hi > a.lo && b.hi > b.lo;
+}
+
+// Sizes that are malformed (INVALID) or outside what the kernels serve
+// (UNSUPPORTED).  k == 0: no finalize.
+frn_status check_sizes(int32_t R, int32_t k, int64_t T, int64_t H, int32_t epilogue) {
+    if (R < 1) return fail(FRN_ERR_INVALID, "R must be >= 1 (got %d)", R);
+    if (k < 0) return fail(FRN_ERR_INVALID, "k must be >= 0 (got %d)", k);
+    if (T < 0) return fail(FRN_ERR_INVALID, "T must be >= 0 (got %lld)", (long long)T);
+    if (H <= 0) return fail(FRN_ERR_INVALID, "H must be > 0 (got %lld)", (long long)H);
+    if (epilogue != FRN_EPI_RMSNORM && epilogue != FRN_EPI_SANDWICH && epilogue != frn::kStoreSum)
+        return fail(FRN_ERR_INVALID, "unknown epilogue %d", epilogue);
+    if (force_decline()) return fail(FRN_ERR_UNSUPPORTED, "declined: FRN_FORCE_DECLINE=1");
+    if (R > FRN_MAX_R) return fail(FRN_ERR_UNSUPPORTED, "R=%d exceeds %d", R, FRN_MAX_R);
+    if (k > FRN_MAX_K) return fail(FRN_ERR_UNSUPPORTED, "k=%d exceeds %d", k, FRN_MAX_K);
+    if (H % 8 != 0)
+        return fail(FRN_ERR_UNSUPPORTED, "H=%lld is not a multiple of 8", (long long)H);
+    if (H < 8 || H > FRN_MAX_H)
+        return fail(FRN_ERR_UNSUPPORTED, "H=%lld outside [8, %d]", (long long)H, FRN_MAX_H);
+    if (T > 0x7fffffffLL)
+        return fail(FRN_ERR_UNSUPPORTED, "T=%lld exceeds 2^31-1 rows", (long long)T);
+    return FRN_OK;
+}
+
+// Pointer checks shared by every call.
+struct Call {
+    frn::RowArgs a;
+    Span in[2 * FRN_MAX_R + 6];
+    int n_in = 0;
+    Span outs[3];
+    int n_out = 0;
+};
+
+frn_status add_in(Call& c, const char* name, const void* p, size_t bytes, bool need16 = true) {
+    if (p == nullptr) return fail(FRN_ERR_INVALID, "%s is NULL", name);
+    if (need16 && !aligned16(p)) return fail(FRN_ERR_UNSUPPORTED, "%s is not 16-byte aligned", name);
+    if (!need16 && (reinterpret_cast<uintptr_t>(p) & 3u))
+        return fail(FRN_ERR_UNSUPPORTED, "%s is not 4-byte aligned", name);
+    c.in[c.n_in++] = span(name, p, bytes);
+    return FRN_OK;
+}
+
+frn_status add_out(Call& c, const char* name, void* p, size_t bytes) {
+    if (p == nullptr) return fail(FRN_ERR_INVALID, "%s is NULL", name);
+    if (!aligned16(p)) return fail(FRN_ERR_UNSUPPORTED, "%s is not 16-byte aligned", name);
+    c.outs[c.n_out++] = span(name, p, bytes);
+    return FRN_OK;
+}
+
+// Outputs may not overlap inputs or each other; the one exception is the
+// residual updated in place (residual_out == residual_in, same extent).
+frn_status check_alias(const Call& c) {
+    for (int o = 0; o < c.n_out; ++o) {
+        for (int i = 0; i < c.n_in; ++i) {
+            const bool in_place = strcmp(c.outs[o].name, "residual_out") == 0 &&
+                                  strcmp(c.in[i].name, "residual_in") == 0 &&
+                                  c.outs[o].lo == c.in[i].lo && c.outs[o].hi == c.in[i].hi;
+            if (!in_place && overlap(c.outs[o], c.in[i]))
+                return fail(FRN_ERR_INVALID, "%s overlaps %s", c.outs[o].name, c.in[i].name);
+        }
+        for (int p = o + 1; p < c.n_out; ++p)
+            if (overlap(c.outs[o], c.outs[p]))
+                return fail(FRN_ERR_INVALID, "%s overlaps %s", c.outs[o].name, c.outs[p].name);
+    }
+    return FRN_OK;
+}
+
+// Fill the source part of the argument block: partials (k == 0) or the
+// finalize operands (k > 0).
+frn_status set_sources(Call& c, const void* const* src, const void* const* shared, int32_t R,
+                       const float* topk_w, const int32_t* topk_row, int32_t k,
+                       int64_t num_rows, int64_t T, int64_t H) {
+    static const char* const kSrcNames[FRN_MAX_R] = {
+        "src[0]", "src[1]", "src[2]", "src[3]", "src[4]", "src[5]", "src[6]", "src[7]",
+        "src[8]", "src[9]", "src[10]", "src[11]", "src[12]", "src[13]", "src[14]", "src[15]"};
+    static const char* const kSharedNames[FRN_MAX_R] = {
+        "shared[0]", "shared[1]", "shared[2]", "shared[3]", "shared[4]", "shared[5]",
+        "shared[6]", "shared[7]", "shared[8]", "shared[9]", "shared[10]", "shared[11]",
+        "shared[12]", "shared[13]", "shared[14]", "shared[15]"};
+    if (src == nullptr) return fail(FRN_ERR_INVALID, "source pointer array is NULL");
+    const size_t row_bytes = (size_t)H * 2;
+    frn_status st;
+    if (k > 0) {
+        if (num_rows < 1) return fail(FRN_ERR_INVALID, "num_rows must be >= 1");
+        if (num_rows > (int64_t)0x7fffffff)
+            return fail(FRN_ERR_UNSUPPORTED, "num_rows exceeds int32 indexing");
+        if ((st = add_in(c, "topk_w", topk_w, (size_t)T * k * 4, false)) != FRN_OK) return st;
+        if ((st = add_in(c, "topk_row", topk_row, (size_t)T * k * 4, false)) != FRN_OK) return st;
+        c.a.topk_w = topk_w;
+        c.a.topk_row = topk_row;
+        c.a.num_rows = num_rows;
+    }
+    const size_t src_bytes = (k > 0 ? (size_t)num_rows : (size_t)T) * row_bytes;
+    for (int r = 0; r < R; ++r) {
+        if ((st = add_in(c, kSrcNames[r], src[r], src_bytes)) != FRN_OK) return st;
+        c.a.src[r] = static_cast<const uint4*>(src[r]);
+        c.a.shared[r] = nullptr;
+    }
+    c.a.has_shared = 0;
+    if (k > 0 && shared != nullptr) {
+        for (int r = 0; r < R; ++r) {
+            if ((st = add_in(c, kSharedNames[r], shared[r], (size_t)T * row_bytes)) != FRN_OK)
+                return st;
+            c.a.shared[r] = static_cast<const uint4*>(shared[r]);
+        }
+        c.a.has_shared = 1;
+    }
+    c.a.R = R;
+    c.a.k = k;
+    c.a.nvec = (int32_t)(H / 8);
+    c.a.H = (int32_t)H;
+    return FRN_OK;
+}
+
+frn_status set_epilogue(Call& c, int32_t epilogue, const void* residual_in, const float* g1,
+                        const float* g2, float eps, int64_t T, int64_t H, void* out,
+                        void* residual_out) {
+    frn_status st;
+    if (!(eps >= 0.0f) || !__builtin_isfinite(eps))
+        return fail(FRN_ERR_INVALID, "eps must be finite and >= 0");
+    const size_t tensor = (size_t)T * H * 2;
+    if ((st = add_in(c, "residual_in", residual_in, tensor)) != FRN_OK) return st;
+    if ((st = add_in(c, "gamma1", g1, (size_t)H * 4)) != FRN_OK) return st;
+    if (epilogue == FRN_EPI_SANDWICH) {
+        if ((st = add_in(c, "gamma2", g2, (size_t)H * 4)) != FRN_OK) return st;
+    }
+    if ((st = add_out(c, "out", out, tensor)) != FRN_OK) return st;
+    if ((st = add_out(c, "residual_out", residual_out, tensor)) != FRN_OK) return st;
+    c.a.residual = static_cast<const uint4*>(residual_in);
+    c.a.gamma1 = reinterpret_cast<const float4*>(g1);
+    c.a.gamma2 = reinterpret_cast<const float4*>(epilogue == FRN_EPI_SANDWICH ? g2 : g1);
+    c.a.out = static_cast<uint4*>(out);
+    c.a.residual_out = static_cast<uint4*>(residual_out);
+    c.a.eps = eps;
+    return FRN_OK;
+}
+
+frn_status run(const Call& c, int32_t epilogue, int64_t T, void* stream) {
+    if (T == 0) return FRN_OK;
+    const hipError_t e = frn::launch_rows(c.a, epilogue, T, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(FRN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return FRN_OK;
+}
+
+frn_status fused(const void* const* src, const void* const* shared, int32_t R,
+                 const float* topk_w, const int32_t* topk_row, int32_t k, int64_t num_rows,
+                 int32_t epilogue, const void* residual_in, const float* g1, const float* g2,
+                 float eps, int64_t T, int64_t H, void* out, void* residual_out, void* stream) {
+    g_last_error[0] = '\0';
+    frn_status st = check_sizes(R, k, T, H, epilogue);
+    if (st != FRN_OK || T == 0) return st;  // empty tensors may carry null pointers
+    Call c{};
+    if ((st = set_sources(c, src, shared, R, topk_w, topk_row, k, num_rows, T, H)) != FRN_OK)
+        return st;
+    if ((st = set_epilogue(c, epilogue, residual_in, g1, g2, eps, T, H, out, residual_out)) !=
+        FRN_OK)
+        return st;
+    if ((st = check_alias(c)) != FRN_OK) return st;
+    return run(c, epilogue, T, stream);
+}
+
+frn_status pass1(const void* const* src, const void* const* shared, int32_t R,
+                 const float* topk_w, const int32_t* topk_row, int32_t k, int64_t num_rows,
+                 int64_t T, int64_t H, void* sum_out, void* stream) {
+    g_last_error[0] = '\0';
+    frn_status st = check_sizes(R, k, T, H, frn::kStoreSum);
+    if (st != FRN_OK || T == 0) return st;
+    Call c{};
+    if ((st = set_sources(c, src, shared, R, topk_w, topk_row, k, num_rows, T, H)) != FRN_OK)
+        return st;
+    if ((st = add_out(c, "sum_out", sum_out, (size_t)T * H * 2)) != FRN_OK) return st;
+    if ((st = check_alias(c)) != FRN_OK) return st;
+    c.a.out = static_cast<uint4*>(sum_out);
+    return run(c, frn::kStoreSum, T, stream);
+}
+
+}  // namespace
+
+FRN_API frn_status frn_reduce_residual_rmsnorm(const void* const* partials, int32_t R,
+                                               const void* residual_in, const float* gamma,
+                                               float eps, int64_t T, int64_t H, void* out,
+                                               void* residual_out, void* workspace,
+                                               size_t workspace_bytes, void* stream) {
+    (void)workspace;
+    (void)workspace_bytes;
+    return fused(partials, nullptr, R, nullptr, nullptr, 0, 0, FRN_EPI_RMSNORM, residual_in,
+                 gamma, nullptr, eps, T, H, out, residual_out, stream);
+}
+
+FRN_API frn_status frn_reduce_sandwich_norm(const void* const* partials, int32_t R,
+                                            const void* residual_in, const float* gamma1,
+                                            const float* gamma2, float eps, int64_t T,
+                                            int64_t H, void* out, void* residual_out,
+                                            void* workspace, size_t workspace_bytes,
+                                            void* stream) {
+    (void)workspace;
+    (void)workspace_bytes;
+    return fused(partials, nullptr, R, nullptr, nullptr, 0, 0, FRN_EPI_SANDWICH, residual_in,
+                 gamma1, gamma2, eps, T, H, out, residual_out, stream);
+}
+
+FRN_API frn_status frn_moe_finalize_reduce_norm(
+    const void* const* expert_rows, const void* const* shared, int32_t R, const float* topk_w,
+    const int32_t* topk_row, int32_t k, int64_t num_rows, int32_t epilogue,
+    const void* residual_in, const float* gamma1, const float* gamma2, float eps, int64_t T,
+    int64_t H, void* out, void* residual_out, void* workspace, size_t workspace_bytes,
+    void* stream) {
+    (void)workspace;
+    (void)workspace_bytes;
+    if (k < 1) {
+        g_last_error[0] = '\0';
+        return fail(FRN_ERR_INVALID, "k must be >= 1 for the finalize (got %d)", k);
+    }
+    if (epilogue != FRN_EPI_RMSNORM && epilogue != FRN_EPI_SANDWICH) {
+        g_last_error[0] = '\0';
+        return fail(FRN_ERR_INVALID, "unknown epilogue %d", epilogue);
+    }
+    return fused(expert_rows, shared, R, topk_w, topk_row, k, num_rows, epilogue, residual_in,
+                 gamma1, gamma2, eps, T, H, out, residual_out, stream);
+}
+
+FRN_API frn_status frn_reduce_bf16(const void* const* partials, int32_t R, int64_t T, int64_t H,
+                                   void* sum_out, void* stream) {
+    return pass1(partials, nullptr, R, nullptr, nullptr, 0, 0, T, H, sum_out, stream);
+}
+
+FRN_API frn_status frn_moe_finalize_reduce_bf16(const void* const* expert_rows,
+                                                const void* const* shared, int32_t R,
+                                                const float* topk_w, const int32_t* topk_row,
+                                                int32_t k, int64_t num_rows, int64_t T,
+                                                int64_t H, void* sum_out, void* stream) {
+    if (k < 1) {
+        g_last_error[0] = '\0';
+        return fail(FRN_ERR_INVALID, "k must be >= 1 for the finalize (got %d)", k);
+    }
+    return pass1(expert_rows, shared, R, topk_w, topk_row, k, num_rows, T, H, sum_out, stream);
+}
+
+FRN_API frn_status frn_split_reduce_norm(const void* const* src, const void* const* shared,
+                                         int32_t R, const float* topk_w,
+                                         const int32_t* topk_row, int32_t k, int64_t num_rows,
+                                         int32_t epilogue, const void* residual_in,
+                                         const float* gamma1, const float* gamma2, float eps,
+                                         int64_t T, int64_t H, void* scratch, void* out,
+                                         void* residual_out, void* stream) {
+    g_last_error[0] = '\0';
+    if (epilogue != FRN_EPI_RMSNORM && epilogue != FRN_EPI_SANDWICH)
+        return fail(FRN_ERR_INVALID, "unknown epilogue %d", epilogue);
+    // Check both passes completely before launching either.
+    frn_status st = check_sizes(R, k, T, H, epilogue);
+    if (st != FRN_OK || T == 0) return st;
+    Call c1{};
+    if ((st = set_sources(c1, src, shared, R, topk_w, topk_row, k, num_rows, T, H)) != FRN_OK)
+        return st;
+    if ((st = add_out(c1, "scratch", scratch, (size_t)T * H * 2)) != FRN_OK) return st;
+    // the scratch tensor must not overlap the pass-2 operands either
+    if ((st = set_epilogue(c1, epilogue, residual_in, gamma1, gamma2, eps, T, H, out,
+                           residual_out)) != FRN_OK)
+        return st;
+    if ((st = check_alias(c1)) != FRN_OK) return st;
+    c1.a.out = static_cast<uint4*>(scratch);
+    Call c2{};
+    const void* one[1] = {scratch};
+    if ((st = set_sources(c2, one, nullptr, 1, nullptr, nullptr, 0, 0, T, H)) != FRN_OK)
+        return st;
+    if ((st = set_epilogue(c2, epilogue, residual_in, gamma1, gamma2, eps, T, H, out,
+                           residual_out)) != FRN_OK)
+        return st;
+    if ((st = run(c1, frn::kStoreSum, T, stream)) != FRN_OK) return st;
+    return run(c2, epilogue, T, stream);
+}
+
+FRN_API frn_status frn_query(int32_t R, int32_t k, int64_t T, int64_t H, int32_t epilogue) {
+    g_last_error[0] = '\0';
+    return check_sizes(R, k, T, H, epilogue);
+}
+
+FRN_API size_t frn_workspace_bytes(int64_t max_T, int64_t H, int32_t R, int32_t k) {
+    (void)max_T;
+    (void)H;
+    (void)R;
+    (void)k;
+    return 0;
+}
+
+FRN_API const char* frn_status_string(frn_status s) {
+    switch (s) {
+        case FRN_OK: return "FRN_OK";
+        case FRN_ERR_INVALID: return "FRN_ERR_INVALID: malformed arguments";
+        case FRN_ERR_UNSUPPORTED: return "FRN_ERR_UNSUPPORTED: call declined";
+        case FRN_ERR_HIP: return "FRN_ERR_HIP: HIP launch failed";
+    }
+    return "unknown frn_status";
+}
+
+FRN_API const char* frn_last_error(void) { return g_last_error; }
+
+FRN_API const char* frn_version(void) { return FRN_VERSION_STRING; }

@@ -1,0 +1,54 @@
+// frn_internal.h -- what the host entry points and the gfx950 kernels share:
+// the kernel argument block and the launch functions.  Not installed; the
+// public interface is include/fused_reduce_norm.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fused_reduce_norm.h"
+
+namespace frn {
+
+// Which epilogue a kernel runs after the FP32 reduction.
+enum Epilogue : int {
+    kRmsNorm = FRN_EPI_RMSNORM,    // h = s + x; y = norm(h) * g1
+    kSandwich = FRN_EPI_SANDWICH,  // a = norm(s) * g1; h = a + x; y = norm(h) * g2
+    kStoreSum = 2,                 // split pass 1: sum_out = bf16(s)
+};
+
+// Everything one launch needs, passed by value as the kernel argument.
+// All tensors are addressed in 16-byte vectors of 8 BF16 values (or 4 FP32
+// values for gamma); nvec = H / 8 vectors per row.
+struct RowArgs {
+    const uint4* src[FRN_MAX_R];     // partials [T,H], or expert rows [num_rows,H]
+    const uint4* shared[FRN_MAX_R];  // shared-expert rows [T,H] (finalize), may be null
+    const float* topk_w;             // [T,k]
+    const int32_t* topk_row;         // [T,k]
+    const uint4* residual;           // [T,H]
+    const float4* gamma1;            // [H]
+    const float4* gamma2;            // [H]
+    uint4* out;                      // [T,H] normed output, or the pass-1 sum
+    uint4* residual_out;             // [T,H]
+    int64_t num_rows;                // rows in each expert buffer
+    int32_t R;                       // ranks
+    int32_t k;                       // top-k slots (0: no finalize)
+    int32_t nvec;                    // H / 8
+    int32_t H;
+    float eps;
+    int32_t has_shared;
+};
+
+// Launch shape of one call: one token row per workgroup, `threads` lanes
+// per row, each lane owning `vec` 16-byte vectors of the row.
+struct LaunchShape {
+    int threads;
+    int vec;
+};
+
+LaunchShape choose_shape(int nvec, bool finalize);
+
+// Enqueue the boundary kernel for T rows.  Returns the HIP launch status.
+hipError_t launch_rows(const RowArgs& a, int epilogue, int64_t T, hipStream_t stream);
+
+}  // namespace frn

@@ -1,0 +1,361 @@
+// frn_kernels.hip -- gfx950 kernels of the fused reduce + norm boundary.
+//
+// One token row per workgroup.  Each lane owns V 16-byte vectors of the row
+// (8 BF16 values each), placed `threads` vectors apart so that every wave
+// instruction touches 64 consecutive vectors (1 KiB) of a row.  A lane
+// issues all loads of a rank chunk (or of a top-k chunk) before it consumes
+// any of them, keeps the FP32 row slice in registers for the whole
+// epilogue, and writes each output exactly once.  Row-wide sums of squares
+// are FP64: per lane, then a 64-lane butterfly, then one LDS slot per wave
+// summed in wave order, so every lane sees the same bits and the result
+// does not depend on scheduling.
+//
+// Arithmetic (vLLM PR #62366 "Claims": FP32 reduction, FP32 epilogue,
+// per-rank BF16 rounding of the finalize; "Details": no FMA contraction --
+// this file is built with -ffp-contract=off):
+//   finalize   acc = 0; acc = acc + w_j * e_j for j ascending; acc = acc + shared;
+//              P_r = bf16(acc)
+//   reduce     s = P_0; s = s + P_r for r ascending
+//   rinv(x)    ms = (float)(sum x^2 (FP64) / H); v = ms + eps; rinv = 1 / sqrt(v)
+//   rmsnorm    h = s + x; y = (h * rinv(h)) * gamma
+//   sandwich   a = (s * rinv(s)) * gamma1; h = a + x; y = (h * rinv(h)) * gamma2
+// No MFMA: nothing here is a dense contraction; the kernels are bound by HBM.
+#include "frn_internal.h"
+
+namespace frn {
+namespace {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// BF16 -> FP32 is exact: the BF16 bits are the high half of the FP32 bits.
+__device__ __forceinline__ void widen(const uint4& q, float (&f)[8]) {
+    f[0] = __uint_as_float(q.x << 16);
+    f[1] = __uint_as_float(q.x & 0xffff0000u);
+    f[2] = __uint_as_float(q.y << 16);
+    f[3] = __uint_as_float(q.y & 0xffff0000u);
+    f[4] = __uint_as_float(q.z << 16);
+    f[5] = __uint_as_float(q.z & 0xffff0000u);
+    f[6] = __uint_as_float(q.w << 16);
+    f[7] = __uint_as_float(q.w & 0xffff0000u);
+}
+
+// FP32 -> BF16, round to nearest even (one v_cvt_pk_bf16_f32 per pair).
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    const f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+__device__ __forceinline__ uint4 narrow(const float (&f)[8]) {
+    uint4 q;
+    q.x = pack2(f[0], f[1]);
+    q.y = pack2(f[2], f[3]);
+    q.z = pack2(f[4], f[5]);
+    q.w = pack2(f[6], f[7]);
+    return q;
+}
+
+__device__ __forceinline__ void load_gamma(const float4* g, int v, float (&out)[8]) {
+    const float4 a = g[2 * v];
+    const float4 b = g[2 * v + 1];
+    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+    out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+}
+
+// Sum of one double per lane over the workgroup, the same bits in every lane.
+__device__ __forceinline__ double block_sum(double v, double* slots) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    if (lane == 0) slots[wave] = v;
+    __syncthreads();
+    const int nw = blockDim.x >> 6;
+    double t = slots[0];
+    for (int w = 1; w < nw; ++w) t += slots[w];
+    return t;
+}
+
+// Inverse RMS from the FP64 sum of squares: eps inside the root, each FP32
+// step correctly rounded (hipcc's default sqrt and divide are).
+__device__ __forceinline__ float inv_rms(double ss, int H, float eps) {
+    const float ms = (float)(ss / (double)H);
+    const float v = ms + eps;
+    const float d = sqrtf(v);
+    return 1.0f / d;
+}
+
+template <int V>
+__device__ __forceinline__ double sum_squares(const float (&x)[V][8], const bool (&ok)[V]) {
+    double ss = 0.0;
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+        if (!ok[j]) continue;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const double d = (double)x[j][i];
+            ss = __fma_rn(d, d, ss);  // d*d is exact in FP64, so this is one rounding
+        }
+    }
+    return ss;
+}
+
+// EPI: epilogue; FIN: top-k finalize ahead of the reduction; V: vectors per
+// lane; C: ranks (no finalize) or top-k slots (finalize) loaded per chunk.
+template <int EPI, bool FIN, int V, int C>
+__global__ __launch_bounds__(1024) void boundary_kernel(const RowArgs a) {
+    __shared__ double slots[2][16];
+    const int64_t t = blockIdx.x;
+    const int nt = blockDim.x;
+    const int nvec = a.nvec;
+    const int64_t row = t * (int64_t)nvec;
+
+    int vi[V];
+    bool ok[V];
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+        vi[j] = threadIdx.x + j * nt;
+        ok[j] = vi[j] < nvec;
+    }
+
+    // The residual does not depend on the reduction: start its loads first.
+    uint4 xr[V];
+    if constexpr (EPI != kStoreSum) {
+#pragma unroll
+        for (int j = 0; j < V; ++j) {
+            xr[j] = make_uint4(0, 0, 0, 0);
+            if (ok[j]) xr[j] = a.residual[row + vi[j]];
+        }
+    }
+
+    float s[V][8];
+#pragma unroll
+    for (int j = 0; j < V; ++j)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s[j][i] = 0.0f;
+
+    if constexpr (!FIN) {
+        // s = P_0 + P_1 + ... + P_{R-1}, ranks in chunks of C.
+        for (int r0 = 0; r0 < a.R; r0 += C) {
+            uint4 q[C][V];
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+                if (r0 + c < a.R) {
+                    const uint4* p = a.src[r0 + c];
+#pragma unroll
+                    for (int j = 0; j < V; ++j) {
+                        q[c][j] = make_uint4(0, 0, 0, 0);
+                        if (ok[j]) q[c][j] = p[row + vi[j]];
+                    }
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+                if (r0 + c < a.R) {
+#pragma unroll
+                    for (int j = 0; j < V; ++j) {
+                        float f[8];
+                        widen(q[c][j], f);
+                        if (r0 + c == 0) {
+#pragma unroll
+                            for (int i = 0; i < 8; ++i) s[j][i] = f[i];
+                        } else {
+#pragma unroll
+                            for (int i = 0; i < 8; ++i) s[j][i] = s[j][i] + f[i];
+                        }
+                    }
+                }
+            }
+        }
+    } else {
+        const int k = a.k;
+        const int32_t* rows_t = a.topk_row + t * k;
+        const float* w_t = a.topk_w + t * k;
+        const uint4 nan8 = make_uint4(0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u);
+        for (int r = 0; r < a.R; ++r) {
+            const uint4* E = a.src[r];
+            float acc[V][8];
+#pragma unroll
+            for (int j = 0; j < V; ++j)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[j][i] = 0.0f;
+            for (int j0 = 0; j0 < k; j0 += C) {
+                uint4 e[C][V];
+                float w[C];
+#pragma unroll
+                for (int c = 0; c < C; ++c) {
+                    w[c] = 0.0f;
+                    if (j0 + c < k) {
+                        const int32_t er = rows_t[j0 + c];
+                        w[c] = w_t[j0 + c];
+                        // an index outside the buffer is never dereferenced
+                        const bool in = er >= 0 && (int64_t)er < a.num_rows;
+                        const int64_t base = (int64_t)(in ? er : 0) * nvec;
+#pragma unroll
+                        for (int j = 0; j < V; ++j) {
+                            e[c][j] = nan8;
+                            if (in && ok[j]) e[c][j] = E[base + vi[j]];
+                        }
+                    }
+                }
+#pragma unroll
+                for (int c = 0; c < C; ++c) {
+                    if (j0 + c < k) {
+#pragma unroll
+                        for (int j = 0; j < V; ++j) {
+                            float f[8];
+                            widen(e[c][j], f);
+#pragma unroll
+                            for (int i = 0; i < 8; ++i) {
+                                const float prod = w[c] * f[i];
+                                acc[j][i] = acc[j][i] + prod;
+                            }
+                        }
+                    }
+                }
+            }
+            if (a.has_shared) {
+                const uint4* S = a.shared[r];
+#pragma unroll
+                for (int j = 0; j < V; ++j) {
+                    uint4 q = make_uint4(0, 0, 0, 0);
+                    if (ok[j]) q = S[row + vi[j]];
+                    float f[8];
+                    widen(q, f);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) acc[j][i] = acc[j][i] + f[i];
+                }
+            }
+            // The rank's finalized partial is a BF16 tensor: round, then sum.
+#pragma unroll
+            for (int j = 0; j < V; ++j) {
+                float p[8];
+                widen(narrow(acc[j]), p);
+                if (r == 0) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) s[j][i] = p[i];
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) s[j][i] = s[j][i] + p[i];
+                }
+            }
+        }
+    }
+
+    if constexpr (EPI == kStoreSum) {
+#pragma unroll
+        for (int j = 0; j < V; ++j)
+            if (ok[j]) a.out[row + vi[j]] = narrow(s[j]);
+        return;
+    } else {
+        const float eps = a.eps;
+        const int H = a.H;
+        float h[V][8];
+        if constexpr (EPI == kSandwich) {
+            const float r1 = inv_rms(block_sum(sum_squares<V>(s, ok), slots[0]), H, eps);
+#pragma unroll
+            for (int j = 0; j < V; ++j) {
+                float g[8], x[8];
+                if (ok[j]) load_gamma(a.gamma1, vi[j], g);
+                else
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) g[i] = 0.0f;
+                widen(xr[j], x);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float n = s[j][i] * r1;
+                    const float av = n * g[i];
+                    h[j][i] = av + x[i];
+                }
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < V; ++j) {
+                float x[8];
+                widen(xr[j], x);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) h[j][i] = s[j][i] + x[i];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < V; ++j)
+            if (ok[j]) a.residual_out[row + vi[j]] = narrow(h[j]);
+
+        const float r2 = inv_rms(block_sum(sum_squares<V>(h, ok), slots[1]), H, eps);
+        const float4* g2 = (EPI == kSandwich) ? a.gamma2 : a.gamma1;
+#pragma unroll
+        for (int j = 0; j < V; ++j) {
+            if (!ok[j]) continue;
+            float g[8], y[8];
+            load_gamma(g2, vi[j], g);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float n = h[j][i] * r2;
+                y[i] = n * g[i];
+            }
+            a.out[row + vi[j]] = narrow(y);
+        }
+    }
+}
+
+template <int EPI, bool FIN, int V, int C>
+hipError_t launch(const RowArgs& a, int64_t T, int threads, hipStream_t stream) {
+    hipLaunchKernelGGL((boundary_kernel<EPI, FIN, V, C>), dim3((unsigned)T), dim3(threads), 0,
+                       stream, a);
+    return hipGetLastError();
+}
+
+// Ranks (or top-k slots) per load chunk: at most 64 VGPRs of loads in
+// flight per lane (32 for a two-vector finalize, which holds more live
+// state and would otherwise spill).
+template <int EPI, bool FIN, int V>
+hipError_t launch_c(const RowArgs& a, int64_t T, int threads, hipStream_t stream) {
+    constexpr int CMAX = 16 / V;
+    if constexpr (FIN) {
+        return launch<EPI, FIN, V, (V == 1 ? 16 : 4)>(a, T, threads, stream);
+    } else {
+        if (a.R <= 2) return launch<EPI, FIN, V, 2>(a, T, threads, stream);
+        if (a.R <= 4) return launch<EPI, FIN, V, 4>(a, T, threads, stream);
+        if (a.R <= 8 || CMAX == 8) return launch<EPI, FIN, V, 8>(a, T, threads, stream);
+        return launch<EPI, FIN, V, CMAX>(a, T, threads, stream);
+    }
+}
+
+template <int EPI, bool FIN>
+hipError_t launch_v(const RowArgs& a, int64_t T, LaunchShape sh, hipStream_t stream) {
+    if (sh.vec == 1) return launch_c<EPI, FIN, 1>(a, T, sh.threads, stream);
+    return launch_c<EPI, FIN, 2>(a, T, sh.threads, stream);
+}
+
+}  // namespace
+
+LaunchShape choose_shape(int nvec, bool finalize) {
+    // Up to 512 lanes per row keep 2+ rows per CU resident; a finalize keeps
+    // more of its loads in flight per lane, so it prefers one vector each.
+    const int limit = finalize ? 1024 : 512;
+    LaunchShape sh;
+    sh.vec = nvec <= limit ? 1 : 2;
+    const int lanes = (nvec + sh.vec - 1) / sh.vec;
+    sh.threads = ((lanes + 63) / 64) * 64;
+    return sh;
+}
+
+hipError_t launch_rows(const RowArgs& a, int epilogue, int64_t T, hipStream_t stream) {
+    const bool fin = a.k > 0;
+    const LaunchShape sh = choose_shape(a.nvec, fin);
+    switch (epilogue) {
+        case kRmsNorm:
+            return fin ? launch_v<kRmsNorm, true>(a, T, sh, stream)
+                       : launch_v<kRmsNorm, false>(a, T, sh, stream);
+        case kSandwich:
+            return fin ? launch_v<kSandwich, true>(a, T, sh, stream)
+                       : launch_v<kSandwich, false>(a, T, sh, stream);
+        case kStoreSum:
+            return fin ? launch_v<kStoreSum, true>(a, T, sh, stream)
+                       : launch_v<kStoreSum, false>(a, T, sh, stream);
+        default:
+            return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace frn
