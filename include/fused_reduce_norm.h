@@ -87,7 +87,8 @@ typedef enum frn_epilogue {
  *   out[t] = bf16((h * rinv(h)) * gamma)
  * partials: R device pointers to [T,H] BF16.  residual_in/out, out: [T,H]
  * BF16.  gamma: [H] FP32.  eps >= 0, finite.  workspace/workspace_bytes:
- * optional scratch (NULL/0 allowed); see frn_workspace_bytes.
+ * optional scratch, NULL/0 allowed (see frn_workspace_bytes; unused
+ * without the finalize).
  */
 frn_status frn_reduce_residual_rmsnorm(const void* const* partials, int32_t R,
                                        const void* residual_in, const float* gamma,
@@ -184,8 +185,24 @@ frn_status frn_split_reduce_norm(const void* const* src, const void* const* shar
  */
 frn_status frn_query(int32_t R, int32_t k, int64_t T, int64_t H, int32_t epilogue);
 
-/* Bytes of optional workspace that lets calls up to max_T tokens use the
- * split-row kernels for small T.  0 means no workspace is ever used. */
+/*
+ * Bytes of the optional workspace argument of the fused calls for calls of
+ * up to max_T tokens (0: the call never uses one).  Today only the MoE
+ * finalize (k > 0) uses it: for T <= 256 the finalize of each (token, rank,
+ * 2048-column slice) then runs in a workgroup of its own and writes its
+ * BF16 partial to the workspace, and a second kernel on the same stream
+ * reduces the R partials and runs the epilogue.  This spreads a token's row
+ * over many workgroups at small batch, the analogue of the pages' row
+ * spread over several blocks (SGLang PR #34134, the publish-granularity
+ * discussion).  Results are bit-identical with and without it (the
+ * partials are the same BF16 values, summed in the same order).  Layout: R
+ * x T x H BF16.  The caller allocates it (256-byte aligned); it needs no
+ * initialisation and holds nothing between calls.  Calls that share one
+ * workspace must not run concurrently.  A workspace that is NULL or smaller
+ * than needed for a call is ignored (the call then uses the
+ * one-row-per-workgroup kernel); one that is used must not overlap any
+ * other argument (FRN_ERR_INVALID).
+ */
 size_t frn_workspace_bytes(int64_t max_T, int64_t H, int32_t R, int32_t k);
 
 /* Static text for a status code. */

@@ -205,6 +205,27 @@ def test_pass1_rejects(lib):
     assert lib.frn_reduce_bf16(src, 2, 0, 64, addr(20), None) == OK
 
 
+def test_workspace_bytes(lib):
+    assert lib.frn_workspace_bytes(8, 6144, 8, 10) == 8 * 8 * 6144 * 2
+    assert lib.frn_workspace_bytes(5000, 7168, 2, 8) == 256 * 2 * 7168 * 2
+    assert lib.frn_workspace_bytes(64, 5120, 4, 0) == 0      # no finalize: none used
+    assert lib.frn_workspace_bytes(64, 5124, 4, 2) == 0      # unsupported H
+    assert lib.frn_workspace_bytes(0, 5120, 4, 2) == 0
+
+
+def test_misaligned_or_overlapping_workspace_rejected(lib):
+    need = lib.frn_workspace_bytes(4, 64, 2, 3)
+    src = ptrs(addr(10), addr(11))
+    sh = ptrs(addr(30), addr(31))
+    def moe(ws, wsb):
+        return lib.frn_moe_finalize_reduce_norm(src, sh, 2, addr(5), addr(6), 3, 12, 0, addr(1),
+                                                addr(2), None, 1e-6, 4, 64, addr(3), addr(4),
+                                                ws, wsb, None)
+    assert moe(addr(40, 16), need) == UNSUPPORTED   # not 256-byte aligned
+    assert moe(addr(10), need) == INVALID           # overlaps expert rows of rank 0
+    assert moe(addr(3), need) == INVALID            # overlaps out
+
+
 def test_query(lib):
     assert lib.frn_query(4, 0, 1024, 5120, 1) == OK
     assert lib.frn_query(8, 10, 64, 6144, 0) == OK

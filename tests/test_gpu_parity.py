@@ -377,3 +377,84 @@ def test_no_fma_contraction_in_sandwich():
     torch.cuda.synchronize()
     assert not torch.any(x.view(torch.int16) & 0x7FFF), "sandwich add was contracted"
     assert not torch.any(y.view(torch.int16) & 0x7FFF)
+
+
+# ------------------------------------------------- split-row finalize --- #
+
+MOE_CASES = [c for c in MODERATE if c[4] > 0]
+
+
+@pytest.mark.parametrize("case", MOE_CASES, ids=[mid_id(c) for c in MOE_CASES])
+def test_finalize_without_workspace_uses_row_kernel(case):
+    """The same finalize cases through the one-row-per-workgroup kernel (no
+    workspace): identical to the oracle, so identical to the split-row path."""
+    R, T, H, epi, k, sh = case
+    log(f"finalize row kernel {mid_id(case)}")
+    inp = workloads.make(R, T, H, epilogue=epi, sigma=0.5, k=k, shared=sh,
+                         seed=1000 + R * 7 + T * 13 + H)
+    y, x = gpu_fused(to_dev(inp), workspace=None)
+    check(f"row-kernel finalize {mid_id(case)}", y, x, oracle_ref(inp))
+
+
+def test_split_row_workspace_explicit_and_reused():
+    m = frn()
+    R, H, k = 8, 6144, 10
+    need = m.workspace_bytes(256, H, R, k)
+    assert need == 256 * R * H * 2
+    assert m.workspace_bytes(1000, H, R, k) == need  # capped at 256 tokens
+    assert m.workspace_bytes(64, H, R, 0) == 0
+    ws = torch.full((need,), 0xA5, dtype=torch.uint8, device=DEV)  # no initialisation needed
+    for T in (1, 7, 64, 256, 3):
+        inp = workloads.make(R, T, H, k=k, shared=True, seed=400 + T)
+        y, x = gpu_fused(to_dev(inp), workspace=ws)
+        check(f"explicit workspace T={T}", y, x, oracle_ref(inp))
+
+
+def test_split_row_small_or_misaligned_workspace():
+    m = frn()
+    inp = workloads.make(4, 8, 2048, k=3, shared=True, seed=55)
+    ref = oracle_ref(inp)
+    d = to_dev(inp)
+    small = torch.zeros(64, dtype=torch.uint8, device=DEV)   # too small: ignored
+    y, x = gpu_fused(d, workspace=small)
+    check("too-small workspace ignored", y, x, ref)
+    big = torch.zeros(m.workspace_bytes(8, 2048, 4, 3) + 512, dtype=torch.uint8, device=DEV)
+    with pytest.raises(m.FusedReduceNormUnsupported):
+        gpu_fused(d, workspace=big[16:])                      # 16-byte, not 256-byte aligned
+
+
+def test_split_row_graph_replay():
+    """Graph-captured split-row finalize (two kernels through the workspace):
+    every replay, with new data, matches the oracle."""
+    m = frn()
+    R, T, H, k = 8, 4, 6144, 10
+    base = to_dev(workloads.make(R, T, H, k=k, shared=True, seed=600))
+    ws = torch.empty(m.workspace_bytes(T, H, R, k), dtype=torch.uint8, device=DEV)
+    out = torch.empty(T, H, dtype=torch.bfloat16, device=DEV)
+    rout = torch.empty(T, H, dtype=torch.bfloat16, device=DEV)
+
+    def call():
+        m.moe_finalize_reduce_norm(base.expert_rows, base.topk_w, base.topk_idx, base.residual,
+                                   base.gamma1, None, base.eps, shared=base.shared,
+                                   out=out, residual_out=rout, workspace=ws)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for rep in range(4):
+        new = workloads.make(R, T, H, k=k, shared=True, seed=700 + rep)
+        for dst, src in zip(base.expert_rows + base.shared, new.expert_rows + new.shared):
+            dst.copy_(src.to(DEV))
+        base.topk_w.copy_(new.topk_w.to(DEV))
+        base.topk_idx.copy_(new.topk_idx.to(DEV))
+        base.residual.copy_(new.residual.to(DEV))
+        base.gamma1.copy_(new.gamma1.to(DEV))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        check(f"split-row graph replay {rep}", out, rout, oracle_ref(new))

@@ -177,9 +177,29 @@ def _outputs(T, H, device, out, residual_out):
     return out, residual_out
 
 
-def _workspace(workspace):
+_AUTO_WS = {}
+
+
+def _workspace(workspace, T=0, H=0, R=0, k=0, device=None, stream=None):
+    """(pointer, bytes) of the workspace argument.  ``"auto"``: a buffer
+    cached per (device, stream) and grown on demand (it holds nothing between
+    calls).  ``None``: none."""
     if workspace is None:
         return None, 0
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace must be a tensor, None or 'auto'")
+        need = workspace_bytes(T, H, R, k) if k > 0 else 0
+        if need == 0:
+            return None, 0
+        key = (device.index, stream)
+        ws = _AUTO_WS.get(key)
+        if ws is None or ws.numel() < need:
+            ws = torch.empty(need, dtype=torch.uint8, device=device)
+            _AUTO_WS[key] = ws
+        return ws.data_ptr(), ws.numel()
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
     return workspace.data_ptr(), workspace.numel() * workspace.element_size()
 
 
@@ -277,9 +297,12 @@ def moe_finalize_reduce_norm(expert_rows: TensorList, topk_weights: torch.Tensor
                              gamma1: torch.Tensor, gamma2: Optional[torch.Tensor] = None,
                              eps: float = 1e-6, *, shared: Optional[TensorList] = None,
                              epilogue: int = EPI_RMSNORM, out=None, residual_out=None,
-                             workspace=None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+                             workspace="auto", stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Per rank r: P_r = bf16(sum_j w[t,j] * E_r[rows[t,j]] (+ shared_r[t])); then
-    the epilogue on sum_r P_r.  Returns (out, residual_out)."""
+    the epilogue on sum_r P_r.  Returns (out, residual_out).  ``workspace``:
+    "auto" (a buffer cached per device and stream, used for T <= 256), None
+    (never), or a uint8 GPU tensor of at least ``workspace_bytes(T, H, R, k)``
+    bytes, 256-byte aligned."""
     if residual is None:
         raise ValueError("residual is required: this boundary always adds the residual")
     es, sh, T, H, k, num_rows, device = _check_finalize(expert_rows, topk_weights, topk_rows,
@@ -293,14 +316,15 @@ def moe_finalize_reduce_norm(expert_rows: TensorList, topk_weights: torch.Tensor
             raise ValueError("the sandwich epilogue needs gamma2")
         _check_gamma(gamma2, H, device, "gamma2")
     out, residual_out = _outputs(T, H, device, out, residual_out)
-    ws, wsb = _workspace(workspace)
+    st = _stream(stream, device)
+    ws, wsb = _workspace(workspace, T, H, len(es), k, device, st)
     earr = _ptr_array(es)
     sarr = _ptr_array(sh) if sh is not None else None
     _check(_c_moe(ctypes.cast(earr, _P), ctypes.cast(sarr, _P) if sarr is not None else None,
                   len(es), topk_weights.data_ptr(), topk_rows.data_ptr(), k, num_rows, epilogue,
                   residual.data_ptr(), gamma1.data_ptr(),
                   gamma2.data_ptr() if gamma2 is not None else None, eps, T, H,
-                  out.data_ptr(), residual_out.data_ptr(), ws, wsb, _stream(stream, device)))
+                  out.data_ptr(), residual_out.data_ptr(), ws, wsb, st))
     return out, residual_out
 
 

@@ -75,7 +75,7 @@ struct Call {
     frn::RowArgs a;
     Span in[2 * FRN_MAX_R + 6];
     int n_in = 0;
-    Span outs[3];
+    Span outs[4];
     int n_out = 0;
 };
 
@@ -155,6 +155,7 @@ frn_status set_sources(Call& c, const void* const* src, const void* const* share
     }
     c.a.R = R;
     c.a.k = k;
+    c.a.T = T;
     c.a.nvec = (int32_t)(H / 8);
     c.a.H = (int32_t)H;
     return FRN_OK;
@@ -190,10 +191,27 @@ frn_status run(const Call& c, int32_t epilogue, int64_t T, void* stream) {
     return FRN_OK;
 }
 
+// The optional workspace serves the split-row finalize when it is large
+// enough for this T; otherwise it is ignored (the one-row kernel needs none).
+frn_status set_workspace(Call& c, void* workspace, size_t workspace_bytes, int32_t k, int64_t T,
+                         int64_t H, int32_t R) {
+    c.a.ws_p = nullptr;
+    if (k == 0 || workspace == nullptr) return FRN_OK;
+    const size_t need = frn::split_workspace_bytes(T, H, R);
+    if (need == 0 || workspace_bytes < need) return FRN_OK;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return fail(FRN_ERR_UNSUPPORTED, "workspace is not 256-byte aligned");
+    frn_status st = add_out(c, "workspace", workspace, need);
+    if (st != FRN_OK) return st;
+    c.a.ws_p = static_cast<uint4*>(workspace);
+    return FRN_OK;
+}
+
 frn_status fused(const void* const* src, const void* const* shared, int32_t R,
                  const float* topk_w, const int32_t* topk_row, int32_t k, int64_t num_rows,
                  int32_t epilogue, const void* residual_in, const float* g1, const float* g2,
-                 float eps, int64_t T, int64_t H, void* out, void* residual_out, void* stream) {
+                 float eps, int64_t T, int64_t H, void* out, void* residual_out,
+                 void* workspace, size_t workspace_bytes, void* stream) {
     g_last_error[0] = '\0';
     frn_status st = check_sizes(R, k, T, H, epilogue);
     if (st != FRN_OK || T == 0) return st;  // empty tensors may carry null pointers
@@ -203,6 +221,7 @@ frn_status fused(const void* const* src, const void* const* shared, int32_t R,
     if ((st = set_epilogue(c, epilogue, residual_in, g1, g2, eps, T, H, out, residual_out)) !=
         FRN_OK)
         return st;
+    if ((st = set_workspace(c, workspace, workspace_bytes, k, T, H, R)) != FRN_OK) return st;
     if ((st = check_alias(c)) != FRN_OK) return st;
     return run(c, epilogue, T, stream);
 }
@@ -229,10 +248,9 @@ FRN_API frn_status frn_reduce_residual_rmsnorm(const void* const* partials, int3
                                                float eps, int64_t T, int64_t H, void* out,
                                                void* residual_out, void* workspace,
                                                size_t workspace_bytes, void* stream) {
-    (void)workspace;
-    (void)workspace_bytes;
     return fused(partials, nullptr, R, nullptr, nullptr, 0, 0, FRN_EPI_RMSNORM, residual_in,
-                 gamma, nullptr, eps, T, H, out, residual_out, stream);
+                 gamma, nullptr, eps, T, H, out, residual_out, workspace, workspace_bytes,
+                 stream);
 }
 
 FRN_API frn_status frn_reduce_sandwich_norm(const void* const* partials, int32_t R,
@@ -241,10 +259,9 @@ FRN_API frn_status frn_reduce_sandwich_norm(const void* const* partials, int32_t
                                             int64_t H, void* out, void* residual_out,
                                             void* workspace, size_t workspace_bytes,
                                             void* stream) {
-    (void)workspace;
-    (void)workspace_bytes;
     return fused(partials, nullptr, R, nullptr, nullptr, 0, 0, FRN_EPI_SANDWICH, residual_in,
-                 gamma1, gamma2, eps, T, H, out, residual_out, stream);
+                 gamma1, gamma2, eps, T, H, out, residual_out, workspace, workspace_bytes,
+                 stream);
 }
 
 FRN_API frn_status frn_moe_finalize_reduce_norm(
@@ -253,8 +270,6 @@ FRN_API frn_status frn_moe_finalize_reduce_norm(
     const void* residual_in, const float* gamma1, const float* gamma2, float eps, int64_t T,
     int64_t H, void* out, void* residual_out, void* workspace, size_t workspace_bytes,
     void* stream) {
-    (void)workspace;
-    (void)workspace_bytes;
     if (k < 1) {
         g_last_error[0] = '\0';
         return fail(FRN_ERR_INVALID, "k must be >= 1 for the finalize (got %d)", k);
@@ -264,7 +279,8 @@ FRN_API frn_status frn_moe_finalize_reduce_norm(
         return fail(FRN_ERR_INVALID, "unknown epilogue %d", epilogue);
     }
     return fused(expert_rows, shared, R, topk_w, topk_row, k, num_rows, epilogue, residual_in,
-                 gamma1, gamma2, eps, T, H, out, residual_out, stream);
+                 gamma1, gamma2, eps, T, H, out, residual_out, workspace, workspace_bytes,
+                 stream);
 }
 
 FRN_API frn_status frn_reduce_bf16(const void* const* partials, int32_t R, int64_t T, int64_t H,
@@ -324,11 +340,10 @@ FRN_API frn_status frn_query(int32_t R, int32_t k, int64_t T, int64_t H, int32_t
 }
 
 FRN_API size_t frn_workspace_bytes(int64_t max_T, int64_t H, int32_t R, int32_t k) {
-    (void)max_T;
-    (void)H;
-    (void)R;
-    (void)k;
-    return 0;
+    if (k < 1 || R < 1 || R > FRN_MAX_R || H < 8 || H > FRN_MAX_H || H % 8 != 0 || max_T < 1)
+        return 0;
+    const int64_t t = max_T < frn::kSplitMaxT ? max_T : frn::kSplitMaxT;
+    return frn::split_workspace_bytes(t, H, R);
 }
 
 FRN_API const char* frn_status_string(frn_status s) {

@@ -31,6 +31,8 @@ struct RowArgs {
     uint4* out;                      // [T,H] normed output, or the pass-1 sum
     uint4* residual_out;             // [T,H]
     int64_t num_rows;                // rows in each expert buffer
+    int64_t T;                       // token rows of the call
+    uint4* ws_p;                     // split-row finalize: R x T x nvec BF16 partials, or null
     int32_t R;                       // ranks
     int32_t k;                       // top-k slots (0: no finalize)
     int32_t nvec;                    // H / 8
@@ -38,6 +40,22 @@ struct RowArgs {
     float eps;
     int32_t has_shared;
 };
+
+// Split-row finalize (small T): workgroup size, the largest T it serves and
+// its workspace, R x T x H BF16 finalized partials (no other state: the
+// workspace needs no initialisation and keeps nothing between calls).
+constexpr int kSplitThreads = 256;
+constexpr int64_t kSplitMaxT = 256;
+
+// Workspace bytes the split-row finalize needs for T rows (0 if T is too
+// large for it).
+inline size_t split_workspace_bytes(int64_t T, int64_t H, int32_t R) {
+    if (T < 1 || T > kSplitMaxT) return 0;
+    return (size_t)T * (size_t)R * (size_t)H * 2;
+}
+
+// Column slices of one row in the split-row finalize.
+int split_slices(int nvec);
 
 // Launch shape of one call: one token row per workgroup, `threads` lanes
 // per row, each lane owning `vec` 16-byte vectors of the row.

@@ -1,14 +1,27 @@
 // frn_kernels.hip -- gfx950 kernels of the fused reduce + norm boundary.
 //
-// One token row per workgroup.  Each lane owns V 16-byte vectors of the row
-// (8 BF16 values each), placed `threads` vectors apart so that every wave
-// instruction touches 64 consecutive vectors (1 KiB) of a row.  A lane
+// Two kernels share the per-row building blocks below.
+//
+// row_kernel: one token row per workgroup.  Each lane owns V 16-byte vectors
+// of the row (8 BF16 values each), placed `threads` vectors apart so every
+// wave instruction touches 64 consecutive vectors (1 KiB) of a row.  A lane
 // issues all loads of a rank chunk (or of a top-k chunk) before it consumes
-// any of them, keeps the FP32 row slice in registers for the whole
-// epilogue, and writes each output exactly once.  Row-wide sums of squares
-// are FP64: per lane, then a 64-lane butterfly, then one LDS slot per wave
-// summed in wave order, so every lane sees the same bits and the result
-// does not depend on scheduling.
+// any of them, keeps the FP32 row slice in registers through the epilogue,
+// and writes each output exactly once.
+//
+// finalize_slices_kernel: for the MoE finalize at small T, where one
+// workgroup per token would walk the R ranks one memory round trip after
+// another.  Workgroup (t, r, c) finalizes slice c of rank r of token t and
+// stores the BF16 partial into the caller's workspace -- the per-rank
+// finalize materialized -- and row_kernel then reduces those R partials in
+// rank order and runs the epilogue.  The kernel boundary orders the two, so
+// no workgroup waits for another and no cross-XCD cache maintenance is
+// issued inside a kernel (a device-scope fence per workgroup writes back and
+// invalidates the whole L2 of its XCD, which measured far slower).
+//
+// Row-wide sums of squares are FP64: per lane, then a 64-lane butterfly, then
+// one LDS slot per wave summed in wave order, so every lane sees the same
+// bits and the result does not depend on scheduling.
 //
 // Arithmetic (vLLM PR #62366 "Claims": FP32 reduction, FP32 epilogue,
 // per-rank BF16 rounding of the finalize; "Details": no FMA contraction --
@@ -30,6 +43,7 @@ namespace {
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
 
 // Streamed tensors (partials, expert rows, residual, outputs) are touched
 // once: load and store them non-temporally so they do not displace the
@@ -101,12 +115,26 @@ __device__ __forceinline__ float inv_rms(double ss, int H, float eps) {
     return 1.0f / d;
 }
 
+// The vectors of a row that one lane owns: V of them, blockDim.x apart.
 template <int V>
-__device__ __forceinline__ double sum_squares(const float (&x)[V][8], const bool (&ok)[V]) {
+struct Lanes {
+    int vi[V];
+    bool ok[V];
+    __device__ __forceinline__ explicit Lanes(int nvec) {
+#pragma unroll
+        for (int j = 0; j < V; ++j) {
+            vi[j] = threadIdx.x + j * blockDim.x;
+            ok[j] = vi[j] < nvec;
+        }
+    }
+};
+
+template <int V>
+__device__ __forceinline__ double sum_squares(const float (&x)[V][8], const Lanes<V>& L) {
     double ss = 0.0;
 #pragma unroll
     for (int j = 0; j < V; ++j) {
-        if (!ok[j]) continue;
+        if (!L.ok[j]) continue;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const double d = (double)x[j][i];
@@ -116,33 +144,196 @@ __device__ __forceinline__ double sum_squares(const float (&x)[V][8], const bool
     return ss;
 }
 
-// EPI: epilogue; FIN: top-k finalize ahead of the reduction; V: vectors per
-// lane; C: ranks (no finalize) or top-k slots (finalize) loaded per chunk.
-template <int EPI, bool FIN, int V, int C>
-__global__ __launch_bounds__(1024) void boundary_kernel(const RowArgs a) {
-    __shared__ double slots[2][16];
-    const int64_t t = blockIdx.x;
-    const int nt = blockDim.x;
-    const int nvec = a.nvec;
-    const int64_t row = t * (int64_t)nvec;
-
-    int vi[V];
-    bool ok[V];
+template <int V>
+__device__ __forceinline__ void load_residual(const RowArgs& a, int64_t row, const Lanes<V>& L,
+                                              uint4 (&xr)[V]) {
 #pragma unroll
     for (int j = 0; j < V; ++j) {
-        vi[j] = threadIdx.x + j * nt;
-        ok[j] = vi[j] < nvec;
+        xr[j] = make_uint4(0, 0, 0, 0);
+        if (L.ok[j]) xr[j] = ld_stream(a.residual + row + L.vi[j]);
     }
+}
+
+// s = P_0 + P_1 + ... + P_{R-1} (FP32, rank order) over the lane's vectors.
+// rank_row(r) gives rank r's row as a vector pointer; ranks are loaded in
+// chunks of C, every load of a chunk issued before any is consumed.
+template <int V, int C, bool STREAM, typename RankRow>
+__device__ __forceinline__ void reduce_ranks(RankRow rank_row, int R, const Lanes<V>& L,
+                                             float (&s)[V][8]) {
+    for (int r0 = 0; r0 < R; r0 += C) {
+        uint4 q[C][V];
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            if (r0 + c < R) {
+                const uint4* p = rank_row(r0 + c);
+#pragma unroll
+                for (int j = 0; j < V; ++j) {
+                    q[c][j] = make_uint4(0, 0, 0, 0);
+                    if (L.ok[j]) q[c][j] = STREAM ? ld_stream(p + L.vi[j]) : p[L.vi[j]];
+                }
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            if (r0 + c < R) {
+#pragma unroll
+                for (int j = 0; j < V; ++j) {
+                    float f[8];
+                    widen(q[c][j], f);
+                    if (r0 + c == 0) {
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) s[j][i] = f[i];
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) s[j][i] = s[j][i] + f[i];
+                    }
+                }
+            }
+        }
+    }
+}
+
+// Finalize of one rank for token t over the lane's vectors, before the BF16
+// rounding: acc = sum_j w_j * E[row_j] (+ shared), j in order, top-k slots
+// loaded in chunks of C.  A row index outside [0, num_rows) is never
+// dereferenced; its slot reads as NaN.
+template <int V, int C>
+__device__ __forceinline__ void finalize_rank(const RowArgs& a, int r, int64_t t,
+                                              const Lanes<V>& L, float (&acc)[V][8]) {
+    const int k = a.k;
+    const int32_t* rows_t = a.topk_row + t * k;
+    const float* w_t = a.topk_w + t * k;
+    const uint4 nan8 = make_uint4(0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u);
+    const uint4* E = a.src[r];
+    const int nvec = a.nvec;
+#pragma unroll
+    for (int j = 0; j < V; ++j)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[j][i] = 0.0f;
+    for (int j0 = 0; j0 < k; j0 += C) {
+        uint4 e[C][V];
+        float w[C];
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            w[c] = 0.0f;
+            if (j0 + c < k) {
+                const int32_t er = rows_t[j0 + c];
+                w[c] = w_t[j0 + c];
+                const bool in = er >= 0 && (int64_t)er < a.num_rows;
+                const int64_t base = (int64_t)(in ? er : 0) * nvec;
+#pragma unroll
+                for (int j = 0; j < V; ++j) {
+                    e[c][j] = nan8;
+                    if (in && L.ok[j]) e[c][j] = ld_stream(E + base + L.vi[j]);
+                }
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            if (j0 + c < k) {
+#pragma unroll
+                for (int j = 0; j < V; ++j) {
+                    float f[8];
+                    widen(e[c][j], f);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const float prod = w[c] * f[i];
+                        acc[j][i] = acc[j][i] + prod;
+                    }
+                }
+            }
+        }
+    }
+    if (a.has_shared) {
+        const uint4* S = a.shared[r] + t * nvec;
+#pragma unroll
+        for (int j = 0; j < V; ++j) {
+            uint4 q = make_uint4(0, 0, 0, 0);
+            if (L.ok[j]) q = ld_stream(S + L.vi[j]);
+            float f[8];
+            widen(q, f);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[j][i] = acc[j][i] + f[i];
+        }
+    }
+}
+
+// Epilogue of one row: residual add and norm(s), stores of out and
+// residual_out (or the pass-1 sum).  Every lane of the workgroup takes part
+// (the row-wide sums synchronise the workgroup).
+template <int EPI, int V>
+__device__ __forceinline__ void epilogue(const RowArgs& a, int64_t row, const Lanes<V>& L,
+                                         float (&s)[V][8], const uint4 (&xr)[V],
+                                         double (&slots)[2][16]) {
+    if constexpr (EPI == kStoreSum) {
+#pragma unroll
+        for (int j = 0; j < V; ++j)
+            if (L.ok[j]) st_stream(a.out + row + L.vi[j], narrow(s[j]));
+    } else {
+        const float eps = a.eps;
+        const int H = a.H;
+        // h overwrites s in place
+        if constexpr (EPI == kSandwich) {
+            const float r1 = inv_rms(block_sum(sum_squares<V>(s, L), slots[0]), H, eps);
+#pragma unroll
+            for (int j = 0; j < V; ++j) {
+                float g[8], x[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) g[i] = 0.0f;
+                if (L.ok[j]) load_gamma(a.gamma1, L.vi[j], g);
+                widen(xr[j], x);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float n = s[j][i] * r1;
+                    const float av = n * g[i];
+                    s[j][i] = av + x[i];
+                }
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < V; ++j) {
+                float x[8];
+                widen(xr[j], x);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) s[j][i] = s[j][i] + x[i];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < V; ++j)
+            if (L.ok[j]) st_stream(a.residual_out + row + L.vi[j], narrow(s[j]));
+
+        const float r2 = inv_rms(block_sum(sum_squares<V>(s, L), slots[1]), H, eps);
+        const float4* g2 = (EPI == kSandwich) ? a.gamma2 : a.gamma1;
+#pragma unroll
+        for (int j = 0; j < V; ++j) {
+            if (!L.ok[j]) continue;
+            float g[8], y[8];
+            load_gamma(g2, L.vi[j], g);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float n = s[j][i] * r2;
+                y[i] = n * g[i];
+            }
+            st_stream(a.out + row + L.vi[j], narrow(y));
+        }
+    }
+}
+
+// ------------------------------------------------------------ kernels --- //
+
+// One token row per workgroup.  EPI: epilogue; FIN: top-k finalize ahead of
+// the reduction; V: vectors per lane; C: ranks (no finalize) or top-k slots
+// (finalize) loaded per chunk.
+template <int EPI, bool FIN, int V, int C>
+__global__ __launch_bounds__(1024) void row_kernel(const RowArgs a) {
+    __shared__ double slots[2][16];
+    const int64_t t = blockIdx.x;
+    const int64_t row = t * (int64_t)a.nvec;
+    const Lanes<V> L(a.nvec);
 
     // The residual does not depend on the reduction: start its loads first.
     uint4 xr[V];
-    if constexpr (EPI != kStoreSum) {
-#pragma unroll
-        for (int j = 0; j < V; ++j) {
-            xr[j] = make_uint4(0, 0, 0, 0);
-            if (ok[j]) xr[j] = ld_stream(a.residual + row + vi[j]);
-        }
-    }
+    if constexpr (EPI != kStoreSum) load_residual<V>(a, row, L, xr);
 
     float s[V][8];
 #pragma unroll
@@ -151,97 +342,11 @@ __global__ __launch_bounds__(1024) void boundary_kernel(const RowArgs a) {
         for (int i = 0; i < 8; ++i) s[j][i] = 0.0f;
 
     if constexpr (!FIN) {
-        // s = P_0 + P_1 + ... + P_{R-1}, ranks in chunks of C.
-        for (int r0 = 0; r0 < a.R; r0 += C) {
-            uint4 q[C][V];
-#pragma unroll
-            for (int c = 0; c < C; ++c) {
-                if (r0 + c < a.R) {
-                    const uint4* p = a.src[r0 + c];
-#pragma unroll
-                    for (int j = 0; j < V; ++j) {
-                        q[c][j] = make_uint4(0, 0, 0, 0);
-                        if (ok[j]) q[c][j] = ld_stream(p + row + vi[j]);
-                    }
-                }
-            }
-#pragma unroll
-            for (int c = 0; c < C; ++c) {
-                if (r0 + c < a.R) {
-#pragma unroll
-                    for (int j = 0; j < V; ++j) {
-                        float f[8];
-                        widen(q[c][j], f);
-                        if (r0 + c == 0) {
-#pragma unroll
-                            for (int i = 0; i < 8; ++i) s[j][i] = f[i];
-                        } else {
-#pragma unroll
-                            for (int i = 0; i < 8; ++i) s[j][i] = s[j][i] + f[i];
-                        }
-                    }
-                }
-            }
-        }
+        reduce_ranks<V, C, true>([&](int r) { return a.src[r] + row; }, a.R, L, s);
     } else {
-        const int k = a.k;
-        const int32_t* rows_t = a.topk_row + t * k;
-        const float* w_t = a.topk_w + t * k;
-        const uint4 nan8 = make_uint4(0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u);
         for (int r = 0; r < a.R; ++r) {
-            const uint4* E = a.src[r];
             float acc[V][8];
-#pragma unroll
-            for (int j = 0; j < V; ++j)
-#pragma unroll
-                for (int i = 0; i < 8; ++i) acc[j][i] = 0.0f;
-            for (int j0 = 0; j0 < k; j0 += C) {
-                uint4 e[C][V];
-                float w[C];
-#pragma unroll
-                for (int c = 0; c < C; ++c) {
-                    w[c] = 0.0f;
-                    if (j0 + c < k) {
-                        const int32_t er = rows_t[j0 + c];
-                        w[c] = w_t[j0 + c];
-                        // an index outside the buffer is never dereferenced
-                        const bool in = er >= 0 && (int64_t)er < a.num_rows;
-                        const int64_t base = (int64_t)(in ? er : 0) * nvec;
-#pragma unroll
-                        for (int j = 0; j < V; ++j) {
-                            e[c][j] = nan8;
-                            if (in && ok[j]) e[c][j] = ld_stream(E + base + vi[j]);
-                        }
-                    }
-                }
-#pragma unroll
-                for (int c = 0; c < C; ++c) {
-                    if (j0 + c < k) {
-#pragma unroll
-                        for (int j = 0; j < V; ++j) {
-                            float f[8];
-                            widen(e[c][j], f);
-#pragma unroll
-                            for (int i = 0; i < 8; ++i) {
-                                const float prod = w[c] * f[i];
-                                acc[j][i] = acc[j][i] + prod;
-                            }
-                        }
-                    }
-                }
-            }
-            if (a.has_shared) {
-                const uint4* S = a.shared[r];
-#pragma unroll
-                for (int j = 0; j < V; ++j) {
-                    uint4 q = make_uint4(0, 0, 0, 0);
-                    if (ok[j]) q = ld_stream(S + row + vi[j]);
-                    float f[8];
-                    widen(q, f);
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) acc[j][i] = acc[j][i] + f[i];
-                }
-            }
+            finalize_rank<V, C>(a, r, t, L, acc);
             // The rank's finalized partial is a BF16 tensor: round, then sum.
 #pragma unroll
             for (int j = 0; j < V; ++j) {
@@ -257,66 +362,28 @@ __global__ __launch_bounds__(1024) void boundary_kernel(const RowArgs a) {
             }
         }
     }
+    epilogue<EPI, V>(a, row, L, s, xr, slots);
+}
 
-    if constexpr (EPI == kStoreSum) {
-#pragma unroll
-        for (int j = 0; j < V; ++j)
-            if (ok[j]) st_stream(a.out + row + vi[j], narrow(s[j]));
-        return;
-    } else {
-        const float eps = a.eps;
-        const int H = a.H;
-        float h[V][8];
-        if constexpr (EPI == kSandwich) {
-            const float r1 = inv_rms(block_sum(sum_squares<V>(s, ok), slots[0]), H, eps);
-#pragma unroll
-            for (int j = 0; j < V; ++j) {
-                float g[8], x[8];
-                if (ok[j]) load_gamma(a.gamma1, vi[j], g);
-                else
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) g[i] = 0.0f;
-                widen(xr[j], x);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const float n = s[j][i] * r1;
-                    const float av = n * g[i];
-                    h[j][i] = av + x[i];
-                }
-            }
-        } else {
-#pragma unroll
-            for (int j = 0; j < V; ++j) {
-                float x[8];
-                widen(xr[j], x);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) h[j][i] = s[j][i] + x[i];
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < V; ++j)
-            if (ok[j]) st_stream(a.residual_out + row + vi[j], narrow(h[j]));
-
-        const float r2 = inv_rms(block_sum(sum_squares<V>(h, ok), slots[1]), H, eps);
-        const float4* g2 = (EPI == kSandwich) ? a.gamma2 : a.gamma1;
-#pragma unroll
-        for (int j = 0; j < V; ++j) {
-            if (!ok[j]) continue;
-            float g[8], y[8];
-            load_gamma(g2, vi[j], g);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float n = h[j][i] * r2;
-                y[i] = n * g[i];
-            }
-            st_stream(a.out + row + vi[j], narrow(y));
-        }
-    }
+// Per-rank MoE finalize of T rows, one row slice of one rank per workgroup:
+// workgroup (t, r, c) writes bf16(finalize) of vectors [c * kSplitThreads,
+// (c + 1) * kSplitThreads) of rank r, token t to P[r][t] (P = R x T x nvec
+// vectors).
+__global__ __launch_bounds__(kSplitThreads) void finalize_slices_kernel(const RowArgs a, int S) {
+    const int c = blockIdx.x % S;
+    const int r = (blockIdx.x / S) % a.R;
+    const int64_t t = blockIdx.x / (S * a.R);
+    Lanes<1> L(a.nvec);
+    L.vi[0] = c * kSplitThreads + threadIdx.x;
+    L.ok[0] = L.vi[0] < a.nvec;
+    float acc[1][8];
+    finalize_rank<1, 16>(a, r, t, L, acc);
+    if (L.ok[0]) a.ws_p[((int64_t)r * a.T + t) * a.nvec + L.vi[0]] = narrow(acc[0]);
 }
 
 template <int EPI, bool FIN, int V, int C>
 hipError_t launch(const RowArgs& a, int64_t T, int threads, hipStream_t stream) {
-    hipLaunchKernelGGL((boundary_kernel<EPI, FIN, V, C>), dim3((unsigned)T), dim3(threads), 0,
+    hipLaunchKernelGGL((row_kernel<EPI, FIN, V, C>), dim3((unsigned)T), dim3(threads), 0,
                        stream, a);
     return hipGetLastError();
 }
@@ -345,6 +412,8 @@ hipError_t launch_v(const RowArgs& a, int64_t T, LaunchShape sh, hipStream_t str
 
 }  // namespace
 
+int split_slices(int nvec) { return (nvec + kSplitThreads - 1) / kSplitThreads; }
+
 LaunchShape choose_shape(int nvec, bool finalize) {
     // Up to 512 lanes per row keep 2+ rows per CU resident; a finalize keeps
     // more of its loads in flight per lane, so it prefers one vector each.
@@ -362,7 +431,20 @@ LaunchShape choose_shape(int nvec, bool finalize) {
     return sh;
 }
 
-hipError_t launch_rows(const RowArgs& a, int epilogue, int64_t T, hipStream_t stream) {
+hipError_t launch_rows(const RowArgs& a_in, int epilogue, int64_t T, hipStream_t stream) {
+    RowArgs a = a_in;
+    if (a.k > 0 && a.ws_p != nullptr) {
+        // Split-row finalize: materialize the R finalized partials into the
+        // workspace, then reduce them like ordinary partials.
+        const int S = split_slices(a.nvec);
+        hipLaunchKernelGGL(finalize_slices_kernel, dim3((unsigned)(T * a.R * S)),
+                           dim3(kSplitThreads), 0, stream, a, S);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        for (int r = 0; r < a.R; ++r) a.src[r] = a.ws_p + (int64_t)r * T * a.nvec;
+        a.k = 0;
+        a.has_shared = 0;
+    }
     const bool fin = a.k > 0;
     const LaunchShape sh = choose_shape(a.nvec, fin);
     switch (epilogue) {
