@@ -105,6 +105,9 @@ MODERATE = [
     (4, 6, 1024, "rmsnorm", 1, False),       # k = 1, no shared expert
     (3, 5, 16384, "rmsnorm", 3, True),       # finalize at maximum H (2 vectors/lane)
     (9, 3, 1536, "sandwich", 0, False),      # R not a power of two, > 8
+    (3, 1100, 5128, "sandwich", 0, False),   # T > 1024: two vectors per lane, ragged
+    (2, 200, 520, "rmsnorm", 2, False),      # finalize, split-row, ragged, no shared
+    (2, 300, 520, "sandwich", 2, True),      # finalize above the split-row range
 ]
 
 

@@ -64,7 +64,7 @@ struct LaunchShape {
     int vec;
 };
 
-LaunchShape choose_shape(int nvec, bool finalize);
+LaunchShape choose_shape(int nvec, bool finalize, int64_t T, int epilogue);
 
 // Enqueue the boundary kernel for T rows.  Returns the HIP launch status.
 hipError_t launch_rows(const RowArgs& a, int epilogue, int64_t T, hipStream_t stream);

@@ -44,7 +44,6 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
-
 // Streamed tensors (partials, expert rows, residual, outputs) are touched
 // once: load and store them non-temporally so they do not displace the
 // reused gamma rows from the caches.  Worth ~10% of HBM bandwidth on gfx950.
@@ -407,6 +406,9 @@ hipError_t launch_c(const RowArgs& a, int64_t T, int threads, hipStream_t stream
 template <int EPI, bool FIN>
 hipError_t launch_v(const RowArgs& a, int64_t T, LaunchShape sh, hipStream_t stream) {
     if (sh.vec == 1) return launch_c<EPI, FIN, 1>(a, T, sh.threads, stream);
+    if constexpr (!FIN && EPI != kStoreSum) {
+        if (sh.vec == 4) return launch<EPI, FIN, 4, 4>(a, T, sh.threads, stream);
+    }
     return launch_c<EPI, FIN, 2>(a, T, sh.threads, stream);
 }
 
@@ -414,18 +416,34 @@ hipError_t launch_v(const RowArgs& a, int64_t T, LaunchShape sh, hipStream_t str
 
 int split_slices(int nvec) { return (nvec + kSplitThreads - 1) / kSplitThreads; }
 
-LaunchShape choose_shape(int nvec, bool finalize) {
-    // Up to 512 lanes per row keep 2+ rows per CU resident; a finalize keeps
-    // more of its loads in flight per lane, so it prefers one vector each.
-    // FRN_VEC=1|2 overrides the choice (tuning aid) where it fits 1024 lanes.
+LaunchShape choose_shape(int nvec, bool finalize, int64_t T, int epilogue) {
+    // Vectors per lane, from a sweep of the sandwich workloads on MI355X
+    // (graph replay; H=5120 R=4 and H=8192 R=8):
+    //  - small T (<= 256, latency-bound): the fewest vectors that keep a row
+    //    within 640 lanes -- more lanes issue the row's loads at once
+    //    (H=5120 T=1: 4.3 us with one vector, 4.6 with two);
+    //  - 256 < T <= 1024 (every row resident at once): four vectors, fewer
+    //    waves per row to synchronise (H=5120 T=1024: 15.6 -> 14.6 us);
+    //  - T > 1024: two vectors for rows over 512 vectors (H=5120 T=4096:
+    //    54 us with two, 55 with four, 60 with one).
+    // A finalize holds more live state per vector, so it keeps one vector
+    // per lane up to 1024 lanes.  FRN_VEC=1|2|4 overrides (tuning aid).
     static const int forced = [] {
         const char* e = getenv("FRN_VEC");
-        return (e && (e[0] == '1' || e[0] == '2')) ? e[0] - '0' : 0;
+        return (e && (e[0] == '1' || e[0] == '2' || e[0] == '4')) ? e[0] - '0' : 0;
     }();
-    const int limit = finalize ? 1024 : 512;
     LaunchShape sh;
-    sh.vec = nvec <= limit ? 1 : 2;
-    if (forced && (nvec + forced - 1) / forced <= 1024) sh.vec = forced;
+    if (finalize)
+        sh.vec = nvec <= 1024 ? 1 : 2;
+    else if (T <= 256)
+        sh.vec = nvec <= 640 ? 1 : 2;
+    else if (T <= 1024 && nvec >= 512 && epilogue != kStoreSum)
+        sh.vec = 4;
+    else
+        sh.vec = nvec <= 512 ? 1 : 2;
+    if (forced && (nvec + forced - 1) / forced <= 1024 &&
+        !(forced == 4 && (finalize || epilogue == kStoreSum)))
+        sh.vec = forced;
     const int lanes = (nvec + sh.vec - 1) / sh.vec;
     sh.threads = ((lanes + 63) / 64) * 64;
     return sh;
@@ -446,7 +464,7 @@ hipError_t launch_rows(const RowArgs& a_in, int epilogue, int64_t T, hipStream_t
         a.has_shared = 0;
     }
     const bool fin = a.k > 0;
-    const LaunchShape sh = choose_shape(a.nvec, fin);
+    const LaunchShape sh = choose_shape(a.nvec, fin, T, epilogue);
     switch (epilogue) {
         case kRmsNorm:
             return fin ? launch_v<kRmsNorm, true>(a, T, sh, stream)
