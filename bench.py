@@ -45,8 +45,9 @@ COLD_BYTES = 1 << 30       # rotate inputs over > 1 GiB where bandwidth is measu
 
 
 def kernel_source_digest() -> str:
-    """SHA-256 over the kernel sources and build flags: counter data taken
-    for another version of the kernels is not reported."""
+    """SHA-256 over the kernel sources, the public header and the code
+    generation flags: counter data taken for another version of the kernels
+    is not reported."""
     from tp_reduction_rmsnorm_amd import build as B
     h = hashlib.sha256()
     for f in sorted(glob.glob(os.path.join(B.CSRC, "*"))):
@@ -55,7 +56,7 @@ def kernel_source_digest() -> str:
             h.update(fh.read())
     with open(os.path.join(ROOT, "include", "fused_reduce_norm.h"), "rb") as fh:
         h.update(fh.read())
-    h.update(" ".join(B.FLAGS).encode())
+    h.update(" ".join(B.CODEGEN_FLAGS).encode())
     return h.hexdigest()
 
 

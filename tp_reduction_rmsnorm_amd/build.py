@@ -21,11 +21,15 @@ SOURCES = [os.path.join(CSRC, f) for f in ("frn_kernels.hip", "frn_api.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-FLAGS = [
+# Flags that decide the generated code (no paths, so a hash of them does not
+# depend on where the repository is checked out).
+CODEGEN_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-fvisibility=hidden",
+]
+FLAGS = CODEGEN_FLAGS + [
     "-Wall", "-Wno-unused-command-line-argument",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
