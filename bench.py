@@ -44,11 +44,22 @@ SWEEP_T = (1, 8, 64, 256, 1024, 4096)
 COLD_BYTES = 1 << 30       # rotate inputs over > 1 GiB where bandwidth is measured
 
 
+def hip_build_module():
+    """tp_reduction_rmsnorm_amd/build.py loaded by path (importing it through
+    the package would first load the library it builds)."""
+    import importlib.util
+    path = os.path.join(ROOT, "tp_reduction_rmsnorm_amd", "build.py")
+    spec = importlib.util.spec_from_file_location("frn_hip_build", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
 def kernel_source_digest() -> str:
     """SHA-256 over the kernel sources, the public header and the code
     generation flags: counter data taken for another version of the kernels
     is not reported."""
-    from tp_reduction_rmsnorm_amd import build as B
+    B = hip_build_module()
     h = hashlib.sha256()
     for f in sorted(glob.glob(os.path.join(B.CSRC, "*"))):
         with open(f, "rb") as fh:
@@ -78,7 +89,7 @@ def stored_traffic(workload: str, T: int, digest: str):
 class Runner:
     """Rotating input/output sets of one workload and the fused call on them."""
 
-    def __init__(self, cid, T, dev, cold=True, split=False):
+    def __init__(self, cid, T, dev, cold=True, split=False, unfused=False):
         import torch
         import tp_reduction_rmsnorm_amd as frn
         import workloads
@@ -86,6 +97,7 @@ class Runner:
         self.w = workloads.WORKLOADS[cid]
         self.T = T
         self.split = split
+        self.unfused = unfused
         w = self.w
         self.bytes = workloads.algorithmic_bytes(w.R, T, w.H, epilogue=w.epilogue, k=w.k,
                                                  shared=w.shared)
@@ -94,6 +106,8 @@ class Runner:
         self.outs = [(torch.empty(T, w.H, dtype=torch.bfloat16, device=dev),
                       torch.empty(T, w.H, dtype=torch.bfloat16, device=dev)) for _ in range(n)]
         self.scratch = torch.empty(T, w.H, dtype=torch.bfloat16, device=dev) if split else None
+        self.parts = ([torch.empty(T, w.H, dtype=torch.bfloat16, device=dev) for _ in range(w.R)]
+                      if unfused else None)
         self.epi = frn.EPI_SANDWICH if w.epilogue == "sandwich" else frn.EPI_RMSNORM
 
     def call(self, i):
@@ -106,6 +120,14 @@ class Runner:
                                        topk_rows=d.topk_idx if d.k else None,
                                        shared=d.shared if d.k else None, epilogue=self.epi,
                                        scratch=self.scratch, out=o, residual_out=r)
+        if d.k and self.unfused:
+            # the standalone finalize, then the plain reduction of its output
+            f.moe_finalize(d.expert_rows, d.topk_w, d.topk_idx, shared=d.shared, out=self.parts)
+            if self.epi == f.EPI_SANDWICH:
+                return f.reduce_sandwich_norm(self.parts, d.residual, d.gamma1, d.gamma2, d.eps,
+                                              out=o, residual_out=r)
+            return f.reduce_residual_rmsnorm(self.parts, d.residual, d.gamma1, d.eps,
+                                             out=o, residual_out=r)
         if d.k:
             return f.moe_finalize_reduce_norm(d.expert_rows, d.topk_w, d.topk_idx, d.residual,
                                               d.gamma1, d.gamma2, d.eps, shared=d.shared,
@@ -163,12 +185,14 @@ def sweep(dev, cids=(2, 3), Ts=SWEEP_T):
 
 def extra_configs(dev):
     rows = []
-    for cid, Ts, split in ((1, (8,), False), (4, (1, 2, 4, 8, 16, 32, 64), False),
-                           (5, (4096, 16384), False), (5, (4096, 16384), True)):
+    for cid, Ts, mode in ((1, (8,), ""), (4, (1, 2, 4, 8, 16, 32, 64), ""),
+                          (4, (1, 8, 64), "unfused"),
+                          (5, (4096, 16384), ""), (5, (4096, 16384), "split")):
         for T in Ts:
-            r = Runner(cid, T, dev, cold=T >= 256, split=split)
+            r = Runner(cid, T, dev, cold=T >= 256, split=mode == "split",
+                       unfused=mode == "unfused")
             us = r.graph_us()
-            rows.append(dict(workload=r.w.name + ("_split" if split else ""), T=T,
+            rows.append(dict(workload=r.w.name + (f"_{mode}" if mode else ""), T=T,
                              us_per_call=round(us, 3), GBps=round(r.bytes / us / 1e3, 1),
                              frac_of_peak=round(r.bytes / us / 1e3 / PEAK_GBS, 4)))
             print(json.dumps(dict(extra=rows[-1])), file=sys.stderr, flush=True)
@@ -223,8 +247,7 @@ def main():
     import torch
     lib = os.path.join(ROOT, "tp_reduction_rmsnorm_amd", "libfused_reduce_norm.so")
     if not os.path.exists(lib):
-        from tp_reduction_rmsnorm_amd import build as B
-        B.build()
+        hip_build_module().build()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 

@@ -175,6 +175,25 @@ frn_status frn_split_reduce_norm(const void* const* src, const void* const* shar
                                  void* scratch, void* out, void* residual_out, void* stream);
 
 /*
+ * The MoE top-k finalize alone, materialized per rank: for r = 0..R-1,
+ * partials_out[r][t] = P_r[t] with P_r exactly as in
+ * frn_moe_finalize_reduce_norm (j ascending, shared expert last, BF16
+ * rounding).  This is the standalone finalize kernel the fused path
+ * replaces (SGLang PR #34134, first commit message: a separate finalize
+ * kernel, and the rule that a deferred finalize reaching a non-fusing path
+ * is materialized in place): a caller whose reduction runs elsewhere
+ * finalizes with this and reduces the R tensors itself.  Reducing the R
+ * outputs with frn_reduce_residual_rmsnorm / frn_reduce_sandwich_norm gives
+ * bit for bit the fused call's results.  partials_out: HOST array of R
+ * device pointers to [T,H] BF16 buffers, which must not overlap each other
+ * or any input.  Other arguments as in frn_moe_finalize_reduce_norm.
+ */
+frn_status frn_moe_finalize(const void* const* expert_rows, const void* const* shared,
+                            int32_t R, const float* topk_w, const int32_t* topk_row, int32_t k,
+                            int64_t num_rows, int64_t T, int64_t H, void* const* partials_out,
+                            void* stream);
+
+/*
  * Capability check without launching anything: FRN_OK if a call with these
  * sizes is served, FRN_ERR_UNSUPPORTED if it would be declined, and
  * FRN_ERR_INVALID for malformed sizes (the analogue of a workspace factory

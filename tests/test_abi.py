@@ -25,8 +25,8 @@ P = ctypes.c_void_p
 @pytest.fixture(scope="module")
 def lib():
     if not os.path.exists(LIB):
-        from tp_reduction_rmsnorm_amd import build
-        build.build()
+        import __graft_entry__
+        __graft_entry__.hip_build_module().build()
     L = ctypes.CDLL(LIB)
     L.frn_reduce_residual_rmsnorm.argtypes = [P, ctypes.c_int32, P, P, ctypes.c_float,
                                               ctypes.c_int64, ctypes.c_int64, P, P, P,
@@ -224,6 +224,22 @@ def test_misaligned_or_overlapping_workspace_rejected(lib):
     assert moe(addr(40, 16), need) == UNSUPPORTED   # not 256-byte aligned
     assert moe(addr(10), need) == INVALID           # overlaps expert rows of rank 0
     assert moe(addr(3), need) == INVALID            # overlaps out
+
+
+def test_standalone_finalize_rejects(lib):
+    lib.frn_moe_finalize.argtypes = [P, P, ctypes.c_int32, P, P, ctypes.c_int32, ctypes.c_int64,
+                                     ctypes.c_int64, ctypes.c_int64, P, P]
+    src = ptrs(addr(10), addr(11))
+    outs = ptrs(addr(20), addr(21))
+    ok_args = (src, None, 2, addr(5), addr(6), 3, 12, 4, 64)
+    assert lib.frn_moe_finalize(*ok_args[:-2], 0, 64, outs, None) == OK        # T = 0
+    assert lib.frn_moe_finalize(src, None, 2, addr(5), addr(6), 0, 12, 4, 64, outs, None) == INVALID
+    assert lib.frn_moe_finalize(*ok_args, None, None) == INVALID                 # no outputs
+    assert lib.frn_moe_finalize(*ok_args, ptrs(addr(20), 0), None) == INVALID
+    assert lib.frn_moe_finalize(*ok_args, ptrs(addr(20), addr(20, 64)), None) == INVALID  # overlap
+    assert lib.frn_moe_finalize(*ok_args, ptrs(addr(20), addr(10)), None) == INVALID      # aliases E_0
+    assert lib.frn_moe_finalize(*ok_args, ptrs(addr(20), addr(21, 8)), None) == UNSUPPORTED
+    assert lib.frn_moe_finalize(src, None, 2, addr(5), addr(6), 3, 12, 4, 68, outs, None) == UNSUPPORTED
 
 
 def test_query(lib):

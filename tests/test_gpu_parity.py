@@ -206,20 +206,47 @@ def test_full_size_sampled_rows(cid, T, split):
 # ----------------------------------------------------------- structure --- #
 
 def test_fused_finalize_equals_materialized():
-    """Fused finalize == finalize materialized to BF16 per rank (pass 1 with
-    R = 1 gives exactly P_r), then the plain reduction: bit for bit."""
+    """Fused finalize == the standalone finalize (moe_finalize, R BF16
+    tensors) followed by the plain reduction: bit for bit, both epilogues,
+    with and without the split-row workspace."""
     m = frn()
     for epi in ("rmsnorm", "sandwich"):
-        inp = to_dev(workloads.make(4, 24, 6144, epilogue=epi, k=10, shared=True, seed=77))
-        y, x = gpu_fused(inp)
-        mats = [m.moe_finalize_reduce_bf16([e], inp.topk_w, inp.topk_idx, shared=[s])
-                for e, s in zip(inp.expert_rows, inp.shared)]
-        plain = workloads.Inputs(R=4, T=24, H=6144, epilogue=epi, residual=inp.residual,
-                                 gamma1=inp.gamma1, gamma2=inp.gamma2, partials=mats)
-        y2, x2 = gpu_fused(plain)
-        torch.cuda.synchronize()
-        assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), epi
-        assert torch.equal(x.view(torch.int16), x2.view(torch.int16)), epi
+        for T in (24, 300):
+            inp = to_dev(workloads.make(4, T, 6144, epilogue=epi, k=10, shared=True, seed=77 + T))
+            y, x = gpu_fused(inp)
+            mats = m.moe_finalize(inp.expert_rows, inp.topk_w, inp.topk_idx, shared=inp.shared)
+            plain = workloads.Inputs(R=4, T=T, H=6144, epilogue=epi, residual=inp.residual,
+                                     gamma1=inp.gamma1, gamma2=inp.gamma2, partials=mats)
+            y2, x2 = gpu_fused(plain)
+            torch.cuda.synchronize()
+            assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), (epi, T)
+            assert torch.equal(x.view(torch.int16), x2.view(torch.int16)), (epi, T)
+
+
+FINALIZE_CASES = [(8, 8, 6144, 10, True), (2, 32, 7168, 8, True), (3, 5, 2056, 16, True),
+                  (4, 6, 1024, 1, False), (2, 70, 16384, 3, True)]
+
+
+@pytest.mark.parametrize("case", FINALIZE_CASES,
+                         ids=[f"R{c[0]}_T{c[1]}_H{c[2]}_k{c[3]}{'_shared' if c[4] else ''}"
+                              for c in FINALIZE_CASES])
+def test_standalone_finalize_matches_oracle(case):
+    """moe_finalize writes exactly the oracle's per-rank BF16 partials."""
+    R, T, H, k, sh = case
+    log(f"standalone finalize {case}")
+    inp = workloads.make(R, T, H, k=k, shared=sh, seed=900 + T)
+    d = to_dev(inp)
+    parts = frn().moe_finalize(d.expert_rows, d.topk_w, d.topk_idx, shared=d.shared)
+    torch.cuda.synchronize()
+    ref = oracle.boundary([workloads.bits(e) for e in inp.expert_rows],
+                          residual=workloads.bits(inp.residual), gamma1=workloads.f32(inp.gamma1),
+                          eps=inp.eps, topk_w=workloads.f32(inp.topk_w),
+                          topk_idx=inp.topk_idx.numpy(),
+                          shared=[workloads.bits(s) for s in inp.shared] if sh else None,
+                          debug=True, nthreads=8)
+    for r in range(R):
+        parity.compare(f"finalize {case} rank {r}", workloads.bits(parts[r]), ref.p[r],
+                       min_exact=1.0)
 
 
 def test_deterministic_across_runs():

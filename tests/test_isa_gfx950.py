@@ -24,8 +24,8 @@ LLVM = "/opt/rocm/llvm/bin"
 @pytest.fixture(scope="module")
 def mnemonics(tmp_path_factory):
     if not os.path.exists(LIB):
-        from tp_reduction_rmsnorm_amd import build
-        build.build()
+        import __graft_entry__
+        __graft_entry__.hip_build_module().build()
     d = tmp_path_factory.mktemp("isa")
     fatbin, co = str(d / "fatbin.bin"), str(d / "gfx950.co")
     subprocess.run([f"{LLVM}/llvm-objcopy", f"--dump-section=.hip_fatbin={fatbin}", LIB,

@@ -15,6 +15,7 @@ Function names are the C entry points without their ``frn_`` prefix:
                                  rounded to BF16, then either epilogue
 * ``reduce_bf16``, ``moe_finalize_reduce_bf16``  split path, pass 1
 * ``split_reduce_norm``          both passes of the split path
+* ``moe_finalize``               the per-rank finalize alone (materialized)
 * ``query``, ``workspace_bytes``, ``version``
 
 Every call returns its outputs.  A declined call raises
@@ -55,7 +56,7 @@ class FusedReduceNormUnsupported(RuntimeError):
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is missing: build it with `python -m tp_reduction_rmsnorm_amd.build` "
+        f"{LIB_PATH} is missing: build it with `python tp_reduction_rmsnorm_amd/build.py` "
         "(or __graft_entry__.build()); there is no fallback path")
 
 _lib = ctypes.CDLL(LIB_PATH)
@@ -86,6 +87,8 @@ _c_moe_bf16 = _sig("frn_moe_finalize_reduce_bf16", ctypes.c_int,
 _c_split = _sig("frn_split_reduce_norm", ctypes.c_int,
                 [_P, _P, _I32, _P, _P, _I32, _I64, _I32, _P, _P, _P, _F32, _I64, _I64,
                  _P, _P, _P, _P])
+_c_finalize = _sig("frn_moe_finalize", ctypes.c_int,
+                   [_P, _P, _I32, _P, _P, _I32, _I64, _I64, _I64, _P, _P])
 _c_query = _sig("frn_query", ctypes.c_int, [_I32, _I32, _I64, _I64, _I32])
 _c_ws = _sig("frn_workspace_bytes", _SZ, [_I64, _I64, _I32, _I32])
 _c_status = _sig("frn_status_string", ctypes.c_char_p, [ctypes.c_int])
@@ -94,7 +97,8 @@ _c_version = _sig("frn_version", ctypes.c_char_p, [])
 
 C_FUNCTIONS = ("frn_reduce_residual_rmsnorm", "frn_reduce_sandwich_norm",
                "frn_moe_finalize_reduce_norm", "frn_reduce_bf16",
-               "frn_moe_finalize_reduce_bf16", "frn_split_reduce_norm", "frn_query",
+               "frn_moe_finalize_reduce_bf16", "frn_split_reduce_norm", "frn_moe_finalize",
+               "frn_query",
                "frn_workspace_bytes", "frn_status_string", "frn_last_error", "frn_version")
 
 
@@ -356,6 +360,34 @@ def moe_finalize_reduce_bf16(expert_rows: TensorList, topk_weights: torch.Tensor
     _check(_c_moe_bf16(ctypes.cast(earr, _P), ctypes.cast(sarr, _P) if sarr is not None else None,
                        len(es), topk_weights.data_ptr(), topk_rows.data_ptr(), k, num_rows, T, H,
                        out.data_ptr(), _stream(stream, device)))
+    return out
+
+
+def moe_finalize(expert_rows: TensorList, topk_weights: torch.Tensor, topk_rows: torch.Tensor,
+                 *, shared: Optional[TensorList] = None, out=None, stream=None):
+    """The per-rank finalize alone: returns R BF16 tensors [T, H],
+    P_r = bf16(sum_j w[t,j] * E_r[rows[t,j]] (+ shared_r[t])).  Reducing them
+    with ``reduce_residual_rmsnorm`` / ``reduce_sandwich_norm`` reproduces the
+    fused ``moe_finalize_reduce_norm`` bit for bit."""
+    es, sh, T, H, k, num_rows, device = _check_finalize(expert_rows, topk_weights, topk_rows,
+                                                        shared)
+    R = len(es)
+    if out is None:
+        out = [torch.empty((T, H), dtype=torch.bfloat16, device=device) for _ in range(R)]
+    else:
+        out = _as_list(out, "out")
+        if len(out) != R:
+            raise ValueError("out must give one [T, H] tensor per rank")
+        for i, o in enumerate(out):
+            _need(o, f"out[{i}]", torch.bfloat16, 2, device)
+            if tuple(o.shape) != (T, H):
+                raise ValueError("out tensors must be [T, H]")
+    earr = _ptr_array(es)
+    sarr = _ptr_array(sh) if sh is not None else None
+    oarr = _ptr_array(out)
+    _check(_c_finalize(ctypes.cast(earr, _P), ctypes.cast(sarr, _P) if sarr is not None else None,
+                       R, topk_weights.data_ptr(), topk_rows.data_ptr(), k, num_rows, T, H,
+                       ctypes.cast(oarr, _P), _stream(stream, device)))
     return out
 
 

@@ -1,7 +1,10 @@
 """Build step of the HIP library: compiles csrc/*.hip for gfx950 into
 ``libfused_reduce_norm.so`` next to this file.
 
-    python -m tp_reduction_rmsnorm_amd.build
+    python tp_reduction_rmsnorm_amd/build.py
+
+(run it as a file: importing it through the package would first load the
+Python binding, which needs the library this builds).
 
 Flags: -ffp-contract=off keeps every FP32 multiply and add separate (the
 pages build their boundary file with FMA contraction disabled, vLLM PR

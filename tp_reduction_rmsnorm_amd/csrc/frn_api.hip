@@ -75,7 +75,7 @@ struct Call {
     frn::RowArgs a;
     Span in[2 * FRN_MAX_R + 6];
     int n_in = 0;
-    Span outs[4];
+    Span outs[FRN_MAX_R + 4];
     int n_out = 0;
 };
 
@@ -332,6 +332,35 @@ FRN_API frn_status frn_split_reduce_norm(const void* const* src, const void* con
         return st;
     if ((st = run(c1, frn::kStoreSum, T, stream)) != FRN_OK) return st;
     return run(c2, epilogue, T, stream);
+}
+
+FRN_API frn_status frn_moe_finalize(const void* const* expert_rows, const void* const* shared,
+                                    int32_t R, const float* topk_w, const int32_t* topk_row,
+                                    int32_t k, int64_t num_rows, int64_t T, int64_t H,
+                                    void* const* partials_out, void* stream) {
+    static const char* const kOutNames[FRN_MAX_R] = {
+        "partials_out[0]", "partials_out[1]", "partials_out[2]", "partials_out[3]",
+        "partials_out[4]", "partials_out[5]", "partials_out[6]", "partials_out[7]",
+        "partials_out[8]", "partials_out[9]", "partials_out[10]", "partials_out[11]",
+        "partials_out[12]", "partials_out[13]", "partials_out[14]", "partials_out[15]"};
+    g_last_error[0] = '\0';
+    if (k < 1) return fail(FRN_ERR_INVALID, "k must be >= 1 for the finalize (got %d)", k);
+    frn_status st = check_sizes(R, k, T, H, frn::kStoreSum);
+    if (st != FRN_OK || T == 0) return st;
+    Call c{};
+    if ((st = set_sources(c, expert_rows, shared, R, topk_w, topk_row, k, num_rows, T, H)) !=
+        FRN_OK)
+        return st;
+    if (partials_out == nullptr) return fail(FRN_ERR_INVALID, "partials_out array is NULL");
+    for (int r = 0; r < R; ++r) {
+        if ((st = add_out(c, kOutNames[r], partials_out[r], (size_t)T * H * 2)) != FRN_OK)
+            return st;
+        c.a.part_out[r] = static_cast<uint4*>(partials_out[r]);
+    }
+    if ((st = check_alias(c)) != FRN_OK) return st;
+    const hipError_t e = frn::launch_finalize(c.a, T, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(FRN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return FRN_OK;
 }
 
 FRN_API frn_status frn_query(int32_t R, int32_t k, int64_t T, int64_t H, int32_t epilogue) {

@@ -33,6 +33,7 @@ struct RowArgs {
     int64_t num_rows;                // rows in each expert buffer
     int64_t T;                       // token rows of the call
     uint4* ws_p;                     // split-row finalize: R x T x nvec BF16 partials, or null
+    uint4* part_out[FRN_MAX_R];      // finalize_slices_kernel: [T,H] BF16 output per rank
     int32_t R;                       // ranks
     int32_t k;                       // top-k slots (0: no finalize)
     int32_t nvec;                    // H / 8
@@ -68,5 +69,9 @@ LaunchShape choose_shape(int nvec, bool finalize, int64_t T, int epilogue);
 
 // Enqueue the boundary kernel for T rows.  Returns the HIP launch status.
 hipError_t launch_rows(const RowArgs& a, int epilogue, int64_t T, hipStream_t stream);
+
+// Enqueue the per-rank finalize alone: a.part_out[r][t] = bf16(finalize of
+// rank r, token t) for all R ranks and T tokens.
+hipError_t launch_finalize(const RowArgs& a, int64_t T, hipStream_t stream);
 
 }  // namespace frn

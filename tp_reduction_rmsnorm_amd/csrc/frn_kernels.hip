@@ -366,8 +366,7 @@ __global__ __launch_bounds__(1024) void row_kernel(const RowArgs a) {
 
 // Per-rank MoE finalize of T rows, one row slice of one rank per workgroup:
 // workgroup (t, r, c) writes bf16(finalize) of vectors [c * kSplitThreads,
-// (c + 1) * kSplitThreads) of rank r, token t to P[r][t] (P = R x T x nvec
-// vectors).
+// (c + 1) * kSplitThreads) of rank r, token t to row t of part_out[r].
 __global__ __launch_bounds__(kSplitThreads) void finalize_slices_kernel(const RowArgs a, int S) {
     const int c = blockIdx.x % S;
     const int r = (blockIdx.x / S) % a.R;
@@ -377,7 +376,7 @@ __global__ __launch_bounds__(kSplitThreads) void finalize_slices_kernel(const Ro
     L.ok[0] = L.vi[0] < a.nvec;
     float acc[1][8];
     finalize_rank<1, 16>(a, r, t, L, acc);
-    if (L.ok[0]) a.ws_p[((int64_t)r * a.T + t) * a.nvec + L.vi[0]] = narrow(acc[0]);
+    if (L.ok[0]) a.part_out[r][t * a.nvec + L.vi[0]] = narrow(acc[0]);
 }
 
 template <int EPI, bool FIN, int V, int C>
@@ -415,6 +414,13 @@ hipError_t launch_v(const RowArgs& a, int64_t T, LaunchShape sh, hipStream_t str
 }  // namespace
 
 int split_slices(int nvec) { return (nvec + kSplitThreads - 1) / kSplitThreads; }
+
+hipError_t launch_finalize(const RowArgs& a, int64_t T, hipStream_t stream) {
+    const int S = split_slices(a.nvec);
+    hipLaunchKernelGGL(finalize_slices_kernel, dim3((unsigned)(T * a.R * S)), dim3(kSplitThreads),
+                       0, stream, a, S);
+    return hipGetLastError();
+}
 
 LaunchShape choose_shape(int nvec, bool finalize, int64_t T, int epilogue) {
     // Vectors per lane, from a sweep of the sandwich workloads on MI355X
@@ -454,12 +460,10 @@ hipError_t launch_rows(const RowArgs& a_in, int epilogue, int64_t T, hipStream_t
     if (a.k > 0 && a.ws_p != nullptr) {
         // Split-row finalize: materialize the R finalized partials into the
         // workspace, then reduce them like ordinary partials.
-        const int S = split_slices(a.nvec);
-        hipLaunchKernelGGL(finalize_slices_kernel, dim3((unsigned)(T * a.R * S)),
-                           dim3(kSplitThreads), 0, stream, a, S);
-        const hipError_t e = hipGetLastError();
+        for (int r = 0; r < a.R; ++r) a.part_out[r] = a.ws_p + (int64_t)r * T * a.nvec;
+        const hipError_t e = launch_finalize(a, T, stream);
         if (e != hipSuccess) return e;
-        for (int r = 0; r < a.R; ++r) a.src[r] = a.ws_p + (int64_t)r * T * a.nvec;
+        for (int r = 0; r < a.R; ++r) a.src[r] = a.part_out[r];
         a.k = 0;
         a.has_shared = 0;
     }
