@@ -19,9 +19,10 @@
 // issued inside a kernel (a device-scope fence per workgroup writes back and
 // invalidates the whole L2 of its XCD, which measured far slower).
 //
-// Row-wide sums of squares are FP64: per lane, then a 64-lane butterfly, then
-// one LDS slot per wave summed in wave order, so every lane sees the same
-// bits and the result does not depend on scheduling.
+// Row-wide sums of squares are FP64: per lane, then within each wave (DPP
+// swaps and four lane reads in a fixed order), then one LDS slot per wave
+// summed in wave order, so every lane sees the same bits and the result does
+// not depend on scheduling.
 //
 // Arithmetic (vLLM PR #62366 "Claims": FP32 reduction, FP32 epilogue,
 // per-rank BF16 rounding of the finalize; "Details": no FMA contraction --
@@ -91,10 +92,31 @@ __device__ __forceinline__ void load_gamma(const float4* g, int v, float (&out)[
     out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
 }
 
+// One DPP lane permutation applied to a double (two 32-bit DPP moves).
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+    const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, 0xF, 0xF, false);
+    return __hiloint2double(hi, lo);
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+    const int lo = __builtin_amdgcn_readlane(__double2loint(v), lane);
+    const int hi = __builtin_amdgcn_readlane(__double2hiint(v), lane);
+    return __hiloint2double(hi, lo);
+}
+
 // Sum of one double per lane over the workgroup, the same bits in every lane.
+// Within a 16-lane row: DPP swaps (lane ^ 1, ^ 2, then the half-row and row
+// mirrors), each step adding two equal partial sums in either order, so all
+// 16 lanes hold identical bits; the four row sums are then read out and
+// added in row order; the waves' sums meet in LDS and are added in wave order.
 __device__ __forceinline__ double block_sum(double v, double* slots) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    v = v + dpp_f64<0xB1>(v);   // quad_perm [1,0,3,2]
+    v = v + dpp_f64<0x4E>(v);   // quad_perm [2,3,0,1]
+    v = v + dpp_f64<0x141>(v);  // row_half_mirror
+    v = v + dpp_f64<0x140>(v);  // row_mirror
+    v = ((readlane_f64(v, 0) + readlane_f64(v, 16)) + readlane_f64(v, 32)) + readlane_f64(v, 48);
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     if (lane == 0) slots[wave] = v;
