@@ -238,6 +238,11 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy (counter calibration)")
+    ap.add_argument("--workload", default=None,
+                    help="time another workload than the headline one (by name; for "
+                         "profiling runs -- the contract line is the default)")
+    ap.add_argument("--tokens", type=int, default=None, help="T for --workload")
+    ap.add_argument("--split", action="store_true", help="with --workload: the split path")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -252,7 +257,15 @@ def main():
     torch.cuda.set_device(dev)
 
     cid, T = HEADLINE
-    run = Runner(cid, T, dev, cold=True)
+    if args.workload is not None:
+        import workloads
+        byname = {w.name: c for c, w in workloads.WORKLOADS.items()}
+        if args.workload not in byname:
+            print(f"unknown workload {args.workload!r}; known: {sorted(byname)}", file=sys.stderr)
+            sys.exit(2)
+        cid = byname[args.workload]
+        T = args.tokens or workloads.WORKLOADS[cid].tokens[-1]
+    run = Runner(cid, T, dev, cold=True, split=args.split)
     for i in range(args.warmup):
         run.call(i)
     torch.cuda.synchronize()
@@ -281,7 +294,7 @@ def main():
         torch.cuda.synchronize()
 
     digest = kernel_source_digest()
-    traffic = stored_traffic(run.w.name, T, digest)
+    traffic = stored_traffic(run.w.name + ("_split" if args.split else ""), T, digest)
     out = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -297,7 +310,8 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": run.w.name, "T": T, "H": run.w.H, "R": run.w.R,
+        "config": {"workload": run.w.name + ("_split" if args.split else ""), "T": T,
+                   "H": run.w.H, "R": run.w.R, "k": run.w.k,
                    "epilogue": run.w.epilogue, "storage": "bf16",
                    "algorithmic_bytes_per_call": run.bytes,
                    "rotating_sets": len(run.sets), "parallelism": "single GPU"},
@@ -312,7 +326,7 @@ def main():
         out["sweep"] = sweep(dev)
     if args.all:
         out["other_configs"] = extra_configs(dev)
-    if not args.no_cpu:
+    if not args.no_cpu and args.workload is None:
         base = Runner(cid, T, dev, cold=False)
         out["cpu_baseline"] = cpu_baseline(base)
         del base
