@@ -205,6 +205,35 @@ frn_status frn_moe_finalize(const void* const* expert_rows, const void* const* s
 frn_status frn_query(int32_t R, int32_t k, int64_t T, int64_t H, int32_t epilogue);
 
 /*
+ * Tuned launch shapes.  Each call launches one workgroup per token row
+ * whose lanes own 1, 2 or 4 vectors of 8 BF16 values ("vec"); the best vec
+ * depends on H, R, k, the epilogue and T, and shapes tuned for one hidden
+ * size do not carry over to another (SGLang PR #34134: the shipped H=8192
+ * profiles misfit H=6144).  A built-in rule, measured on MI355X, applies
+ * unless a table of tuned rules overrides it.  Table text: one rule per
+ * line, '#' starts a comment:
+ *     H  R  k  epilogue  Tmin  Tmax  vec
+ * H, R, k, Tmin, Tmax: integers or '*' (any); k = 0 means no finalize;
+ * epilogue: rmsnorm | sandwich | sum (split pass 1) | *; vec: 1 | 2 | 4.
+ * The first rule that matches a call and fits it (at most 1024 lanes; vec 4
+ * only without finalize and outside split pass 1) decides.  Results are
+ * identical for every shape; only speed changes.  tp_reduction_rmsnorm_amd/
+ * tune.py measures a table.  frn_set_launch_table(NULL) restores the
+ * built-in rule; an unparsable text returns FRN_ERR_INVALID (the line is in
+ * frn_last_error) and leaves the table as it was.  If no table was set
+ * before the first launch, the file named by the environment variable
+ * FRN_LAUNCH_TABLE (if any) is loaded.  Thread-safe; affects later launches
+ * only.
+ */
+frn_status frn_set_launch_table(const char* text);
+
+/* The shape (lanes per workgroup, vectors per lane) the one-row kernel gets
+ * for a call of these sizes, without launching.  threads, vectors: host
+ * pointers to receive the values. */
+frn_status frn_launch_shape(int32_t R, int32_t k, int64_t T, int64_t H, int32_t epilogue,
+                            int32_t* threads, int32_t* vectors);
+
+/*
  * Bytes of the optional workspace argument of the fused calls for calls of
  * up to max_T tokens (0: the call never uses one).  Today only the MoE
  * finalize (k > 0) uses it: for T <= 256 the finalize of each (token, rank,

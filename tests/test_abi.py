@@ -297,3 +297,84 @@ def test_python_layer_requires_gpu_tensors():
         frn.reduce_residual_rmsnorm([p, p], None, g)
     with pytest.raises(TypeError):
         frn.reduce_residual_rmsnorm([p.float()], p, g)
+
+
+# ------------------------------------------------------- launch tables --- #
+
+def test_launch_shape_builtin_rule():
+    import tp_reduction_rmsnorm_amd as frn
+    frn.set_launch_table(None)
+    S = frn.EPI_SANDWICH
+    assert frn.launch_shape(4, 0, 1, 5120, S) == (640, 1)      # small T: <= 640 lanes
+    assert frn.launch_shape(8, 0, 8, 8192, S) == (512, 2)
+    assert frn.launch_shape(4, 0, 1024, 5120, S) == (192, 4)   # mid T: four vectors
+    assert frn.launch_shape(4, 0, 4096, 5120, S) == (320, 2)   # large T
+    assert frn.launch_shape(8, 0, 4096, 8192, S) == (256, 4)   # long rows: four up to 4096
+    assert frn.launch_shape(8, 0, 16384, 8192, S) == (512, 2)
+    assert frn.launch_shape(2, 8, 4096, 7168, 0) == (896, 1)   # finalize: one vector
+    assert frn.launch_shape(2, 8, 1024, 7168, 0) == (448, 2)   # ... two at mid T
+    assert frn.launch_shape(2, 8, 1024, 7168, frn.EPI_SUM) == (896, 1)
+    assert frn.launch_shape(2, 0, 1024, 7168, frn.EPI_SUM) == (448, 2)  # no 4 in pass 1
+    assert frn.launch_shape(2, 0, 8, 16384, S) == (1024, 2)
+
+
+def test_launch_table_overrides_and_restores():
+    import tp_reduction_rmsnorm_amd as frn
+    try:
+        frn.set_launch_table("""
+            # comment line
+            5120 4 0 sandwich 1000 5000 1   # exact shape, T range
+            * * 0 * 0 * 4                   # any shape without finalize
+            * * * * 0 * 2
+        """)
+        S = frn.EPI_SANDWICH
+        assert frn.launch_shape(4, 0, 4096, 5120, S) == (640, 1)
+        assert frn.launch_shape(4, 0, 8, 5120, S) == (192, 4)      # second rule
+        assert frn.launch_shape(8, 0, 8, 8192, S) == (256, 4)
+        # vec 4 does not fit a finalize or pass 1: the next fitting rule decides
+        assert frn.launch_shape(8, 10, 8, 6144, 0) == (384, 2)
+        assert frn.launch_shape(2, 0, 8, 7168, frn.EPI_SUM) == (448, 2)
+        # a rule that would need more than 1024 lanes is skipped
+        frn.set_launch_table("* * * * 0 * 1")
+        assert frn.launch_shape(2, 0, 8, 16384, S) == (1024, 2)
+        with pytest.raises(ValueError, match="line 2"):
+            frn.set_launch_table("* * * * 0 * 1\n5120 4 0 sandwich 1 2 3\n")
+        assert frn.launch_shape(4, 0, 8, 5120, S) == (640, 1)      # unchanged by the failure
+    finally:
+        frn.set_launch_table(None)
+    assert frn.launch_shape(4, 0, 4096, 5120, frn.EPI_SANDWICH) == (320, 2)
+
+
+ENV_TABLE_SCRIPT = r"""
+import sys
+sys.path.insert(0, {root!r})
+import tp_reduction_rmsnorm_amd as frn
+print(frn.launch_shape(4, 0, 4096, 5120, frn.EPI_SANDWICH))
+"""
+
+
+def test_launch_table_from_environment(tmp_path):
+    table = tmp_path / "table.txt"
+    table.write_text("5120 4 0 sandwich 0 * 4\n")
+    env = dict(os.environ, FRN_LAUNCH_TABLE=str(table))
+    r = subprocess.run([sys.executable, "-c", ENV_TABLE_SCRIPT.format(root=ROOT)], env=env,
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.strip() == "(192, 4)"
+    table.write_text("not a table\n")
+    r = subprocess.run([sys.executable, "-c", ENV_TABLE_SCRIPT.format(root=ROOT)], env=env,
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0 and r.stdout.strip() == "(320, 2)"
+    assert "launch table line 1" in r.stderr
+
+
+def test_tuner_merges_rules():
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "frn_tune", os.path.join(ROOT, "tp_reduction_rmsnorm_amd", "tune.py"))
+    tune = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(tune)
+    rows = [(1, 1, {}), (8, 1, {}), (64, 2, {}), (1024, 4, {}), (4096, 2, {})]
+    assert tune.rules_for(5120, 4, 0, "sandwich", rows) == [
+        "5120 4 0 sandwich 0 8 1", "5120 4 0 sandwich 9 64 2",
+        "5120 4 0 sandwich 65 1024 4", "5120 4 0 sandwich 1025 * 2"]

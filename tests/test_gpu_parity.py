@@ -488,3 +488,51 @@ def test_split_row_graph_replay():
         g.replay()
         torch.cuda.synchronize()
         check(f"split-row graph replay {rep}", out, rout, oracle_ref(new))
+
+
+# ------------------------------------------------------ launch shapes --- #
+
+SHAPE_CASES = [(4, 300, 5120, "sandwich", 0, False), (3, 7, 5128, "rmsnorm", 0, False),
+               (8, 40, 8192, "sandwich", 0, False), (2, 260, 7168, "rmsnorm", 8, True),
+               (16, 5, 16384, "rmsnorm", 0, False)]
+
+
+@pytest.mark.parametrize("vec", [1, 2, 4])
+def test_results_do_not_depend_on_launch_shape(vec):
+    """Force every vectors-per-lane choice through a launch table: fused and
+    split results stay equal to the oracle (rules that do not fit a call are
+    skipped, so the built-in rule takes over there)."""
+    m = frn()
+    try:
+        m.set_launch_table(f"* * * * 0 * {vec}")
+        for case in SHAPE_CASES:
+            R, T, H, epi, k, sh = case
+            log(f"launch shape vec={vec} {mid_id(case)} -> {m.launch_shape(R, k, T, H)}")
+            inp = workloads.make(R, T, H, epilogue=epi, sigma=0.5, k=k, shared=sh,
+                                 seed=3000 + vec * 11 + T)
+            d = to_dev(inp)
+            y, x = gpu_fused(d)
+            check(f"vec={vec} fused {mid_id(case)}", y, x, oracle_ref(inp))
+            y, x = gpu_split(d)
+            check(f"vec={vec} split {mid_id(case)}", y, x, oracle_ref(inp, split=True))
+    finally:
+        m.set_launch_table(None)
+
+
+def test_tuner_writes_a_loadable_table(tmp_path):
+    import importlib.util
+    import os
+    spec = importlib.util.spec_from_file_location(
+        "frn_tune", os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                                 "tp_reduction_rmsnorm_amd", "tune.py"))
+    tune = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(tune)
+    rows = tune.tune_shape(512, 2, 0, "rmsnorm", [1, 300], 4, DEV, log=log)
+    assert [r[0] for r in rows] == [1, 300] and all(r[1] in r[2] for r in rows)
+    text = "\n".join(tune.rules_for(512, 2, 0, "rmsnorm", rows))
+    m = frn()
+    try:
+        m.set_launch_table(text)
+        assert m.launch_shape(2, 0, 300, 512)[1] == rows[1][1]
+    finally:
+        m.set_launch_table(None)

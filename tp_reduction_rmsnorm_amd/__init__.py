@@ -17,6 +17,7 @@ Function names are the C entry points without their ``frn_`` prefix:
 * ``split_reduce_norm``          both passes of the split path
 * ``moe_finalize``               the per-rank finalize alone (materialized)
 * ``query``, ``workspace_bytes``, ``version``
+* ``set_launch_table``, ``launch_shape``  tuned launch shapes (tune.py)
 
 Every call returns its outputs.  A declined call raises
 ``FusedReduceNormUnsupported``; it never returns unreduced data.  (The pages
@@ -90,6 +91,9 @@ _c_split = _sig("frn_split_reduce_norm", ctypes.c_int,
 _c_finalize = _sig("frn_moe_finalize", ctypes.c_int,
                    [_P, _P, _I32, _P, _P, _I32, _I64, _I64, _I64, _P, _P])
 _c_query = _sig("frn_query", ctypes.c_int, [_I32, _I32, _I64, _I64, _I32])
+_c_set_table = _sig("frn_set_launch_table", ctypes.c_int, [ctypes.c_char_p])
+_c_shape = _sig("frn_launch_shape", ctypes.c_int,
+                [_I32, _I32, _I64, _I64, _I32, ctypes.POINTER(_I32), ctypes.POINTER(_I32)])
 _c_ws = _sig("frn_workspace_bytes", _SZ, [_I64, _I64, _I32, _I32])
 _c_status = _sig("frn_status_string", ctypes.c_char_p, [ctypes.c_int])
 _c_last = _sig("frn_last_error", ctypes.c_char_p, [])
@@ -98,7 +102,7 @@ _c_version = _sig("frn_version", ctypes.c_char_p, [])
 C_FUNCTIONS = ("frn_reduce_residual_rmsnorm", "frn_reduce_sandwich_norm",
                "frn_moe_finalize_reduce_norm", "frn_reduce_bf16",
                "frn_moe_finalize_reduce_bf16", "frn_split_reduce_norm", "frn_moe_finalize",
-               "frn_query",
+               "frn_query", "frn_set_launch_table", "frn_launch_shape",
                "frn_workspace_bytes", "frn_status_string", "frn_last_error", "frn_version")
 
 
@@ -127,6 +131,22 @@ def query(R: int, k: int, T: int, H: int, epilogue: int = EPI_RMSNORM) -> bool:
 
 def workspace_bytes(max_T: int, H: int, R: int, k: int = 0) -> int:
     return int(_c_ws(max_T, H, R, k))
+
+
+EPI_SUM = 2  # split pass 1, for launch tables and launch_shape
+
+
+def set_launch_table(text: Optional[str]) -> None:
+    """Load tuned launch rules ('H R k epilogue Tmin Tmax vec' per line), or
+    None to restore the built-in rule.  Raises ValueError on bad text."""
+    _check(_c_set_table(None if text is None else text.encode()))
+
+
+def launch_shape(R: int, k: int, T: int, H: int, epilogue: int = EPI_RMSNORM):
+    """(lanes per workgroup, vectors per lane) the one-row kernel would use."""
+    th, v = _I32(), _I32()
+    _check(_c_shape(R, k, T, H, epilogue, ctypes.byref(th), ctypes.byref(v)))
+    return th.value, v.value
 
 
 # ---------------------------------------------------------------- helpers --- #

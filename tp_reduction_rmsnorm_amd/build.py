@@ -20,7 +20,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfused_reduce_norm.so")
-SOURCES = [os.path.join(CSRC, f) for f in ("frn_kernels.hip", "frn_api.hip")]
+SOURCES = [os.path.join(CSRC, f) for f in ("frn_kernels.hip", "frn_shapes.hip", "frn_api.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

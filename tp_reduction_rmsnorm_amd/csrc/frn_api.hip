@@ -363,6 +363,27 @@ FRN_API frn_status frn_moe_finalize(const void* const* expert_rows, const void* 
     return FRN_OK;
 }
 
+FRN_API frn_status frn_set_launch_table(const char* text) {
+    g_last_error[0] = '\0';
+    const char* err = frn::set_launch_table(text);
+    if (err != nullptr) return fail(FRN_ERR_INVALID, "%s", err);
+    return FRN_OK;
+}
+
+FRN_API frn_status frn_launch_shape(int32_t R, int32_t k, int64_t T, int64_t H, int32_t epilogue,
+                                    int32_t* threads, int32_t* vectors) {
+    g_last_error[0] = '\0';
+    frn_status st = check_sizes(R, k, T, H, epilogue);
+    if (st != FRN_OK) return st;
+    if (threads == nullptr || vectors == nullptr)
+        return fail(FRN_ERR_INVALID, "threads and vectors must not be NULL");
+    const frn::LaunchShape sh =
+        frn::choose_shape((int)(H / 8), k > 0, T, epilogue, R, k);
+    *threads = sh.threads;
+    *vectors = sh.vec;
+    return FRN_OK;
+}
+
 FRN_API frn_status frn_query(int32_t R, int32_t k, int64_t T, int64_t H, int32_t epilogue) {
     g_last_error[0] = '\0';
     return check_sizes(R, k, T, H, epilogue);

@@ -65,7 +65,14 @@ struct LaunchShape {
     int vec;
 };
 
-LaunchShape choose_shape(int nvec, bool finalize, int64_t T, int epilogue);
+// Launch shape of row_kernel for a call: the first matching rule of the
+// tuned table (frn_set_launch_table / FRN_LAUNCH_TABLE) that fits the call,
+// else the built-in rule.  Thread-safe.
+LaunchShape choose_shape(int nvec, bool finalize, int64_t T, int epilogue, int R, int k);
+
+// Replace the tuned table (text as documented at frn_set_launch_table; NULL
+// clears it).  Returns nullptr on success, else a message naming the line.
+const char* set_launch_table(const char* text);
 
 // Enqueue the boundary kernel for T rows.  Returns the HIP launch status.
 hipError_t launch_rows(const RowArgs& a, int epilogue, int64_t T, hipStream_t stream);

@@ -34,8 +34,6 @@
 //   rmsnorm    h = s + x; y = (h * rinv(h)) * gamma
 //   sandwich   a = (s * rinv(s)) * gamma1; h = a + x; y = (h * rinv(h)) * gamma2
 // No MFMA: nothing here is a dense contraction; the kernels are bound by HBM.
-#include <stdlib.h>
-
 #include "frn_internal.h"
 
 namespace frn {
@@ -444,38 +442,6 @@ hipError_t launch_finalize(const RowArgs& a, int64_t T, hipStream_t stream) {
     return hipGetLastError();
 }
 
-LaunchShape choose_shape(int nvec, bool finalize, int64_t T, int epilogue) {
-    // Vectors per lane, from a sweep of the sandwich workloads on MI355X
-    // (graph replay; H=5120 R=4 and H=8192 R=8):
-    //  - small T (<= 256, latency-bound): the fewest vectors that keep a row
-    //    within 640 lanes -- more lanes issue the row's loads at once
-    //    (H=5120 T=1: 4.3 us with one vector, 4.6 with two);
-    //  - 256 < T <= 1024 (every row resident at once): four vectors, fewer
-    //    waves per row to synchronise (H=5120 T=1024: 15.6 -> 14.6 us);
-    //  - T > 1024: two vectors for rows over 512 vectors (H=5120 T=4096:
-    //    54 us with two, 55 with four, 60 with one).
-    // A finalize holds more live state per vector, so it keeps one vector
-    // per lane up to 1024 lanes.  FRN_VEC=1|2|4 overrides (tuning aid).
-    static const int forced = [] {
-        const char* e = getenv("FRN_VEC");
-        return (e && (e[0] == '1' || e[0] == '2' || e[0] == '4')) ? e[0] - '0' : 0;
-    }();
-    LaunchShape sh;
-    if (finalize)
-        sh.vec = nvec <= 1024 ? 1 : 2;
-    else if (T <= 256)
-        sh.vec = nvec <= 640 ? 1 : 2;
-    else if (T <= 1024 && nvec >= 512 && epilogue != kStoreSum)
-        sh.vec = 4;
-    else
-        sh.vec = nvec <= 512 ? 1 : 2;
-    if (forced && (nvec + forced - 1) / forced <= 1024 &&
-        !(forced == 4 && (finalize || epilogue == kStoreSum)))
-        sh.vec = forced;
-    const int lanes = (nvec + sh.vec - 1) / sh.vec;
-    sh.threads = ((lanes + 63) / 64) * 64;
-    return sh;
-}
 
 hipError_t launch_rows(const RowArgs& a_in, int epilogue, int64_t T, hipStream_t stream) {
     RowArgs a = a_in;
@@ -490,7 +456,7 @@ hipError_t launch_rows(const RowArgs& a_in, int epilogue, int64_t T, hipStream_t
         a.has_shared = 0;
     }
     const bool fin = a.k > 0;
-    const LaunchShape sh = choose_shape(a.nvec, fin, T, epilogue);
+    const LaunchShape sh = choose_shape(a.nvec, fin, T, epilogue, a.R, a.k);
     switch (epilogue) {
         case kRmsNorm:
             return fin ? launch_v<kRmsNorm, true>(a, T, sh, stream)

@@ -1,0 +1,195 @@
+// frn_shapes.hip -- launch shapes of row_kernel: the built-in rule measured
+// on MI355X, and an optional table of tuned rules that overrides it.  Launch
+// profiles tuned for one hidden size do not carry over to another (SGLang PR
+// #34134: shipped profiles for H=8192 misfit H=6144), so a deployment can
+// measure its own shapes (tp_reduction_rmsnorm_amd/tune.py) and load them.
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "frn_internal.h"
+
+namespace frn {
+namespace {
+
+// One tuned rule; -1 in H, R, k, epilogue means "any".  T in [tmin, tmax].
+struct Rule {
+    int64_t H, R, k, epilogue;
+    int64_t tmin, tmax;
+    int vec;
+};
+
+std::mutex g_mu;
+std::vector<Rule> g_rules;
+bool g_env_checked = false;
+std::string g_parse_error;
+
+bool parse_field(const char* tok, int64_t* out) {
+    if (strcmp(tok, "*") == 0) {
+        *out = -1;
+        return true;
+    }
+    char* end = nullptr;
+    const long long v = strtoll(tok, &end, 10);
+    if (end == tok || *end != '\0' || v < 0) return false;
+    *out = v;
+    return true;
+}
+
+bool parse_epilogue(const char* tok, int64_t* out) {
+    if (strcmp(tok, "*") == 0) *out = -1;
+    else if (strcmp(tok, "rmsnorm") == 0) *out = kRmsNorm;
+    else if (strcmp(tok, "sandwich") == 0) *out = kSandwich;
+    else if (strcmp(tok, "sum") == 0) *out = kStoreSum;
+    else return false;
+    return true;
+}
+
+// Parse the whole text into `out`; on error return false with a message.
+bool parse(const char* text, std::vector<Rule>& out, std::string& err) {
+    out.clear();
+    int lineno = 0;
+    const char* p = text;
+    while (*p) {
+        const char* eol = strchr(p, '\n');
+        std::string line = eol ? std::string(p, eol - p) : std::string(p);
+        p = eol ? eol + 1 : p + line.size();
+        ++lineno;
+        const size_t hash = line.find('#');
+        if (hash != std::string::npos) line.resize(hash);
+        std::vector<std::string> tok;
+        size_t i = 0;
+        while (i < line.size()) {
+            while (i < line.size() && (line[i] == ' ' || line[i] == '\t' || line[i] == '\r')) ++i;
+            size_t j = i;
+            while (j < line.size() && line[j] != ' ' && line[j] != '\t' && line[j] != '\r') ++j;
+            if (j > i) tok.push_back(line.substr(i, j - i));
+            i = j;
+        }
+        if (tok.empty()) continue;
+        Rule r{};
+        int64_t vec = 0;
+        if (tok.size() != 7 || !parse_field(tok[0].c_str(), &r.H) ||
+            !parse_field(tok[1].c_str(), &r.R) || !parse_field(tok[2].c_str(), &r.k) ||
+            !parse_epilogue(tok[3].c_str(), &r.epilogue) ||
+            !parse_field(tok[4].c_str(), &r.tmin) || !parse_field(tok[5].c_str(), &r.tmax) ||
+            !parse_field(tok[6].c_str(), &vec) || !(vec == 1 || vec == 2 || vec == 4)) {
+            err = "launch table line " + std::to_string(lineno) +
+                  ": expected 'H R k epilogue Tmin Tmax vec' (numbers or *, epilogue "
+                  "rmsnorm|sandwich|sum|*, vec 1|2|4)";
+            return false;
+        }
+        if (r.tmin < 0) r.tmin = 0;
+        if (r.tmax < 0) r.tmax = INT64_MAX;
+        r.vec = (int)vec;
+        out.push_back(r);
+    }
+    return true;
+}
+
+// FRN_LAUNCH_TABLE names a table file read at the first launch, unless a
+// table was set through the API first.  A file that does not parse is
+// ignored, with one line on stderr.
+void load_env_table_locked() {
+    if (g_env_checked) return;
+    g_env_checked = true;
+    const char* path = getenv("FRN_LAUNCH_TABLE");
+    if (path == nullptr || path[0] == '\0') return;
+    FILE* f = fopen(path, "rb");
+    if (f == nullptr) {
+        fprintf(stderr, "fused_reduce_norm: cannot open FRN_LAUNCH_TABLE=%s; using built-in shapes\n",
+                path);
+        return;
+    }
+    std::string text;
+    char buf[4096];
+    size_t n;
+    while ((n = fread(buf, 1, sizeof buf, f)) > 0) text.append(buf, n);
+    fclose(f);
+    std::vector<Rule> rules;
+    std::string err;
+    if (!parse(text.c_str(), rules, err)) {
+        fprintf(stderr, "fused_reduce_norm: %s (%s); using built-in shapes\n", err.c_str(), path);
+        return;
+    }
+    g_rules.swap(rules);
+}
+
+// The built-in rule, from graph-replay sweeps on MI355X (the sandwich
+// workloads H=5120 R=4 and H=8192 R=8 by hand, then tune.py over the five
+// measured shapes):
+//  - small T (<= 256, latency-bound): the fewest vectors that keep a row
+//    within 640 lanes -- more lanes issue the row's loads at once
+//    (H=5120 T=1: 4.0 us with one vector, 4.4 with two);
+//  - larger T without finalize: four vectors per lane for rows of 512+
+//    vectors up to T = 1024, and for rows of 768+ vectors (H >= 6144) up to
+//    T = 4096 -- fewer waves per row to synchronise (H=5120 T=1024: 15.4 ->
+//    14.7 us; H=8192 T=512: 18.8 -> 17.7 us, T=4096: 119.2 -> 117.4 us);
+//    beyond that two vectors for rows over 512 vectors;
+//  - with finalize, one vector per lane up to 1024 lanes, except two for
+//    256 < T <= 2048 outside split pass 1 (H=7168 R=2 k=8: T=512 30.0 ->
+//    27.4 us, T=1024 57.4 -> 53.4 us; at T=4096 one vector is ahead again).
+// Four vectors are never used with the finalize (too many live registers)
+// or for split pass 1 (it spills).
+int builtin_vec(int nvec, bool finalize, int64_t T, int epilogue) {
+    if (finalize) {
+        if (T > 256 && T <= 2048 && epilogue != kStoreSum && nvec <= 2048) return 2;
+        return nvec <= 1024 ? 1 : 2;
+    }
+    if (T <= 256) return nvec <= 640 ? 1 : 2;
+    if (epilogue != kStoreSum && nvec >= 512 && (T <= 1024 || (nvec >= 768 && T <= 4096)))
+        return 4;
+    return nvec <= 512 ? 1 : 2;
+}
+
+// A tuned vec must fit the kernels that exist: at most 1024 lanes, and four
+// vectors only without finalize and outside split pass 1.
+bool vec_fits(int vec, int nvec, bool finalize, int epilogue) {
+    if ((nvec + vec - 1) / vec > 1024) return false;
+    if (vec == 4 && (finalize || epilogue == kStoreSum)) return false;
+    return true;
+}
+
+}  // namespace
+
+LaunchShape choose_shape(int nvec, bool finalize, int64_t T, int epilogue, int R, int k) {
+    int vec = 0;
+    {
+        std::lock_guard<std::mutex> lock(g_mu);
+        load_env_table_locked();
+        const int64_t H = (int64_t)nvec * 8;
+        for (const Rule& r : g_rules) {
+            if ((r.H < 0 || r.H == H) && (r.R < 0 || r.R == R) && (r.k < 0 || r.k == k) &&
+                (r.epilogue < 0 || r.epilogue == epilogue) && T >= r.tmin && T <= r.tmax &&
+                vec_fits(r.vec, nvec, finalize, epilogue)) {
+                vec = r.vec;
+                break;
+            }
+        }
+    }
+    if (vec == 0) vec = builtin_vec(nvec, finalize, T, epilogue);
+    LaunchShape sh;
+    sh.vec = vec;
+    const int lanes = (nvec + vec - 1) / vec;
+    sh.threads = ((lanes + 63) / 64) * 64;
+    return sh;
+}
+
+const char* set_launch_table(const char* text) {
+    std::lock_guard<std::mutex> lock(g_mu);
+    g_env_checked = true;  // an explicit table replaces the environment's
+    if (text == nullptr) {
+        g_rules.clear();
+        return nullptr;
+    }
+    std::vector<Rule> rules;
+    if (!parse(text, rules, g_parse_error)) return g_parse_error.c_str();
+    g_rules.swap(rules);
+    return nullptr;
+}
+
+}  // namespace frn

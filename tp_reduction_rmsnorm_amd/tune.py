@@ -1,0 +1,172 @@
+"""Measure launch shapes on the local GPU and write a launch table.
+
+    python tp_reduction_rmsnorm_amd/tune.py --out frn_launch_table.txt \\
+        [--shape H R k epilogue ...] [--tokens T ...] [--calls 20]
+
+For every shape and token count, each vectors-per-lane choice that fits is
+forced through ``set_launch_table`` and timed the way the pages time this
+operation (vLLM PR #62366, kernel microbenchmark table): a HIP graph holding
+``--calls`` calls, median of 5 replays.  Inputs are random BF16 tensors
+rotated over at least 1 GiB from T >= 256, so the timings are not served
+from the Infinity Cache.  The fastest choice per T becomes a rule covering
+the T range up to it; neighbouring ranges with the same choice merge.  Load
+the table with ``FRN_LAUNCH_TABLE=<file>`` or ``set_launch_table(text)``.
+
+Shapes without finalize (k = 0) tune every call of that shape; with k > 0
+the rules matter above T = 256 (below it the finalize runs split-row and
+its reduction pass is a k = 0 call of the same H and R).
+"""
+from __future__ import annotations
+
+import argparse
+import os
+import sys
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, os.path.dirname(HERE))
+
+import tp_reduction_rmsnorm_amd as frn  # noqa: E402
+
+EPI = {"rmsnorm": frn.EPI_RMSNORM, "sandwich": frn.EPI_SANDWICH, "sum": frn.EPI_SUM}
+DEFAULT_SHAPES = [(5120, 4, 0, "sandwich"), (8192, 8, 0, "sandwich"), (512, 2, 0, "rmsnorm"),
+                  (6144, 8, 0, "rmsnorm"), (7168, 2, 8, "rmsnorm"), (7168, 2, 0, "rmsnorm"),
+                  (7168, 2, 8, "sum")]
+DEFAULT_TOKENS = [1, 8, 64, 256, 512, 1024, 2048, 4096, 16384]
+
+
+def _bf16(shape, dev, g):
+    return torch.randn(shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+
+
+class Call:
+    """Rotating input sets of one shape and the library call on them."""
+
+    def __init__(self, H, R, k, epi, T, dev):
+        g = torch.Generator(device=dev)
+        g.manual_seed(H * 131 + R * 17 + k * 7 + T)
+        per_set = T * H * 2 * (R * (k + 1 if k else 1) + 3)
+        n = max(1, min(16, -(-(1 << 30) // per_set))) if T >= 256 else 1
+        self.H, self.R, self.k, self.epi, self.T = H, R, k, epi, T
+        self.sets = []
+        for _ in range(n):
+            d = dict(residual=_bf16((T, H), dev, g), g1=torch.rand(H, generator=g, device=dev) + 0.5,
+                     g2=torch.rand(H, generator=g, device=dev) + 0.5,
+                     out=torch.empty(T, H, dtype=torch.bfloat16, device=dev),
+                     rout=torch.empty(T, H, dtype=torch.bfloat16, device=dev))
+            if k:
+                d["src"] = [_bf16((T * k, H), dev, g) for _ in range(R)]
+                d["shared"] = [_bf16((T, H), dev, g) for _ in range(R)]
+                d["w"] = torch.softmax(torch.randn(T, k, generator=g, device=dev), -1)
+                d["idx"] = torch.randperm(T * k, generator=g, device=dev).to(torch.int32).reshape(T, k)
+            else:
+                d["src"] = [_bf16((T, H), dev, g) for _ in range(R)]
+            self.sets.append(d)
+
+    def __call__(self, i):
+        d = self.sets[i % len(self.sets)]
+        if self.epi == "sum":
+            if self.k:
+                return frn.moe_finalize_reduce_bf16(d["src"], d["w"], d["idx"], shared=d["shared"],
+                                                    out=d["out"])
+            return frn.reduce_bf16(d["src"], out=d["out"])
+        if self.k:
+            return frn.moe_finalize_reduce_norm(d["src"], d["w"], d["idx"], d["residual"], d["g1"],
+                                                d["g2"], shared=d["shared"], epilogue=EPI[self.epi],
+                                                out=d["out"], residual_out=d["rout"],
+                                                workspace=None)
+        if self.epi == "sandwich":
+            return frn.reduce_sandwich_norm(d["src"], d["residual"], d["g1"], d["g2"],
+                                            out=d["out"], residual_out=d["rout"])
+        return frn.reduce_residual_rmsnorm(d["src"], d["residual"], d["g1"], out=d["out"],
+                                           residual_out=d["rout"])
+
+
+def graph_us(call: Call, calls: int) -> float:
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(3):
+            call(i)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(calls):
+            call(i)
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3 / calls)
+    del g
+    return sorted(ts)[2]
+
+
+def tune_shape(H, R, k, epi, tokens, calls, dev, log=print):
+    """[(T, best_vec, {vec: us})] for one shape."""
+    rows = []
+    for T in tokens:
+        call = Call(H, R, k, epi, T, dev)
+        times = {}
+        for vec in (1, 2, 4):
+            frn.set_launch_table(f"{H} {R} {k} {epi} {T} {T} {vec}")
+            if frn.launch_shape(R, k, T, H, EPI[epi])[1] != vec:
+                continue  # does not fit this call
+            times[vec] = graph_us(call, calls)
+        frn.set_launch_table(None)
+        best = min(times, key=times.get)
+        rows.append((T, best, times))
+        log(f"H={H} R={R} k={k} {epi} T={T}: " +
+            ", ".join(f"vec {v}: {us:.2f} us" for v, us in sorted(times.items())) + f" -> {best}")
+        del call
+        torch.cuda.empty_cache()
+    return rows
+
+
+def rules_for(H, R, k, epi, rows):
+    """Merge per-T winners into 'H R k epilogue Tmin Tmax vec' lines."""
+    out = []
+    lo = 0
+    for i, (T, best, _) in enumerate(rows):
+        hi = "*" if i == len(rows) - 1 else str(T)
+        if out and out[-1][2] == best:
+            out[-1][1] = hi
+        else:
+            out.append([lo, hi, best])
+        lo = T + 1
+    return [f"{H} {R} {k} {epi} {a} {b} {v}" for a, b, v in out]
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--out", required=True)
+    ap.add_argument("--shape", nargs=4, action="append", metavar=("H", "R", "k", "EPILOGUE"))
+    ap.add_argument("--tokens", nargs="+", type=int, default=DEFAULT_TOKENS)
+    ap.add_argument("--calls", type=int, default=20)
+    args = ap.parse_args()
+    shapes = ([(int(h), int(r), int(k), e) for h, r, k, e in args.shape] if args.shape
+              else DEFAULT_SHAPES)
+    dev = torch.device("cuda:0")
+    lines = ["# fused_reduce_norm launch table: H R k epilogue Tmin Tmax vec",
+             f"# measured on {torch.cuda.get_device_name(dev)} ({torch.cuda.get_device_properties(dev).gcnArchName.split(':')[0]})"
+             f" with: python tp_reduction_rmsnorm_amd/tune.py {' '.join(sys.argv[1:])}",
+             f"# graph replay of {args.calls} calls, median of 5.  Load with FRN_LAUNCH_TABLE=<file>."]
+    for H, R, k, epi in shapes:
+        rows = tune_shape(H, R, k, epi, sorted(set(args.tokens)), args.calls, dev)
+        lines += rules_for(H, R, k, epi, rows)
+    with open(args.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    frn.set_launch_table(open(args.out).read())  # validates the file
+    print(f"wrote {args.out}", flush=True)
+
+
+if __name__ == "__main__":
+    main()
