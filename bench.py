@@ -17,8 +17,11 @@ Printed: ONE JSON line with the contract fields plus
   * ``sweep``: µs/call and GB/s over T = 1..4096 at H=5120 (R=4) and H=8192
     (R=8), each the median of 5 replays of a HIP graph holding 20 calls (the
     measuring method of the pages' microbenchmark table, vLLM PR #62366);
-  * ``cpu_baseline``: the CPU oracle timed on the host cores on a bounded
-    sample of the same workload.
+  * ``cpu_baseline``: the CPU oracle timed on the host cores (and on one)
+    on a bounded sample of the same workload, with the largest BF16 ulp
+    distance between its rows and the GPU's timed outputs of those rows;
+  * ``roofline.measured_copy_GBps``: a plain 1 GiB device copy on the same
+    GPU, the practical streaming rate, as a second reference line.
 
 The GPU runs one process on one device; ``--gpus N`` with N > 1 exits with a
 message (this build runs on one GPU only).
@@ -184,25 +187,82 @@ def sweep(dev, cids=(2, 3), Ts=SWEEP_T):
 
 
 def extra_configs(dev):
+    """The other workloads.  Where two paths compute the same call (MoE fused
+    against finalize-then-reduce; fused against split), they share one set of
+    inputs and are timed in the order A, B, B, A, each reported as the mean of
+    its two medians, so that neither gains from running second."""
     rows = []
-    for cid, Ts, mode in ((1, (8,), ""), (4, (1, 2, 4, 8, 16, 32, 64), ""),
-                          (4, (1, 8, 64), "unfused"),
-                          (5, (4096, 16384), ""), (5, (4096, 16384), "split")):
+
+    def add(r, T, tag, us):
+        rows.append(dict(workload=r.w.name + (f"_{tag}" if tag else ""), T=T,
+                         us_per_call=round(us, 3), GBps=round(r.bytes / us / 1e3, 1),
+                         frac_of_peak=round(r.bytes / us / 1e3 / PEAK_GBS, 4)))
+        print(json.dumps(dict(extra=rows[-1])), file=sys.stderr, flush=True)
+
+    def pair(r, attr):
+        t = {False: [], True: []}
+        for flag in (False, True, True, False):
+            setattr(r, attr, flag)
+            t[flag].append(r.graph_us())
+        setattr(r, attr, False)
+        return sum(t[False]) / 2, sum(t[True]) / 2
+
+    for cid, Ts in ((1, (8,)), (4, (2, 4, 16, 32))):
         for T in Ts:
-            r = Runner(cid, T, dev, cold=T >= 256, split=mode == "split",
-                       unfused=mode == "unfused")
-            us = r.graph_us()
-            rows.append(dict(workload=r.w.name + (f"_{mode}" if mode else ""), T=T,
-                             us_per_call=round(us, 3), GBps=round(r.bytes / us / 1e3, 1),
-                             frac_of_peak=round(r.bytes / us / 1e3 / PEAK_GBS, 4)))
-            print(json.dumps(dict(extra=rows[-1])), file=sys.stderr, flush=True)
+            r = Runner(cid, T, dev, cold=T >= 256)
+            add(r, T, "", r.graph_us())
             del r
+    for T in (1, 8, 64):
+        r = Runner(4, T, dev, cold=False, unfused=True)
+        fused, unfused = pair(r, "unfused")
+        add(r, T, "", fused)
+        add(r, T, "unfused", unfused)
+        rows[-1]["unfused_over_fused"] = round(unfused / fused, 3)
+        del r
+    for T in (4096, 16384):
+        r = Runner(5, T, dev, cold=True, split=True)
+        fused, split = pair(r, "split")
+        add(r, T, "", fused)
+        add(r, T, "split", split)
+        rows[-1]["split_over_fused"] = round(split / fused, 3)
+        del r
     return rows
 
 
-def cpu_baseline(runner, seconds=10.0):
-    """The CPU oracle, as it is, on a bounded sample of the headline
-    workload (its first 256 token rows), repeated for ~`seconds`."""
+def copy_reference(dev, nbytes=1 << 30):
+    """GB/s of a plain device-to-device copy of `nbytes` (torch ``copy_``),
+    counted as bytes read + bytes written; median of 5 after 2 warm-up."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    ts = []
+    for _ in range(5):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e-3)
+    return 2 * nbytes / sorted(ts)[2] / 1e9
+
+
+def _ordered(bits):
+    """BF16 bit patterns -> integers in the order of their values (+0 = -0)."""
+    import numpy as np
+    b = bits.astype(np.int32)
+    return np.where(b & 0x8000, -(b & 0x7FFF), b)
+
+
+def cpu_baseline(runner, seconds=10.0, single_seconds=5.0):
+    """The CPU oracle, as it is, on a bounded sample of the timed workload:
+    the first 256 token rows of its first input set, repeated for about
+    `seconds` on the host's threads (up to 16) and `single_seconds` on one.
+    The oracle's rows are also compared with the GPU's outputs of those rows
+    from the timed calls (the last timed call on that set)."""
+    import numpy as np
     import oracle
     import workloads
     d = runner.sets[0]
@@ -210,22 +270,33 @@ def cpu_baseline(runner, seconds=10.0):
     w = runner.w
     args = [workloads.bits(p[:rows]) for p in d.partials]
     kw = dict(residual=workloads.bits(d.residual[:rows]), gamma1=workloads.f32(d.gamma1),
-              gamma2=workloads.f32(d.gamma2), eps=d.eps, epilogue=oracle.EPI_SANDWICH)
+              gamma2=workloads.f32(d.gamma2), eps=d.eps,
+              epilogue=oracle.EPI_SANDWICH if w.epilogue == "sandwich" else oracle.EPI_RMSNORM)
     cores = max(1, min(16, len(os.sched_getaffinity(0))))
     byts = workloads.algorithmic_bytes(w.R, rows, w.H, epilogue=w.epilogue)
-    oracle.boundary(args, nthreads=cores, **kw)  # warm
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        oracle.boundary(args, nthreads=cores, **kw)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    gbs = byts * reps / el / 1e9
-    return dict(value=round(gbs, 3), unit="GB/s", cores=cores, kind="oracle",
+
+    def rate(threads, budget):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            res = oracle.boundary(args, nthreads=threads, **kw)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget:
+                return res, reps, el
+
+    res, _, _ = rate(cores, 0.0)  # warm
+    res, reps, el = rate(cores, seconds)
+    _, reps1, el1 = rate(1, single_seconds)
+    y_gpu, x_gpu = (workloads.bits(t[:rows]) for t in runner.outs[0])
+    ulp = max(int(np.abs(_ordered(res.y) - _ordered(y_gpu)).max()),
+              int(np.abs(_ordered(res.xout) - _ordered(x_gpu)).max()))
+    return dict(value=round(byts * reps / el / 1e9, 3), unit="GB/s", cores=cores, kind="oracle",
                 sample=f"{rows} of {runner.T} token rows of {w.name} (R={w.R}, H={w.H}), "
                        f"{reps} repetitions in {el:.1f} s, {cores} threads; "
-                       f"{el / reps * 1e6 / rows:.1f} us per row")
+                       f"{el / reps * 1e6 / rows:.1f} us per row",
+                single_thread=dict(value=round(byts * reps1 / el1 / 1e9, 3), unit="GB/s",
+                                   sample=f"{reps1} repetitions in {el1:.1f} s"),
+                parity=dict(rows=rows, max_ulp_vs_gpu=ulp))
 
 
 def main():
@@ -320,16 +391,20 @@ def main():
                      "traffic": traffic, "kernel_us": round(ev_us, 3),
                      "kernel_source_sha256": digest},
     }
+    if not args.no_cpu and args.workload is None:
+        out["cpu_baseline"] = cpu_baseline(run)
     del run
     torch.cuda.empty_cache()
+    if args.workload is None:
+        copy_gbs = copy_reference(dev)
+        out["roofline"]["measured_copy_GBps"] = round(copy_gbs, 1)
+        out["roofline"]["frac_of_measured_copy"] = round(achieved / copy_gbs, 4)
     if not args.no_sweep:
         out["sweep"] = sweep(dev)
     if args.all:
         out["other_configs"] = extra_configs(dev)
-    if not args.no_cpu and args.workload is None:
-        base = Runner(cid, T, dev, cold=False)
-        out["cpu_baseline"] = cpu_baseline(base)
-        del base
+    if "cpu_baseline" in out:  # keep the contract's key order readable
+        out["cpu_baseline"] = out.pop("cpu_baseline")
     print(json.dumps(out), flush=True)
 
 
