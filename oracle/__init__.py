@@ -18,6 +18,12 @@ What each call computes, and the passages it follows:
   message: the finalize includes the shared-expert add.
 * ``split=True``: the large-batch path of vLLM PR #62366 "Claims": the
   reduction alone produces a BF16 tensor, the boundary kernel runs after it.
+* ``ep_boundary(...)``: the expert-parallel deferral that vLLM PR #62366
+  names in "Overview" and "Details" (tokens replicated on every rank,
+  TP = 1, EP > 1): each rank finalizes only the top-k slots of its own
+  experts (a negative row index marks another rank's slot), may or may not
+  hold a shared-expert row, rounds to BF16, and the R partials then take the
+  same reduction and epilogue.
 """
 from __future__ import annotations
 
@@ -73,6 +79,11 @@ def _bind(lib):
     lib.oracle_boundary.restype = ctypes.c_int
     lib.oracle_boundary.argtypes = [
         P, P, ctypes.c_int32, P, P, ctypes.c_int32, ctypes.c_int64,
+        ctypes.c_int32, ctypes.c_int32, P, P, P, ctypes.c_float,
+        ctypes.c_int64, ctypes.c_int64, P, P, P, P, ctypes.c_int32]
+    lib.oracle_ep_boundary.restype = ctypes.c_int
+    lib.oracle_ep_boundary.argtypes = [
+        P, P, ctypes.c_int32, P, P, ctypes.c_int32, P,
         ctypes.c_int32, ctypes.c_int32, P, P, P, ctypes.c_float,
         ctypes.c_int64, ctypes.c_int64, P, P, P, P, ctypes.c_int32]
     lib.oracle_bf16_to_f32.restype = ctypes.c_float
@@ -169,6 +180,46 @@ class Result:
     p: Optional[np.ndarray] = None    # [R,T,H] uint16 finalized partials
 
 
+def _outputs(T, H, R, epilogue, split, finalize, debug):
+    """Output arrays and, with debug, the debug block for one oracle call."""
+    if epilogue == EPI_NONE:
+        y = xout = None
+        u = np.zeros((T, H), np.uint16)
+    else:
+        y = np.zeros((T, H), np.uint16)
+        xout = np.zeros((T, H), np.uint16)
+        u = None
+    res = Result(y=y, xout=xout, u=u)
+    dbg = None
+    if debug:
+        res.s = np.zeros((T, H), np.float32)
+        res.a = np.zeros((T, H), np.float32)
+        res.h = np.zeros((T, H), np.float32)
+        res.y32 = np.zeros((T, H), np.float32)
+        res.r1 = np.zeros(T, np.float32)
+        res.r2 = np.zeros(T, np.float32)
+        res.ss1 = np.zeros(T, np.float64)
+        res.ss2 = np.zeros(T, np.float64)
+        res.p = np.zeros((R, T, H), np.uint16) if finalize else None
+        res.u = np.zeros((T, H), np.uint16) if u is None else u
+        dbg = _Debug(_ptr(res.s), _ptr(res.a), _ptr(res.h), _ptr(res.y32),
+                     _ptr(res.r1), _ptr(res.r2), _ptr(res.ss1), _ptr(res.ss2),
+                     _ptr(res.p), _ptr(res.u) if (split or epilogue == EPI_NONE) else None)
+    return res, y, xout, u, dbg
+
+
+def _finish(res, rc, name, debug, split, epilogue):
+    if rc != 0:
+        raise ValueError(f"{name} rejected its arguments")
+    if debug and not (split or epilogue == EPI_NONE):
+        res.u = None
+    return res
+
+
+def _dbg_ptr(dbg):
+    return ctypes.cast(ctypes.pointer(dbg), ctypes.c_void_p) if dbg is not None else None
+
+
 def boundary(src: Sequence[np.ndarray], *, residual=None, gamma1=None, gamma2=None,
              eps: float = 1e-6, epilogue: int = EPI_RMSNORM, split: bool = False,
              topk_w=None, topk_idx=None, shared: Optional[Sequence[np.ndarray]] = None,
@@ -201,39 +252,54 @@ def boundary(src: Sequence[np.ndarray], *, residual=None, gamma1=None, gamma2=No
     x = _c(residual, np.uint16) if residual is not None else None
     g1 = _c(gamma1, np.float32) if gamma1 is not None else None
     g2 = _c(gamma2, np.float32) if gamma2 is not None else None
-    if epilogue == EPI_NONE:
-        y = xout = None
-        u = np.zeros((T, H), np.uint16)
-    else:
-        y = np.zeros((T, H), np.uint16)
-        xout = np.zeros((T, H), np.uint16)
-        u = None
-    res = Result(y=y, xout=xout, u=u)
-    dbg = None
-    if debug:
-        res.s = np.zeros((T, H), np.float32)
-        res.a = np.zeros((T, H), np.float32)
-        res.h = np.zeros((T, H), np.float32)
-        res.y32 = np.zeros((T, H), np.float32)
-        res.r1 = np.zeros(T, np.float32)
-        res.r2 = np.zeros(T, np.float32)
-        res.ss1 = np.zeros(T, np.float64)
-        res.ss2 = np.zeros(T, np.float64)
-        res.p = np.zeros((R, T, H), np.uint16) if finalize else None
-        res.u = np.zeros((T, H), np.uint16) if u is None else u
-        dbg = _Debug(_ptr(res.s), _ptr(res.a), _ptr(res.h), _ptr(res.y32),
-                     _ptr(res.r1), _ptr(res.r2), _ptr(res.ss1), _ptr(res.ss2),
-                     _ptr(res.p), _ptr(res.u) if (split or epilogue == EPI_NONE) else None)
+    res, y, xout, u, dbg = _outputs(T, H, R, epilogue, split, finalize, debug)
     rc = lib.oracle_boundary(
         ctypes.cast(src_arr, ctypes.c_void_p),
         ctypes.cast(sh_arr, ctypes.c_void_p) if sh_arr is not None else None,
         R, _ptr(w), _ptr(idx), k, num_rows, epilogue, int(bool(split)),
         _ptr(x), _ptr(g1), _ptr(g2), ctypes.c_float(eps), T, H,
-        _ptr(y), _ptr(xout), _ptr(u),
-        ctypes.cast(ctypes.pointer(dbg), ctypes.c_void_p) if dbg is not None else None,
-        nthreads)
-    if rc != 0:
-        raise ValueError("oracle_boundary rejected its arguments")
-    if debug and not (split or epilogue == EPI_NONE):
-        res.u = None
-    return res
+        _ptr(y), _ptr(xout), _ptr(u), _dbg_ptr(dbg), nthreads)
+    return _finish(res, rc, "oracle_boundary", debug, split, epilogue)
+
+
+def ep_boundary(expert_rows: Sequence[Optional[np.ndarray]], *, topk_w, topk_rows,
+                residual=None, gamma1=None, gamma2=None, eps: float = 1e-6,
+                epilogue: int = EPI_RMSNORM, split: bool = False,
+                shared: Optional[Sequence[Optional[np.ndarray]]] = None,
+                num_rows: Optional[Sequence[int]] = None, H: Optional[int] = None,
+                debug: bool = False, nthreads: int = 1) -> Result:
+    """Run the oracle with the expert-parallel finalize.
+
+    expert_rows: R arrays of BF16 bits [num_rows_r, H] (None for a rank with
+    no rows); topk_w: [T,k] float32, the same for every rank; topk_rows: R
+    int32 arrays [T,k], row of that rank's buffer or negative for another
+    rank's slot; shared: None, or R entries each [T,H] BF16 bits or None.
+    """
+    lib = _active()
+    R = len(expert_rows)
+    w = _c(topk_w, np.float32)
+    T, k = w.shape
+    rows = [None if e is None else _c(e, np.uint16) for e in expert_rows]
+    if H is None:
+        H = next(e.shape[1] for e in rows if e is not None)
+    nr = [0 if e is None else e.shape[0] for e in rows] if num_rows is None else list(num_rows)
+    nr_arr = np.asarray(nr, np.int64)
+    idx = [_c(i, np.int32) for i in topk_rows]
+    if len(idx) != R or any(i.shape != (T, k) for i in idx):
+        raise ValueError("topk_rows must hold R arrays of shape [T,k]")
+    src_arr = (ctypes.c_void_p * R)(*[None if e is None else e.ctypes.data for e in rows])
+    idx_arr = (ctypes.c_void_p * R)(*[i.ctypes.data for i in idx])
+    sh = None if shared is None else [None if a is None else _c(a, np.uint16) for a in shared]
+    sh_arr = (ctypes.c_void_p * R)(*[None if a is None else a.ctypes.data for a in sh]) \
+        if sh is not None else None
+    x = _c(residual, np.uint16) if residual is not None else None
+    g1 = _c(gamma1, np.float32) if gamma1 is not None else None
+    g2 = _c(gamma2, np.float32) if gamma2 is not None else None
+    res, y, xout, u, dbg = _outputs(T, H, R, epilogue, split, True, debug)
+    rc = lib.oracle_ep_boundary(
+        ctypes.cast(src_arr, ctypes.c_void_p),
+        ctypes.cast(sh_arr, ctypes.c_void_p) if sh_arr is not None else None,
+        R, _ptr(w), ctypes.cast(idx_arr, ctypes.c_void_p), k, _ptr(nr_arr), epilogue,
+        int(bool(split)), _ptr(x), _ptr(g1), _ptr(g2), ctypes.c_float(eps), T, H,
+        _ptr(y), _ptr(xout), _ptr(u), _dbg_ptr(dbg), nthreads)
+    return _finish(res, rc, "oracle_ep_boundary", debug, split, epilogue)

@@ -39,6 +39,15 @@
  *              xout = bf16(h); r2 = inv_rms(h); y = bf16((h * r2) * gamma2).
  *   split      U = bf16(s) (pass 1), then rmsnorm / sandwich with R = 1 on U.
  *
+ *   expert-parallel finalize (vLLM PR #62366 "Overview" and "Details": the
+ *   replicated-token deferral for TP = 1, EP > 1 that builds on the same
+ *   fused boundary):  every rank holds all T tokens and the same weights
+ *   w[t,j], but expert rows only for its own experts.  idx_r[t,j] is the row
+ *   of rank r's buffer for slot j, or negative when slot j's expert lives on
+ *   another rank.  Rank r's finalize is the one above over its own slots
+ *   only, j ascending, plus its shared-expert row if it holds one; the R
+ *   BF16 partials then go through the same reduce and epilogue.
+ *
  * bf16(f) rounds binary32 to bfloat16, nearest with ties to even; NaN stays a
  * quiet NaN with its sign, overflow goes to +-inf.  Widening is exact.
  *
@@ -113,6 +122,35 @@ static void finalize_row(const bf16_t* rows, int64_t num_rows,
             acc = acc + prod;
         }
         if (shared_row) acc = acc + oracle_bf16_to_f32(shared_row[i]);
+        p_row[i] = oracle_f32_to_bf16(acc);
+    }
+}
+
+/*
+ * Expert-parallel finalize of one token row of rank r: the slots whose idx
+ * is negative belong to another rank's experts and take no part in this
+ * rank's sum (they are skipped, not added as zero).  An index at or past
+ * num_rows reads as NaN, as above.  shared_row is NULL when this rank holds
+ * no shared-expert row.
+ */
+static void finalize_row_ep(const bf16_t* rows, int64_t num_rows,
+                            const bf16_t* shared_row, const float* w,
+                            const int32_t* idx, int32_t k, int64_t H,
+                            bf16_t* p_row)
+{
+    for (int64_t i = 0; i < H; ++i) {
+        float acc = 0.0f;
+        for (int32_t j = 0; j < k; ++j) {
+            if (idx[j] < 0) continue; /* another rank's expert */
+            float e;
+            if ((int64_t)idx[j] >= num_rows)
+                e = (float)NAN;
+            else
+                e = oracle_bf16_to_f32(rows[(int64_t)idx[j] * H + i]);
+            float term = w[j] * e;
+            acc = acc + term;
+        }
+        if (shared_row != NULL) acc = acc + oracle_bf16_to_f32(shared_row[i]);
         p_row[i] = oracle_f32_to_bf16(acc);
     }
 }
@@ -219,6 +257,9 @@ typedef struct {
     const int32_t* idx; /* [T,k] */
     int32_t k;          /* 0: no finalize */
     int64_t num_rows;
+    /* expert-parallel finalize: R index arrays [T,k] and R row counts */
+    const int32_t* const* idx_r;
+    const int64_t* num_rows_r;
     int32_t epilogue;   /* ORACLE_EPI_* */
     int32_t split;      /* 1: round s to BF16 and restart with R = 1 */
     const bf16_t* x;    /* residual in [T,H] */
@@ -262,7 +303,16 @@ static void* run_rows(void* arg)
     for (int64_t t = sl->t0; t < sl->t1; ++t) {
         /* optional finalize, one rank at a time, into BF16 rows */
         for (int32_t r = 0; r < J->R; ++r) {
-            if (J->k > 0) {
+            if (J->k > 0 && J->idx_r) {
+                finalize_row_ep(J->src[r], J->num_rows_r[r],
+                                J->shared && J->shared[r] ? J->shared[r] + t * H : NULL,
+                                J->w + t * J->k, J->idx_r[r] + t * J->k, J->k, H,
+                                p + (int64_t)r * H);
+                rows[r] = p + (int64_t)r * H;
+                if (D && D->p)
+                    memcpy(D->p + ((int64_t)r * J->T + t) * H, rows[r],
+                           sizeof(bf16_t) * (size_t)H);
+            } else if (J->k > 0) {
                 finalize_row(J->src[r], J->num_rows,
                              J->shared ? J->shared[r] + t * H : NULL,
                              J->w + t * J->k, J->idx + t * J->k, J->k, H,
@@ -378,7 +428,38 @@ int oracle_boundary(const bf16_t* const* src, const bf16_t* const* shared,
     if (epilogue != ORACLE_EPI_NONE && (!x || !g1 || !y || !xout)) return -1;
     if (epilogue == ORACLE_EPI_SANDWICH && !g2) return -1;
     if (epilogue == ORACLE_EPI_NONE && !u) return -1;
-    job_t J = {src, shared, R, w, idx, k, num_rows, epilogue, split, x, g1, g2,
-               eps, T, H, y, xout, u, dbg};
+    job_t J = {src, shared, R, w, idx, k, num_rows, NULL, NULL, epilogue, split,
+               x, g1, g2, eps, T, H, y, xout, u, dbg};
+    return run_job(&J, nthreads);
+}
+
+/*
+ * The boundary with the expert-parallel finalize (see the header of this
+ * file).  src holds R expert-row buffers, src[r] of num_rows_r[r] rows
+ * (NULL allowed when that count is 0); idx_r holds R index arrays [T,k];
+ * w is [T,k], the same for every rank; shared is NULL, or R pointers of
+ * which any may be NULL (that rank holds no shared-expert row).  The other
+ * arguments are those of oracle_boundary.
+ */
+int oracle_ep_boundary(const bf16_t* const* src, const bf16_t* const* shared,
+                       int32_t R, const float* w, const int32_t* const* idx_r,
+                       int32_t k, const int64_t* num_rows_r, int32_t epilogue,
+                       int32_t split, const bf16_t* x, const float* g1,
+                       const float* g2, float eps, int64_t T, int64_t H,
+                       bf16_t* y, bf16_t* xout, bf16_t* u,
+                       const oracle_debug* dbg, int32_t nthreads)
+{
+    if (R < 1 || k < 1 || T < 0 || H < 1 || !src || !w || !idx_r || !num_rows_r)
+        return -1;
+    if (epilogue < ORACLE_EPI_RMSNORM || epilogue > ORACLE_EPI_NONE) return -1;
+    if (epilogue != ORACLE_EPI_NONE && (!x || !g1 || !y || !xout)) return -1;
+    if (epilogue == ORACLE_EPI_SANDWICH && !g2) return -1;
+    if (epilogue == ORACLE_EPI_NONE && !u) return -1;
+    for (int32_t r = 0; r < R; ++r) {
+        if (!idx_r[r] || num_rows_r[r] < 0) return -1;
+        if (num_rows_r[r] > 0 && !src[r]) return -1;
+    }
+    job_t J = {src, shared, R, w, NULL, k, 0, idx_r, num_rows_r, epilogue, split,
+               x, g1, g2, eps, T, H, y, xout, u, dbg};
     return run_job(&J, nthreads);
 }

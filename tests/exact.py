@@ -108,9 +108,9 @@ def mp_to_frac(x) -> Fraction:
 
 
 def bf16_val(bits: int):
-    """Exact value of a BF16 bit pattern (a Fraction; +-inf as a float)."""
+    """Exact value of a BF16 bit pattern (a Fraction; +-inf and NaN as a float)."""
     f = np.uint32(int(bits) << 16).view(np.float32)
-    if np.isinf(f):
+    if not np.isfinite(f):
         return float(f)
     return to_frac(f)
 
@@ -145,6 +145,9 @@ def check_fp32(tally: Tally, label: str, got, exact, bound: float):
 def check_bf16(tally: Tally, label: str, got_bits: int, exact, bound: float):
     """exact: Fraction or mpf; bound: absolute bound on the oracle's FP32
     value before rounding."""
+    if np.isnan(np.uint32(int(got_bits) << 16).view(np.float32)):
+        tally.fail(f"{label}: BF16 NaN where a finite value is defined")
+        return
     ex = mp_to_frac(exact) if not isinstance(exact, Fraction) else exact
     bnd = Fraction(bound)
     if bnd == 0:  # the FP32 value is exact: its rounding is fully decided

@@ -23,7 +23,7 @@ OUT = os.path.join(os.path.dirname(os.path.abspath(__file__)), "oracle_digests.j
 
 # (workload id, T, split)
 CASES = [(1, 8, False), (2, 8, False), (3, 2, False), (4, 2, False), (5, 3, False),
-         (5, 3, True), (2, 3, True)]
+         (5, 3, True), (2, 3, True), (6, 4, False)]
 
 
 def run_case(cid, T, split):
@@ -33,11 +33,21 @@ def run_case(cid, T, split):
     kw = dict(residual=workloads.bits(inp.residual), gamma1=workloads.f32(inp.gamma1),
               gamma2=workloads.f32(inp.gamma2) if inp.gamma2 is not None else None,
               eps=inp.eps, epilogue=epi, split=split)
+    if w.ep:
+        res = oracle.ep_boundary(
+            [workloads.bits(e) for e in inp.expert_rows], topk_w=workloads.f32(inp.topk_w),
+            topk_rows=[r.numpy() for r in inp.ep_rows], H=w.H,
+            shared=[None if s is None else workloads.bits(s) for s in inp.shared], **kw)
+        return _digest(res)
     if inp.k:
         kw.update(topk_w=workloads.f32(inp.topk_w),
                   topk_idx=inp.topk_idx.numpy(),
                   shared=[workloads.bits(s) for s in inp.shared] if inp.shared else None)
     res = oracle.boundary([workloads.bits(s) for s in inp.sources], **kw)
+    return _digest(res)
+
+
+def _digest(res):
     h = hashlib.sha256()
     h.update(res.y.tobytes())
     h.update(res.xout.tobytes())

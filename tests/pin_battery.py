@@ -122,6 +122,9 @@ def pin_exact(case, seed=11, min_decided=0.9) -> List[str]:
                                               d["topk_w"][t], d["topk_idx"][t], i)
                     X.check_bf16(tally, f"P[{r},{t},{i}]", int(res.p[r, t, i]), ex, bd)
                 p_rows.append(res.p[r, t])
+            if not np.all(np.isfinite(oracle.bf16_to_f32(np.stack(p_rows)))):
+                tally.fail(f"token {t}: a finalized partial is not finite")
+                break
         else:
             p_rows = [p[t] for p in d["src"]]
         s_ex, s_bd = [], []
@@ -552,4 +555,6 @@ def all_pins(quick: bool = False) -> List[str]:
     fails += pin_closed_forms()
     fails += pin_invariants()
     fails += pin_contraction()
+    from tests import pin_ep  # the expert-parallel finalize's pins
+    fails += pin_ep.all_ep_pins(quick=quick)
     return fails

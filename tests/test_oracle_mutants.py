@@ -37,6 +37,21 @@ MUTANTS = [
      "for (int64_t i = 0; i < H; ++i) u[i] = oracle_f32_to_bf16(s[i]);\n            if (J->epilogue != ORACLE_EPI_NONE) goto no_split;"),
     ("fp32_sum_of_squares", "double ss = 0.0;", "float ss = 0.0f;"),
     ("invalid_index_clamped", "e = NAN;", "e = 0.0f;"),
+    # expert-parallel finalize
+    ("ep_foreign_slot_reads_nan", "if (idx[j] < 0) continue; /* another rank's expert */",
+     "if (idx[j] < 0) { acc = acc + (float)NAN; continue; }"),
+    ("ep_foreign_slot_reads_row0", "if (idx[j] < 0) continue; /* another rank's expert */",
+     "if (idx[j] < 0) { if (num_rows > 0) acc = acc + w[j] * oracle_bf16_to_f32(rows[i]); continue; }"),
+    ("ep_rank0_indices", "J->idx_r[r] + t * J->k", "J->idx_r[0] + t * J->k"),
+    ("ep_rank0_row_count", "finalize_row_ep(J->src[r], J->num_rows_r[r],",
+     "finalize_row_ep(J->src[r], J->num_rows_r[0],"),
+    ("ep_shared_on_every_rank", "J->shared && J->shared[r] ? J->shared[r] + t * H : NULL",
+     "J->shared && J->shared[0] ? J->shared[0] + t * H : NULL"),
+    ("ep_drop_shared", "if (shared_row != NULL) acc = acc + oracle_bf16_to_f32(shared_row[i]);", ""),
+    ("ep_weight_index", "float term = w[j] * e;", "float term = w[k - 1 - j] * e;"),
+    ("ep_fma", "float term = w[j] * e;\n            acc = acc + term;", "acc = fmaf(w[j], e, acc);"),
+    ("ep_shared_first", "float acc = 0.0f;\n        for (int32_t j = 0; j < k; ++j) {\n            if (idx[j] < 0) continue;",
+     "float acc = shared_row != NULL ? oracle_bf16_to_f32(shared_row[i]) : 0.0f;\n        shared_row = NULL;\n        for (int32_t j = 0; j < k; ++j) {\n            if (idx[j] < 0) continue;"),
 ]
 
 

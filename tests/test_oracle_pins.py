@@ -44,3 +44,29 @@ def test_invariants():
 def test_no_fma_contraction():
     fails = B.pin_contraction()
     assert not fails, "\n".join(fails)
+
+
+@pytest.mark.parametrize("case", __import__("tests.pin_ep", fromlist=["x"]).EP_EXACT_CASES,
+                         ids=lambda c: "ep_R{}_T{}_H{}_{}_k{}_of{}_shared{}".format(*c))
+def test_ep_exact_arithmetic(case):
+    from tests import pin_ep as E
+    fails = E.pin_ep_exact(case)
+    assert not fails, "\n".join(fails)
+
+
+def test_ep_closed_forms():
+    from tests import pin_ep as E
+    fails = E.pin_ep_closed_forms()
+    assert not fails, "\n".join(fails)
+
+
+def test_ep_invariants():
+    from tests import pin_ep as E
+    fails = E.pin_ep_invariants()
+    assert not fails, "\n".join(fails)
+
+
+def test_ep_no_fma_contraction():
+    from tests import pin_ep as E
+    fails = E.pin_ep_contraction()
+    assert not fails, "\n".join(fails)
