@@ -103,7 +103,7 @@ class Runner:
         self.unfused = unfused
         w = self.w
         self.bytes = workloads.algorithmic_bytes(w.R, T, w.H, epilogue=w.epilogue, k=w.k,
-                                                 shared=w.shared)
+                                                 shared=w.shared, ep=w.ep)
         n = max(1, min(32, -(-COLD_BYTES // self.bytes))) if cold else 1
         self.sets = [workloads.make_workload(cid, T, device=dev, salt=i) for i in range(n)]
         self.outs = [(torch.empty(T, w.H, dtype=torch.bfloat16, device=dev),
@@ -123,6 +123,10 @@ class Runner:
                                        topk_rows=d.topk_idx if d.k else None,
                                        shared=d.shared if d.k else None, epilogue=self.epi,
                                        scratch=self.scratch, out=o, residual_out=r)
+        if d.ep_rows is not None:
+            return f.ep_moe_finalize_reduce_norm(d.expert_rows, d.topk_w, d.ep_rows, d.residual,
+                                                 d.gamma1, d.gamma2, d.eps, shared=d.shared,
+                                                 epilogue=self.epi, out=o, residual_out=r)
         if d.k and self.unfused:
             # the standalone finalize, then the plain reduction of its output
             f.moe_finalize(d.expert_rows, d.topk_w, d.topk_idx, shared=d.shared, out=self.parts)
@@ -207,7 +211,7 @@ def extra_configs(dev):
         setattr(r, attr, False)
         return sum(t[False]) / 2, sum(t[True]) / 2
 
-    for cid, Ts in ((1, (8,)), (4, (2, 4, 16, 32))):
+    for cid, Ts in ((1, (8,)), (4, (2, 4, 16, 32)), (6, (1, 8, 64, 1024, 4096))):
         for T in Ts:
             r = Runner(cid, T, dev, cold=T >= 256)
             add(r, T, "", r.graph_us())

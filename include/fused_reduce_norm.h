@@ -194,6 +194,61 @@ frn_status frn_moe_finalize(const void* const* expert_rows, const void* const* s
                             void* stream);
 
 /*
+ * Expert-parallel variant of frn_moe_finalize_reduce_norm: the
+ * replicated-token deferral for TP = 1, EP > 1 that vLLM PR #62366 names in
+ * "Overview" and "Details" (built on the same fused boundary).  Every rank
+ * holds all T tokens and the same top-k weights, but expert outputs only
+ * for its own experts, so each rank has its own row-index array:
+ *   topk_rows[r][t,j] >= 0   the row of E_r holding token t's j-th expert
+ *                            output (that expert lives on rank r);
+ *   topk_rows[r][t,j] <  0   slot j's expert lives on another rank: the
+ *                            slot takes no part in rank r's sum (skipped,
+ *                            not added as zero).
+ * Per rank r, token t, element i:
+ *   acc = 0; for j = 0..k-1 with topk_rows[r][t,j] >= 0:
+ *       acc = acc + topk_w[t,j] * E_r[topk_rows[r][t,j], i]
+ *   if shared[r]: acc = acc + S_r[t, i]
+ *   P_r[t, i] = bf16(acc)
+ * then the reduction and epilogue exactly as in the calls above.
+ * expert_rows: R device pointers, E_r = [num_rows[r], H] BF16; an entry may
+ * be NULL when num_rows[r] == 0.  num_rows: HOST array of R counts (>= 0).
+ * topk_rows: HOST array of R device pointers to [T,k] int32 (4-byte
+ * aligned).  shared: NULL, or a HOST array of R entries, each NULL (that
+ * rank holds no shared-expert row) or a device pointer to [T,H] BF16.
+ * topk_w: [T,k] FP32, the same for every rank.  An index at or past
+ * num_rows[r] is never dereferenced: that slot reads as NaN and the token's
+ * output row becomes NaN.  Workspace, epilogue, aliasing and errors as in
+ * frn_moe_finalize_reduce_norm.  With one rank owning every slot this is
+ * frn_moe_finalize_reduce_norm bit for bit.
+ */
+frn_status frn_ep_moe_finalize_reduce_norm(const void* const* expert_rows,
+                                           const void* const* shared, int32_t R,
+                                           const float* topk_w,
+                                           const int32_t* const* topk_rows, int32_t k,
+                                           const int64_t* num_rows, int32_t epilogue,
+                                           const void* residual_in, const float* gamma1,
+                                           const float* gamma2, float eps, int64_t T,
+                                           int64_t H, void* out, void* residual_out,
+                                           void* workspace, size_t workspace_bytes,
+                                           void* stream);
+
+/*
+ * The expert-parallel finalize alone, materialized per rank:
+ * partials_out[r][t] = P_r[t] with P_r as in
+ * frn_ep_moe_finalize_reduce_norm.  The deferred finalize reaching a
+ * non-fusing path is materialized this way (SGLang PR #34134, first commit
+ * message); reducing the R outputs with frn_reduce_residual_rmsnorm /
+ * frn_reduce_sandwich_norm gives the fused call's results bit for bit.
+ * partials_out as in frn_moe_finalize; other arguments as in
+ * frn_ep_moe_finalize_reduce_norm.
+ */
+frn_status frn_ep_moe_finalize(const void* const* expert_rows, const void* const* shared,
+                               int32_t R, const float* topk_w,
+                               const int32_t* const* topk_rows, int32_t k,
+                               const int64_t* num_rows, int64_t T, int64_t H,
+                               void* const* partials_out, void* stream);
+
+/*
  * Capability check without launching anything: FRN_OK if a call with these
  * sizes is served, FRN_ERR_UNSUPPORTED if it would be declined, and
  * FRN_ERR_INVALID for malformed sizes (the analogue of a workspace factory

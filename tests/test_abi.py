@@ -185,6 +185,64 @@ def test_moe_zero_tokens_is_a_no_op(lib):
     assert call_moe(lib, T=0) == OK
 
 
+def call_ep(lib, R=2, k=3, T=4, H=64, num_rows=(12, 12), epilogue=0, src=None, shared=None,
+            rows=None, w=None, nr_ptr=True, outs=None):
+    lib.frn_ep_moe_finalize_reduce_norm.argtypes = [
+        P, P, ctypes.c_int32, P, P, ctypes.c_int32, P, ctypes.c_int32, P, P, P, ctypes.c_float,
+        ctypes.c_int64, ctypes.c_int64, P, P, P, ctypes.c_size_t, P]
+    src = ptrs(*[addr(10 + r) for r in range(R)]) if src is None else src
+    rows = ptrs(*[addr(40 + r) for r in range(R)]) if rows is None else rows
+    nr = (ctypes.c_int64 * len(num_rows))(*num_rows)
+    return lib.frn_ep_moe_finalize_reduce_norm(
+        src, shared, R, addr(5) if w is None else w, rows, k,
+        ctypes.cast(nr, P) if nr_ptr else None, epilogue, addr(1), addr(2), addr(7), 1e-6, T,
+        H, addr(3), addr(4), None, 0, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=0), INVALID),
+    (dict(k=17), UNSUPPORTED),
+    (dict(epilogue=7), INVALID),
+    (dict(num_rows=(12, -1)), INVALID),
+    (dict(nr_ptr=False), INVALID),
+    (dict(rows=0), INVALID),                                  # no index-array list
+    (dict(rows=ptrs(addr(40), 0)), INVALID),                  # one index array missing
+    (dict(rows=ptrs(addr(40), addr(41, 2))), UNSUPPORTED),    # misaligned index array
+    (dict(src=ptrs(addr(10), 0)), INVALID),                   # rank with rows but no buffer
+    (dict(w=addr(3)), INVALID),                               # out overlaps the weights
+    (dict(rows=ptrs(addr(40), addr(3))), INVALID),            # out overlaps an index array
+    (dict(shared=ptrs(0, addr(3))), INVALID),                 # out overlaps a shared row
+    (dict(H=68), UNSUPPORTED),
+])
+def test_ep_rejects(lib, kw, status):
+    assert call_ep(lib, **kw) == status
+
+
+def test_ep_accepts_ranks_without_rows_or_shared_rows(lib):
+    # Rank 1 owns no rows (NULL buffer) and holds no shared row (NULL entry).
+    # With T > 0 every check runs; the overlap planted on the weights stops
+    # the call before any launch, after those two entries were accepted.
+    src = ptrs(addr(10), 0)
+    st = call_ep(lib, num_rows=(12, 0), src=src, shared=ptrs(addr(30), 0), w=addr(3))
+    assert st == INVALID and b"overlaps" in lib.frn_last_error()
+    assert call_ep(lib, T=0) == OK
+
+
+def test_ep_standalone_finalize_rejects(lib):
+    lib.frn_ep_moe_finalize.argtypes = [P, P, ctypes.c_int32, P, P, ctypes.c_int32, P,
+                                        ctypes.c_int64, ctypes.c_int64, P, P]
+    src = ptrs(addr(10), addr(11))
+    rows = ptrs(addr(40), addr(41))
+    nr = (ctypes.c_int64 * 2)(12, 12)
+    args = (src, None, 2, addr(5), rows, 3, ctypes.cast(nr, P))
+    assert lib.frn_ep_moe_finalize(*args, 0, 64, ptrs(addr(20), addr(21)), None) == OK
+    assert lib.frn_ep_moe_finalize(*args, 4, 64, None, None) == INVALID
+    assert lib.frn_ep_moe_finalize(*args, 4, 64, ptrs(addr(20), addr(10)), None) == INVALID
+    assert lib.frn_ep_moe_finalize(*args, 4, 64, ptrs(addr(20), addr(40)), None) == INVALID
+    assert lib.frn_ep_moe_finalize(src, None, 2, addr(5), rows, 3, None, 4, 64,
+                                   ptrs(addr(20), addr(21)), None) == INVALID
+
+
 def test_split_scratch_must_not_alias(lib):
     src = ptrs(addr(10), addr(11))
     st = lib.frn_split_reduce_norm(src, None, 2, None, None, 0, 0, 0, addr(1), addr(2), None,

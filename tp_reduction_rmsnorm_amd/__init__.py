@@ -16,6 +16,9 @@ Function names are the C entry points without their ``frn_`` prefix:
 * ``reduce_bf16``, ``moe_finalize_reduce_bf16``  split path, pass 1
 * ``split_reduce_norm``          both passes of the split path
 * ``moe_finalize``               the per-rank finalize alone (materialized)
+* ``ep_moe_finalize_reduce_norm``, ``ep_moe_finalize``  the same with
+                                 expert-parallel routing (each rank owns
+                                 some experts; per-rank row indices)
 * ``query``, ``workspace_bytes``, ``version``
 * ``set_launch_table``, ``launch_shape``  tuned launch shapes (tune.py)
 
@@ -90,6 +93,11 @@ _c_split = _sig("frn_split_reduce_norm", ctypes.c_int,
                  _P, _P, _P, _P])
 _c_finalize = _sig("frn_moe_finalize", ctypes.c_int,
                    [_P, _P, _I32, _P, _P, _I32, _I64, _I64, _I64, _P, _P])
+_c_ep_moe = _sig("frn_ep_moe_finalize_reduce_norm", ctypes.c_int,
+                 [_P, _P, _I32, _P, _P, _I32, _P, _I32, _P, _P, _P, _F32, _I64, _I64,
+                  _P, _P, _P, _SZ, _P])
+_c_ep_finalize = _sig("frn_ep_moe_finalize", ctypes.c_int,
+                      [_P, _P, _I32, _P, _P, _I32, _P, _I64, _I64, _P, _P])
 _c_query = _sig("frn_query", ctypes.c_int, [_I32, _I32, _I64, _I64, _I32])
 _c_set_table = _sig("frn_set_launch_table", ctypes.c_int, [ctypes.c_char_p])
 _c_shape = _sig("frn_launch_shape", ctypes.c_int,
@@ -102,6 +110,7 @@ _c_version = _sig("frn_version", ctypes.c_char_p, [])
 C_FUNCTIONS = ("frn_reduce_residual_rmsnorm", "frn_reduce_sandwich_norm",
                "frn_moe_finalize_reduce_norm", "frn_reduce_bf16",
                "frn_moe_finalize_reduce_bf16", "frn_split_reduce_norm", "frn_moe_finalize",
+               "frn_ep_moe_finalize_reduce_norm", "frn_ep_moe_finalize",
                "frn_query", "frn_set_launch_table", "frn_launch_shape",
                "frn_workspace_bytes", "frn_status_string", "frn_last_error", "frn_version")
 
@@ -179,6 +188,12 @@ def _need(t: torch.Tensor, what: str, dtype, dim: int, device):
 
 def _ptr_array(ts):
     return (ctypes.c_void_p * len(ts))(*[t.data_ptr() for t in ts])
+
+
+def _ptr_array_opt(ts):
+    """Like _ptr_array; None entries and empty tensors pass NULL."""
+    return (ctypes.c_void_p * len(ts))(
+        *[None if t is None or t.numel() == 0 else t.data_ptr() for t in ts])
 
 
 def _stream(stream, device) -> int:
@@ -408,6 +423,123 @@ def moe_finalize(expert_rows: TensorList, topk_weights: torch.Tensor, topk_rows:
     _check(_c_finalize(ctypes.cast(earr, _P), ctypes.cast(sarr, _P) if sarr is not None else None,
                        R, topk_weights.data_ptr(), topk_rows.data_ptr(), k, num_rows, T, H,
                        ctypes.cast(oarr, _P), _stream(stream, device)))
+    return out
+
+
+def _check_ep(expert_rows, topk_weights, topk_rows, shared, H=None):
+    """Expert-parallel operands: R expert buffers [num_rows_r, H] (None or
+    0 rows for a rank without rows), weights [T,k] shared by every rank, R
+    int32 index arrays [T,k], and shared: None or R entries each None or
+    [T,H]."""
+    es = list(expert_rows)
+    if not es:
+        raise ValueError("need at least one expert-row buffer")
+    _need(topk_weights, "topk_weights", torch.float32, 2, topk_weights.device)
+    device = topk_weights.device
+    T, k = topk_weights.shape
+    for i, e in enumerate(es):
+        if e is not None:
+            _need(e, f"expert_rows[{i}]", torch.bfloat16, 2, device)
+            if H is None:
+                H = e.shape[1]
+            elif e.shape[1] != H:
+                raise ValueError("all expert-row buffers must have H columns")
+    rows = list(topk_rows) if not isinstance(topk_rows, torch.Tensor) else None
+    if rows is None or len(rows) != len(es):
+        raise ValueError("topk_rows must give one [T, k] int32 tensor per rank")
+    for i, r in enumerate(rows):
+        _need(r, f"topk_rows[{i}]", torch.int32, 2, device)
+        if tuple(r.shape) != (T, k):
+            raise ValueError("every topk_rows tensor must have the shape of topk_weights")
+    sh = None
+    if shared is not None:
+        sh = list(shared)
+        if len(sh) != len(es):
+            raise ValueError("shared must give one entry (a [T, H] tensor or None) per rank")
+        for i, s in enumerate(sh):
+            if s is None:
+                continue
+            _need(s, f"shared[{i}]", torch.bfloat16, 2, device)
+            if H is None:
+                H = s.shape[1]
+            if tuple(s.shape) != (T, H):
+                raise ValueError("shared tensors must be [T, H]")
+    if H is None:
+        raise ValueError("H is unknown: no expert buffer or shared tensor gives it")
+    num_rows = [0 if e is None else int(e.shape[0]) for e in es]
+    return es, sh, rows, T, H, k, num_rows, device
+
+
+def ep_moe_finalize_reduce_norm(expert_rows: Sequence[Optional[torch.Tensor]],
+                                topk_weights: torch.Tensor, topk_rows: TensorList,
+                                residual: torch.Tensor, gamma1: torch.Tensor,
+                                gamma2: Optional[torch.Tensor] = None, eps: float = 1e-6, *,
+                                shared: Optional[Sequence[Optional[torch.Tensor]]] = None,
+                                epilogue: int = EPI_RMSNORM, out=None, residual_out=None,
+                                workspace="auto", stream=None):
+    """Expert-parallel finalize, then the epilogue: per rank r,
+    P_r = bf16(sum over j with topk_rows[r][t,j] >= 0 of w[t,j] * E_r[row]
+    (+ shared[r][t] if given)); a negative index marks another rank's slot.
+    Returns (out, residual_out).  ``workspace`` as in
+    ``moe_finalize_reduce_norm``."""
+    if residual is None:
+        raise ValueError("residual is required: this boundary always adds the residual")
+    es, sh, rows, T, H, k, num_rows, device = _check_ep(
+        expert_rows, topk_weights, topk_rows, shared,
+        H=residual.shape[1] if residual.dim() == 2 else None)
+    _need(residual, "residual", torch.bfloat16, 2, device)
+    if tuple(residual.shape) != (T, H):
+        raise ValueError("residual must be [T, H]")
+    _check_gamma(gamma1, H, device, "gamma1")
+    if epilogue == EPI_SANDWICH:
+        if gamma2 is None:
+            raise ValueError("the sandwich epilogue needs gamma2")
+        _check_gamma(gamma2, H, device, "gamma2")
+    out, residual_out = _outputs(T, H, device, out, residual_out)
+    st = _stream(stream, device)
+    R = len(es)
+    ws, wsb = _workspace(workspace, T, H, R, k, device, st)
+    earr = _ptr_array_opt(es)
+    sarr = _ptr_array_opt(sh) if sh is not None else None
+    rarr = _ptr_array(rows)
+    nrows = (ctypes.c_int64 * R)(*num_rows)
+    _check(_c_ep_moe(ctypes.cast(earr, _P), ctypes.cast(sarr, _P) if sarr is not None else None,
+                     R, topk_weights.data_ptr(), ctypes.cast(rarr, _P), k,
+                     ctypes.cast(nrows, _P), epilogue, residual.data_ptr(), gamma1.data_ptr(),
+                     gamma2.data_ptr() if gamma2 is not None else None, eps, T, H,
+                     out.data_ptr(), residual_out.data_ptr(), ws, wsb, st))
+    return out, residual_out
+
+
+def ep_moe_finalize(expert_rows: Sequence[Optional[torch.Tensor]], topk_weights: torch.Tensor,
+                    topk_rows: TensorList, *, H: Optional[int] = None,
+                    shared: Optional[Sequence[Optional[torch.Tensor]]] = None, out=None,
+                    stream=None):
+    """The expert-parallel finalize alone: returns R BF16 tensors [T, H]
+    (P_r as in ``ep_moe_finalize_reduce_norm``)."""
+    es, sh, rows, T, H, k, num_rows, device = _check_ep(expert_rows, topk_weights, topk_rows,
+                                                        shared, H=H)
+    R = len(es)
+    if out is None:
+        out = [torch.empty((T, H), dtype=torch.bfloat16, device=device) for _ in range(R)]
+    else:
+        out = _as_list(out, "out")
+        if len(out) != R:
+            raise ValueError("out must give one [T, H] tensor per rank")
+        for i, o in enumerate(out):
+            _need(o, f"out[{i}]", torch.bfloat16, 2, device)
+            if tuple(o.shape) != (T, H):
+                raise ValueError("out tensors must be [T, H]")
+    earr = _ptr_array_opt(es)
+    sarr = _ptr_array_opt(sh) if sh is not None else None
+    rarr = _ptr_array(rows)
+    nrows = (ctypes.c_int64 * R)(*num_rows)
+    oarr = _ptr_array(out)
+    _check(_c_ep_finalize(ctypes.cast(earr, _P),
+                          ctypes.cast(sarr, _P) if sarr is not None else None, R,
+                          topk_weights.data_ptr(), ctypes.cast(rarr, _P), k,
+                          ctypes.cast(nrows, _P), T, H, ctypes.cast(oarr, _P),
+                          _stream(stream, device)))
     return out
 
 

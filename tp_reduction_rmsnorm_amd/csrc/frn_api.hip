@@ -73,7 +73,7 @@ frn_status check_sizes(int32_t R, int32_t k, int64_t T, int64_t H, int32_t epilo
 // Pointer checks shared by every call.
 struct Call {
     frn::RowArgs a;
-    Span in[2 * FRN_MAX_R + 6];
+    Span in[3 * FRN_MAX_R + 6];
     int n_in = 0;
     Span outs[FRN_MAX_R + 4];
     int n_out = 0;
@@ -113,11 +113,45 @@ frn_status check_alias(const Call& c) {
     return FRN_OK;
 }
 
+// Top-k routing of a finalize: the weights [T,k] shared by every rank, and
+// per rank the row-index array [T,k] and the row count of its expert buffer.
+// Under TP every rank gets the same index array and row count; under
+// expert-parallel routing (ep) each rank has its own, a negative index marks
+// another rank's slot, and a rank may own no rows (its buffer may be NULL).
+struct Routing {
+    const float* topk_w = nullptr;
+    const int32_t* rows[FRN_MAX_R] = {};
+    int64_t num_rows[FRN_MAX_R] = {};
+    bool ep = false;
+};
+
+Routing tp_routing(int32_t R, const float* topk_w, const int32_t* topk_row, int64_t num_rows) {
+    Routing g;
+    g.topk_w = topk_w;
+    for (int r = 0; r < R && r < FRN_MAX_R; ++r) {
+        g.rows[r] = topk_row;
+        g.num_rows[r] = num_rows;
+    }
+    return g;
+}
+
+frn_status ep_routing(Routing& g, int32_t R, const float* topk_w,
+                      const int32_t* const* topk_rows, const int64_t* num_rows) {
+    if (topk_rows == nullptr) return fail(FRN_ERR_INVALID, "topk_rows pointer array is NULL");
+    if (num_rows == nullptr) return fail(FRN_ERR_INVALID, "num_rows array is NULL");
+    g.topk_w = topk_w;
+    g.ep = true;
+    for (int r = 0; r < R && r < FRN_MAX_R; ++r) {
+        g.rows[r] = topk_rows[r];
+        g.num_rows[r] = num_rows[r];
+    }
+    return FRN_OK;
+}
+
 // Fill the source part of the argument block: partials (k == 0) or the
 // finalize operands (k > 0).
 frn_status set_sources(Call& c, const void* const* src, const void* const* shared, int32_t R,
-                       const float* topk_w, const int32_t* topk_row, int32_t k,
-                       int64_t num_rows, int64_t T, int64_t H) {
+                       const Routing& g, int32_t k, int64_t T, int64_t H) {
     static const char* const kSrcNames[FRN_MAX_R] = {
         "src[0]", "src[1]", "src[2]", "src[3]", "src[4]", "src[5]", "src[6]", "src[7]",
         "src[8]", "src[9]", "src[10]", "src[11]", "src[12]", "src[13]", "src[14]", "src[15]"};
@@ -125,33 +159,50 @@ frn_status set_sources(Call& c, const void* const* src, const void* const* share
         "shared[0]", "shared[1]", "shared[2]", "shared[3]", "shared[4]", "shared[5]",
         "shared[6]", "shared[7]", "shared[8]", "shared[9]", "shared[10]", "shared[11]",
         "shared[12]", "shared[13]", "shared[14]", "shared[15]"};
+    static const char* const kRowNames[FRN_MAX_R] = {
+        "topk_rows[0]", "topk_rows[1]", "topk_rows[2]", "topk_rows[3]", "topk_rows[4]",
+        "topk_rows[5]", "topk_rows[6]", "topk_rows[7]", "topk_rows[8]", "topk_rows[9]",
+        "topk_rows[10]", "topk_rows[11]", "topk_rows[12]", "topk_rows[13]", "topk_rows[14]",
+        "topk_rows[15]"};
     if (src == nullptr) return fail(FRN_ERR_INVALID, "source pointer array is NULL");
     const size_t row_bytes = (size_t)H * 2;
     frn_status st;
+    c.a.ep = 0;
     if (k > 0) {
-        if (num_rows < 1) return fail(FRN_ERR_INVALID, "num_rows must be >= 1");
-        if (num_rows > (int64_t)0x7fffffff)
-            return fail(FRN_ERR_UNSUPPORTED, "num_rows exceeds int32 indexing");
-        if ((st = add_in(c, "topk_w", topk_w, (size_t)T * k * 4, false)) != FRN_OK) return st;
-        if ((st = add_in(c, "topk_row", topk_row, (size_t)T * k * 4, false)) != FRN_OK) return st;
-        c.a.topk_w = topk_w;
-        c.a.topk_row = topk_row;
-        c.a.num_rows = num_rows;
+        if ((st = add_in(c, "topk_w", g.topk_w, (size_t)T * k * 4, false)) != FRN_OK) return st;
+        c.a.topk_w = g.topk_w;
+        c.a.ep = g.ep ? 1 : 0;
+        for (int r = 0; r < R; ++r) {
+            const int64_t n = g.num_rows[r];
+            if (n < (g.ep ? 0 : 1))
+                return fail(FRN_ERR_INVALID, g.ep ? "num_rows[%d] is negative"
+                                                  : "num_rows must be >= 1", r);
+            if (n > (int64_t)0x7fffffff)
+                return fail(FRN_ERR_UNSUPPORTED, "num_rows exceeds int32 indexing");
+            if (g.ep || r == 0) {
+                st = add_in(c, g.ep ? kRowNames[r] : "topk_row", g.rows[r], (size_t)T * k * 4,
+                            false);
+                if (st != FRN_OK) return st;
+            }
+            c.a.topk_row[r] = g.rows[r];
+            c.a.num_rows[r] = n;
+        }
     }
-    const size_t src_bytes = (k > 0 ? (size_t)num_rows : (size_t)T) * row_bytes;
     for (int r = 0; r < R; ++r) {
-        if ((st = add_in(c, kSrcNames[r], src[r], src_bytes)) != FRN_OK) return st;
         c.a.src[r] = static_cast<const uint4*>(src[r]);
         c.a.shared[r] = nullptr;
+        // an expert-parallel rank without rows never has its buffer read
+        if (k > 0 && g.ep && g.num_rows[r] == 0 && src[r] == nullptr) continue;
+        const size_t bytes = (k > 0 ? (size_t)g.num_rows[r] : (size_t)T) * row_bytes;
+        if ((st = add_in(c, kSrcNames[r], src[r], bytes)) != FRN_OK) return st;
     }
-    c.a.has_shared = 0;
     if (k > 0 && shared != nullptr) {
         for (int r = 0; r < R; ++r) {
+            if (g.ep && shared[r] == nullptr) continue;  // this rank holds no shared expert
             if ((st = add_in(c, kSharedNames[r], shared[r], (size_t)T * row_bytes)) != FRN_OK)
                 return st;
             c.a.shared[r] = static_cast<const uint4*>(shared[r]);
         }
-        c.a.has_shared = 1;
     }
     c.a.R = R;
     c.a.k = k;
@@ -208,16 +259,14 @@ frn_status set_workspace(Call& c, void* workspace, size_t workspace_bytes, int32
 }
 
 frn_status fused(const void* const* src, const void* const* shared, int32_t R,
-                 const float* topk_w, const int32_t* topk_row, int32_t k, int64_t num_rows,
-                 int32_t epilogue, const void* residual_in, const float* g1, const float* g2,
+                 const Routing& g, int32_t k, int32_t epilogue, const void* residual_in, const float* g1, const float* g2,
                  float eps, int64_t T, int64_t H, void* out, void* residual_out,
                  void* workspace, size_t workspace_bytes, void* stream) {
     g_last_error[0] = '\0';
     frn_status st = check_sizes(R, k, T, H, epilogue);
     if (st != FRN_OK || T == 0) return st;  // empty tensors may carry null pointers
     Call c{};
-    if ((st = set_sources(c, src, shared, R, topk_w, topk_row, k, num_rows, T, H)) != FRN_OK)
-        return st;
+    if ((st = set_sources(c, src, shared, R, g, k, T, H)) != FRN_OK) return st;
     if ((st = set_epilogue(c, epilogue, residual_in, g1, g2, eps, T, H, out, residual_out)) !=
         FRN_OK)
         return st;
@@ -227,14 +276,13 @@ frn_status fused(const void* const* src, const void* const* shared, int32_t R,
 }
 
 frn_status pass1(const void* const* src, const void* const* shared, int32_t R,
-                 const float* topk_w, const int32_t* topk_row, int32_t k, int64_t num_rows,
-                 int64_t T, int64_t H, void* sum_out, void* stream) {
+                 const Routing& g, int32_t k, int64_t T, int64_t H, void* sum_out,
+                 void* stream) {
     g_last_error[0] = '\0';
     frn_status st = check_sizes(R, k, T, H, frn::kStoreSum);
     if (st != FRN_OK || T == 0) return st;
     Call c{};
-    if ((st = set_sources(c, src, shared, R, topk_w, topk_row, k, num_rows, T, H)) != FRN_OK)
-        return st;
+    if ((st = set_sources(c, src, shared, R, g, k, T, H)) != FRN_OK) return st;
     if ((st = add_out(c, "sum_out", sum_out, (size_t)T * H * 2)) != FRN_OK) return st;
     if ((st = check_alias(c)) != FRN_OK) return st;
     c.a.out = static_cast<uint4*>(sum_out);
@@ -248,7 +296,7 @@ FRN_API frn_status frn_reduce_residual_rmsnorm(const void* const* partials, int3
                                                float eps, int64_t T, int64_t H, void* out,
                                                void* residual_out, void* workspace,
                                                size_t workspace_bytes, void* stream) {
-    return fused(partials, nullptr, R, nullptr, nullptr, 0, 0, FRN_EPI_RMSNORM, residual_in,
+    return fused(partials, nullptr, R, Routing{}, 0, FRN_EPI_RMSNORM, residual_in,
                  gamma, nullptr, eps, T, H, out, residual_out, workspace, workspace_bytes,
                  stream);
 }
@@ -259,7 +307,7 @@ FRN_API frn_status frn_reduce_sandwich_norm(const void* const* partials, int32_t
                                             int64_t H, void* out, void* residual_out,
                                             void* workspace, size_t workspace_bytes,
                                             void* stream) {
-    return fused(partials, nullptr, R, nullptr, nullptr, 0, 0, FRN_EPI_SANDWICH, residual_in,
+    return fused(partials, nullptr, R, Routing{}, 0, FRN_EPI_SANDWICH, residual_in,
                  gamma1, gamma2, eps, T, H, out, residual_out, workspace, workspace_bytes,
                  stream);
 }
@@ -278,14 +326,14 @@ FRN_API frn_status frn_moe_finalize_reduce_norm(
         g_last_error[0] = '\0';
         return fail(FRN_ERR_INVALID, "unknown epilogue %d", epilogue);
     }
-    return fused(expert_rows, shared, R, topk_w, topk_row, k, num_rows, epilogue, residual_in,
-                 gamma1, gamma2, eps, T, H, out, residual_out, workspace, workspace_bytes,
-                 stream);
+    return fused(expert_rows, shared, R, tp_routing(R, topk_w, topk_row, num_rows), k, epilogue,
+                 residual_in, gamma1, gamma2, eps, T, H, out, residual_out, workspace,
+                 workspace_bytes, stream);
 }
 
 FRN_API frn_status frn_reduce_bf16(const void* const* partials, int32_t R, int64_t T, int64_t H,
                                    void* sum_out, void* stream) {
-    return pass1(partials, nullptr, R, nullptr, nullptr, 0, 0, T, H, sum_out, stream);
+    return pass1(partials, nullptr, R, Routing{}, 0, T, H, sum_out, stream);
 }
 
 FRN_API frn_status frn_moe_finalize_reduce_bf16(const void* const* expert_rows,
@@ -297,7 +345,8 @@ FRN_API frn_status frn_moe_finalize_reduce_bf16(const void* const* expert_rows,
         g_last_error[0] = '\0';
         return fail(FRN_ERR_INVALID, "k must be >= 1 for the finalize (got %d)", k);
     }
-    return pass1(expert_rows, shared, R, topk_w, topk_row, k, num_rows, T, H, sum_out, stream);
+    return pass1(expert_rows, shared, R, tp_routing(R, topk_w, topk_row, num_rows), k, T, H,
+                 sum_out, stream);
 }
 
 FRN_API frn_status frn_split_reduce_norm(const void* const* src, const void* const* shared,
@@ -314,7 +363,8 @@ FRN_API frn_status frn_split_reduce_norm(const void* const* src, const void* con
     frn_status st = check_sizes(R, k, T, H, epilogue);
     if (st != FRN_OK || T == 0) return st;
     Call c1{};
-    if ((st = set_sources(c1, src, shared, R, topk_w, topk_row, k, num_rows, T, H)) != FRN_OK)
+    if ((st = set_sources(c1, src, shared, R, tp_routing(R, topk_w, topk_row, num_rows), k, T,
+                          H)) != FRN_OK)
         return st;
     if ((st = add_out(c1, "scratch", scratch, (size_t)T * H * 2)) != FRN_OK) return st;
     // the scratch tensor must not overlap the pass-2 operands either
@@ -325,8 +375,7 @@ FRN_API frn_status frn_split_reduce_norm(const void* const* src, const void* con
     c1.a.out = static_cast<uint4*>(scratch);
     Call c2{};
     const void* one[1] = {scratch};
-    if ((st = set_sources(c2, one, nullptr, 1, nullptr, nullptr, 0, 0, T, H)) != FRN_OK)
-        return st;
+    if ((st = set_sources(c2, one, nullptr, 1, Routing{}, 0, T, H)) != FRN_OK) return st;
     if ((st = set_epilogue(c2, epilogue, residual_in, gamma1, gamma2, eps, T, H, out,
                            residual_out)) != FRN_OK)
         return st;
@@ -334,23 +383,20 @@ FRN_API frn_status frn_split_reduce_norm(const void* const* src, const void* con
     return run(c2, epilogue, T, stream);
 }
 
-FRN_API frn_status frn_moe_finalize(const void* const* expert_rows, const void* const* shared,
-                                    int32_t R, const float* topk_w, const int32_t* topk_row,
-                                    int32_t k, int64_t num_rows, int64_t T, int64_t H,
-                                    void* const* partials_out, void* stream) {
+namespace {
+
+// The per-rank finalize alone, materialized into R BF16 tensors.
+frn_status finalize_only(const void* const* expert_rows, const void* const* shared, int32_t R,
+                         const Routing& g, int32_t k, int64_t T, int64_t H,
+                         void* const* partials_out, void* stream) {
     static const char* const kOutNames[FRN_MAX_R] = {
         "partials_out[0]", "partials_out[1]", "partials_out[2]", "partials_out[3]",
         "partials_out[4]", "partials_out[5]", "partials_out[6]", "partials_out[7]",
         "partials_out[8]", "partials_out[9]", "partials_out[10]", "partials_out[11]",
         "partials_out[12]", "partials_out[13]", "partials_out[14]", "partials_out[15]"};
-    g_last_error[0] = '\0';
-    if (k < 1) return fail(FRN_ERR_INVALID, "k must be >= 1 for the finalize (got %d)", k);
-    frn_status st = check_sizes(R, k, T, H, frn::kStoreSum);
-    if (st != FRN_OK || T == 0) return st;
+    frn_status st;
     Call c{};
-    if ((st = set_sources(c, expert_rows, shared, R, topk_w, topk_row, k, num_rows, T, H)) !=
-        FRN_OK)
-        return st;
+    if ((st = set_sources(c, expert_rows, shared, R, g, k, T, H)) != FRN_OK) return st;
     if (partials_out == nullptr) return fail(FRN_ERR_INVALID, "partials_out array is NULL");
     for (int r = 0; r < R; ++r) {
         if ((st = add_out(c, kOutNames[r], partials_out[r], (size_t)T * H * 2)) != FRN_OK)
@@ -361,6 +407,52 @@ FRN_API frn_status frn_moe_finalize(const void* const* expert_rows, const void* 
     const hipError_t e = frn::launch_finalize(c.a, T, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(FRN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return FRN_OK;
+}
+
+}  // namespace
+
+FRN_API frn_status frn_moe_finalize(const void* const* expert_rows, const void* const* shared,
+                                    int32_t R, const float* topk_w, const int32_t* topk_row,
+                                    int32_t k, int64_t num_rows, int64_t T, int64_t H,
+                                    void* const* partials_out, void* stream) {
+    g_last_error[0] = '\0';
+    if (k < 1) return fail(FRN_ERR_INVALID, "k must be >= 1 for the finalize (got %d)", k);
+    frn_status st = check_sizes(R, k, T, H, frn::kStoreSum);
+    if (st != FRN_OK || T == 0) return st;
+    return finalize_only(expert_rows, shared, R, tp_routing(R, topk_w, topk_row, num_rows), k,
+                         T, H, partials_out, stream);
+}
+
+FRN_API frn_status frn_ep_moe_finalize_reduce_norm(
+    const void* const* expert_rows, const void* const* shared, int32_t R, const float* topk_w,
+    const int32_t* const* topk_rows, int32_t k, const int64_t* num_rows, int32_t epilogue,
+    const void* residual_in, const float* gamma1, const float* gamma2, float eps, int64_t T,
+    int64_t H, void* out, void* residual_out, void* workspace, size_t workspace_bytes,
+    void* stream) {
+    g_last_error[0] = '\0';
+    if (k < 1) return fail(FRN_ERR_INVALID, "k must be >= 1 for the finalize (got %d)", k);
+    if (epilogue != FRN_EPI_RMSNORM && epilogue != FRN_EPI_SANDWICH)
+        return fail(FRN_ERR_INVALID, "unknown epilogue %d", epilogue);
+    frn_status st = check_sizes(R, k, T, H, epilogue);
+    if (st != FRN_OK || T == 0) return st;
+    Routing g;
+    if ((st = ep_routing(g, R, topk_w, topk_rows, num_rows)) != FRN_OK) return st;
+    return fused(expert_rows, shared, R, g, k, epilogue, residual_in, gamma1, gamma2, eps, T, H,
+                 out, residual_out, workspace, workspace_bytes, stream);
+}
+
+FRN_API frn_status frn_ep_moe_finalize(const void* const* expert_rows,
+                                       const void* const* shared, int32_t R,
+                                       const float* topk_w, const int32_t* const* topk_rows,
+                                       int32_t k, const int64_t* num_rows, int64_t T, int64_t H,
+                                       void* const* partials_out, void* stream) {
+    g_last_error[0] = '\0';
+    if (k < 1) return fail(FRN_ERR_INVALID, "k must be >= 1 for the finalize (got %d)", k);
+    frn_status st = check_sizes(R, k, T, H, frn::kStoreSum);
+    if (st != FRN_OK || T == 0) return st;
+    Routing g;
+    if ((st = ep_routing(g, R, topk_w, topk_rows, num_rows)) != FRN_OK) return st;
+    return finalize_only(expert_rows, shared, R, g, k, T, H, partials_out, stream);
 }
 
 FRN_API frn_status frn_set_launch_table(const char* text) {

@@ -22,15 +22,16 @@ enum Epilogue : int {
 // values for gamma); nvec = H / 8 vectors per row.
 struct RowArgs {
     const uint4* src[FRN_MAX_R];     // partials [T,H], or expert rows [num_rows,H]
-    const uint4* shared[FRN_MAX_R];  // shared-expert rows [T,H] (finalize), may be null
+    const uint4* shared[FRN_MAX_R];  // shared-expert rows [T,H] per rank (finalize), or null
     const float* topk_w;             // [T,k]
-    const int32_t* topk_row;         // [T,k]
+    const int32_t* topk_row[FRN_MAX_R];  // [T,k] per rank (the same array for every rank
+                                         // unless routing is expert-parallel)
     const uint4* residual;           // [T,H]
     const float4* gamma1;            // [H]
     const float4* gamma2;            // [H]
     uint4* out;                      // [T,H] normed output, or the pass-1 sum
     uint4* residual_out;             // [T,H]
-    int64_t num_rows;                // rows in each expert buffer
+    int64_t num_rows[FRN_MAX_R];     // rows in each rank's expert buffer
     int64_t T;                       // token rows of the call
     uint4* ws_p;                     // split-row finalize: R x T x nvec BF16 partials, or null
     uint4* part_out[FRN_MAX_R];      // finalize_slices_kernel: [T,H] BF16 output per rank
@@ -39,7 +40,8 @@ struct RowArgs {
     int32_t nvec;                    // H / 8
     int32_t H;
     float eps;
-    int32_t has_shared;
+    int32_t ep;                      // expert-parallel routing: a negative row index
+                                     // marks a slot of another rank's expert
 };
 
 // Split-row finalize (small T): workgroup size, the largest T it serves and

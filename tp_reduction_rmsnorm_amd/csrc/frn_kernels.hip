@@ -215,12 +215,15 @@ __device__ __forceinline__ void reduce_ranks(RankRow rank_row, int R, const Lane
 // Finalize of one rank for token t over the lane's vectors, before the BF16
 // rounding: acc = sum_j w_j * E[row_j] (+ shared), j in order, top-k slots
 // loaded in chunks of C.  A row index outside [0, num_rows) is never
-// dereferenced; its slot reads as NaN.
+// dereferenced; its slot reads as NaN -- except that with expert-parallel
+// routing (a.ep) a negative index marks a slot of another rank's expert,
+// which takes no part in this rank's sum.
 template <int V, int C>
 __device__ __forceinline__ void finalize_rank(const RowArgs& a, int r, int64_t t,
                                               const Lanes<V>& L, float (&acc)[V][8]) {
     const int k = a.k;
-    const int32_t* rows_t = a.topk_row + t * k;
+    const int32_t* rows_t = a.topk_row[r] + t * k;
+    const int64_t num_rows = a.num_rows[r];
     const float* w_t = a.topk_w + t * k;
     const uint4 nan8 = make_uint4(0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u);
     const uint4* E = a.src[r];
@@ -232,13 +235,16 @@ __device__ __forceinline__ void finalize_rank(const RowArgs& a, int r, int64_t t
     for (int j0 = 0; j0 < k; j0 += C) {
         uint4 e[C][V];
         float w[C];
+        bool use[C];
 #pragma unroll
         for (int c = 0; c < C; ++c) {
             w[c] = 0.0f;
+            use[c] = false;
             if (j0 + c < k) {
                 const int32_t er = rows_t[j0 + c];
                 w[c] = w_t[j0 + c];
-                const bool in = er >= 0 && (int64_t)er < a.num_rows;
+                use[c] = !(a.ep && er < 0);
+                const bool in = er >= 0 && (int64_t)er < num_rows;
                 const int64_t base = (int64_t)(in ? er : 0) * nvec;
 #pragma unroll
                 for (int j = 0; j < V; ++j) {
@@ -249,7 +255,7 @@ __device__ __forceinline__ void finalize_rank(const RowArgs& a, int r, int64_t t
         }
 #pragma unroll
         for (int c = 0; c < C; ++c) {
-            if (j0 + c < k) {
+            if (use[c]) {
 #pragma unroll
                 for (int j = 0; j < V; ++j) {
                     float f[8];
@@ -263,8 +269,9 @@ __device__ __forceinline__ void finalize_rank(const RowArgs& a, int r, int64_t t
             }
         }
     }
-    if (a.has_shared) {
-        const uint4* S = a.shared[r] + t * nvec;
+    const uint4* S = a.shared[r];
+    if (S != nullptr) {
+        S += t * nvec;
 #pragma unroll
         for (int j = 0; j < V; ++j) {
             uint4 q = make_uint4(0, 0, 0, 0);
@@ -451,9 +458,12 @@ hipError_t launch_rows(const RowArgs& a_in, int epilogue, int64_t T, hipStream_t
         for (int r = 0; r < a.R; ++r) a.part_out[r] = a.ws_p + (int64_t)r * T * a.nvec;
         const hipError_t e = launch_finalize(a, T, stream);
         if (e != hipSuccess) return e;
-        for (int r = 0; r < a.R; ++r) a.src[r] = a.part_out[r];
+        for (int r = 0; r < a.R; ++r) {
+            a.src[r] = a.part_out[r];
+            a.shared[r] = nullptr;
+        }
         a.k = 0;
-        a.has_shared = 0;
+        a.ep = 0;
     }
     const bool fin = a.k > 0;
     const LaunchShape sh = choose_shape(a.nvec, fin, T, epilogue, a.R, a.k);
