@@ -269,7 +269,9 @@ frn_status frn_query(int32_t R, int32_t k, int64_t T, int64_t H, int32_t epilogu
  * line, '#' starts a comment:
  *     H  R  k  epilogue  Tmin  Tmax  vec
  * H, R, k, Tmin, Tmax: integers or '*' (any); k = 0 means no finalize;
- * epilogue: rmsnorm | sandwich | sum (split pass 1) | *; vec: 1 | 2 | 4.
+ * epilogue: rmsnorm | sandwich | sum (split pass 1) for calls without
+ * expert-parallel routing, ep-rmsnorm | ep-sandwich | ep-* for
+ * frn_ep_moe_finalize_reduce_norm, or * (every call); vec: 1 | 2 | 4.
  * The first rule that matches a call and fits it (at most 1024 lanes; vec 4
  * only without finalize and outside split pass 1) decides.  Results are
  * identical for every shape; only speed changes.  tp_reduction_rmsnorm_amd/
@@ -283,8 +285,11 @@ frn_status frn_query(int32_t R, int32_t k, int64_t T, int64_t H, int32_t epilogu
 frn_status frn_set_launch_table(const char* text);
 
 /* The shape (lanes per workgroup, vectors per lane) the one-row kernel gets
- * for a call of these sizes, without launching.  threads, vectors: host
+ * for a call of these sizes, without launching.  epilogue: FRN_EPI_RMSNORM,
+ * FRN_EPI_SANDWICH or 2 (split pass 1), OR'ed with FRN_SHAPE_EP for a call
+ * of frn_ep_moe_finalize_reduce_norm (k >= 1).  threads, vectors: host
  * pointers to receive the values. */
+#define FRN_SHAPE_EP 16
 frn_status frn_launch_shape(int32_t R, int32_t k, int64_t T, int64_t H, int32_t epilogue,
                             int32_t* threads, int32_t* vectors);
 

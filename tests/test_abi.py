@@ -374,6 +374,32 @@ def test_launch_shape_builtin_rule():
     assert frn.launch_shape(2, 8, 1024, 7168, frn.EPI_SUM) == (896, 1)
     assert frn.launch_shape(2, 0, 1024, 7168, frn.EPI_SUM) == (448, 2)  # no 4 in pass 1
     assert frn.launch_shape(2, 0, 8, 16384, S) == (1024, 2)
+    # expert-parallel finalize: one vector per lane at every T
+    assert frn.launch_shape(8, 10, 1024, 6144, 0, ep=True) == (768, 1)
+    assert frn.launch_shape(8, 10, 1024, 6144, 0) == (384, 2)
+    assert frn.launch_shape(2, 4, 64, 16384, S, ep=True) == (1024, 2)
+    with pytest.raises(ValueError):
+        frn.launch_shape(8, 0, 1024, 6144, 0, ep=True)      # no finalize
+    with pytest.raises(ValueError):
+        frn.launch_shape(8, 10, 1024, 6144, frn.EPI_SUM, ep=True)
+
+
+def test_launch_table_expert_parallel_rules():
+    import tp_reduction_rmsnorm_amd as frn
+    try:
+        frn.set_launch_table("6144 8 10 ep-rmsnorm 0 * 2\n6144 8 10 rmsnorm 0 * 1\n")
+        assert frn.launch_shape(8, 10, 4096, 6144, 0, ep=True) == (384, 2)
+        assert frn.launch_shape(8, 10, 4096, 6144, 0) == (768, 1)
+        frn.set_launch_table("* * * ep-* 0 * 2\n")
+        assert frn.launch_shape(8, 10, 64, 6144, frn.EPI_SANDWICH, ep=True) == (384, 2)
+        assert frn.launch_shape(8, 10, 4096, 6144, 0) == (768, 1)   # TP: built-in rule
+        frn.set_launch_table("* * * * 0 * 2\n")                    # '*' matches both
+        assert frn.launch_shape(8, 10, 4096, 6144, 0, ep=True) == (384, 2)
+        for bad in ("6144 8 10 ep-sum 0 * 1\n", "6144 8 10 ep 0 * 1\n", "1 1 1 ep-x 0 * 1\n"):
+            with pytest.raises(ValueError):
+                frn.set_launch_table(bad)
+    finally:
+        frn.set_launch_table(None)
 
 
 def test_launch_table_overrides_and_restores():

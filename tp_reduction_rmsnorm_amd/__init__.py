@@ -38,6 +38,8 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfused_reduce_norm.so")
 
+SHAPE_EP = 16  # FRN_SHAPE_EP
+
 FRN_OK = 0
 FRN_ERR_INVALID = 1
 FRN_ERR_UNSUPPORTED = 2
@@ -151,10 +153,13 @@ def set_launch_table(text: Optional[str]) -> None:
     _check(_c_set_table(None if text is None else text.encode()))
 
 
-def launch_shape(R: int, k: int, T: int, H: int, epilogue: int = EPI_RMSNORM):
-    """(lanes per workgroup, vectors per lane) the one-row kernel would use."""
+def launch_shape(R: int, k: int, T: int, H: int, epilogue: int = EPI_RMSNORM, *,
+                 ep: bool = False):
+    """(lanes per workgroup, vectors per lane) the one-row kernel would use;
+    ``ep=True`` for an ``ep_moe_finalize_reduce_norm`` call."""
     th, v = _I32(), _I32()
-    _check(_c_shape(R, k, T, H, epilogue, ctypes.byref(th), ctypes.byref(v)))
+    _check(_c_shape(R, k, T, H, epilogue | (SHAPE_EP if ep else 0), ctypes.byref(th),
+                    ctypes.byref(v)))
     return th.value, v.value
 
 

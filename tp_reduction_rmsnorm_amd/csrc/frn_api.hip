@@ -465,12 +465,16 @@ FRN_API frn_status frn_set_launch_table(const char* text) {
 FRN_API frn_status frn_launch_shape(int32_t R, int32_t k, int64_t T, int64_t H, int32_t epilogue,
                                     int32_t* threads, int32_t* vectors) {
     g_last_error[0] = '\0';
+    const bool ep = (epilogue & FRN_SHAPE_EP) != 0;
+    epilogue &= ~FRN_SHAPE_EP;
+    if (ep && (k < 1 || epilogue == frn::kStoreSum))
+        return fail(FRN_ERR_INVALID, "FRN_SHAPE_EP needs k >= 1 and a norm epilogue");
     frn_status st = check_sizes(R, k, T, H, epilogue);
     if (st != FRN_OK) return st;
     if (threads == nullptr || vectors == nullptr)
         return fail(FRN_ERR_INVALID, "threads and vectors must not be NULL");
-    const frn::LaunchShape sh =
-        frn::choose_shape((int)(H / 8), k > 0, T, epilogue, R, k);
+    const int fin = k == 0 ? frn::kNoFinalize : (ep ? frn::kEpFinalize : frn::kTpFinalize);
+    const frn::LaunchShape sh = frn::choose_shape((int)(H / 8), fin, T, epilogue, R, k);
     *threads = sh.threads;
     *vectors = sh.vec;
     return FRN_OK;

@@ -67,10 +67,13 @@ struct LaunchShape {
     int vec;
 };
 
+// Finalize kind of a call: none, TP routing, or expert-parallel routing.
+enum FinKind { kNoFinalize = 0, kTpFinalize = 1, kEpFinalize = 2 };
+
 // Launch shape of row_kernel for a call: the first matching rule of the
 // tuned table (frn_set_launch_table / FRN_LAUNCH_TABLE) that fits the call,
-// else the built-in rule.  Thread-safe.
-LaunchShape choose_shape(int nvec, bool finalize, int64_t T, int epilogue, int R, int k);
+// else the built-in rule.  fin: a FinKind.  Thread-safe.
+LaunchShape choose_shape(int nvec, int fin, int64_t T, int epilogue, int R, int k);
 
 // Replace the tuned table (text as documented at frn_set_launch_table; NULL
 // clears it).  Returns nullptr on success, else a message naming the line.

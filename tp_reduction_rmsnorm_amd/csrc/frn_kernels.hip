@@ -284,6 +284,161 @@ __device__ __forceinline__ void finalize_rank(const RowArgs& a, int r, int64_t t
     }
 }
 
+// The finalize of every rank for token t, then the FP32 sum of the R
+// rounded partials, as a work list that crosses rank boundaries.
+//
+// The token's rows are numbered as pairs p = r * (k + 1) + j: slot j < k of
+// rank r, and j == k for rank r's shared-expert row.  A pair is live when
+// its row enters the sum: a slot under TP routing always (an index out of
+// range then reads as NaN), under expert-parallel routing when its index is
+// >= 0; a shared row when rank r has one.  Each wave finds the live pairs of
+// a 64-pair word with one ballot (every wave computes the same masks, so no
+// LDS or barrier is needed), and the lane of pair p keeps its row index and
+// weight for a readlane.  Live pairs are loaded C at a time in pair order,
+// across rank boundaries, and consumed in the same order: rank r's
+// accumulator takes its slots in j order and its shared row last, then is
+// rounded to BF16 and added to s when the list moves past rank r.  This is
+// the arithmetic of finalize_rank followed by the rank sum, with the loads
+// of several ranks in flight at once.
+struct PairWord {
+    uint64_t live;      // uniform: bit l = pair 64 * word + l is live
+    const uint4* row;   // lane l: start of its pair's row, or null (index out of range)
+    float w;            // lane l: weight of its pair (slots)
+    int32_t meta;       // lane l: its rank, plus kSharedPair for a shared-expert row
+};
+
+constexpr int32_t kSharedPair = 256;
+
+// One word of token t's pairs (see finalize_reduce).  Each lane resolves its
+// pair's row address, so the loop that loads the rows only reads lanes.
+__device__ __forceinline__ PairWord pair_word(const RowArgs& a, int64_t t, int word) {
+    const int k = a.k;
+    const int k1 = k + 1;
+    const int p = word * 64 + (int)(threadIdx.x & 63);
+    bool live = false;
+    PairWord pw;
+    pw.row = nullptr;
+    pw.w = 0.0f;
+    pw.meta = 0;
+    if (p < a.R * k1) {
+        const int r = p / k1;
+        const int j = p - r * k1;
+        const int32_t* rows = nullptr;
+        const uint4* src = nullptr;
+        const uint4* shared = nullptr;
+        int64_t num_rows = 0;
+        for (int rr = 0; rr < a.R; ++rr) {
+            if (rr == r) {
+                rows = a.topk_row[rr];
+                src = a.src[rr];
+                shared = a.shared[rr];
+                num_rows = a.num_rows[rr];
+            }
+        }
+        if (j < k) {
+            const int32_t row = rows[t * k + j];
+            pw.w = a.topk_w[t * k + j];
+            pw.meta = r;
+            live = !a.ep || row >= 0;
+            if (row >= 0 && (int64_t)row < num_rows) pw.row = src + (int64_t)row * a.nvec;
+        } else {
+            pw.meta = r | kSharedPair;
+            live = shared != nullptr;
+            if (live) pw.row = shared + t * a.nvec;
+        }
+    }
+    pw.live = __ballot(live);
+    return pw;
+}
+
+template <int V>
+__device__ __forceinline__ void add_partial(int r, float (&acc)[V][8], float (&s)[V][8]) {
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+        float q[8];
+        widen(narrow(acc[j]), q);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            s[j][i] = (r == 0) ? q[i] : s[j][i] + q[i];
+            acc[j][i] = 0.0f;
+        }
+    }
+}
+
+template <int V, int C>
+__device__ __forceinline__ void finalize_reduce(const RowArgs& a, int64_t t, const Lanes<V>& L,
+                                                float (&s)[V][8]) {
+    const uint4 nan8 = make_uint4(0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u);
+    const int k = a.k;
+    const int k1 = k + 1;
+    const int words = (a.R * k1 + 63) >> 6;
+    float acc[V][8];
+#pragma unroll
+    for (int j = 0; j < V; ++j)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[j][i] = 0.0f;
+    int cur = 0;  // rank whose accumulator is open
+    // The next word's indices and weights are loaded one word ahead, before
+    // this word's rows: loads complete in order, so by the time the next
+    // word is needed (every row load of this one consumed) they have arrived.
+    PairWord next = pair_word(a, t, 0);
+    for (int word = 0; word < words; ++word) {
+        const PairWord pw = next;
+        if (word + 1 < words) next = pair_word(a, t, word + 1);
+        uint64_t m = pw.live;
+        while (m != 0) {
+            uint4 e[C][V];
+            float wc[C];
+            int rc[C];
+            bool slot[C], has[C];
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+                has[c] = m != 0;
+                slot[c] = false;
+                wc[c] = 0.0f;
+                rc[c] = 0;
+                if (has[c]) {
+                    const int bit = __builtin_ctzll(m);
+                    m &= m - 1;
+                    const int meta = __builtin_amdgcn_readlane(pw.meta, bit);
+                    const uintptr_t addr = pw.row == nullptr ? 0 : (uintptr_t)pw.row;
+                    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)addr, bit);
+                    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(addr >> 32), bit);
+                    const uint4* E = (const uint4*)(((uint64_t)hi << 32) | lo);
+                    rc[c] = meta & (kSharedPair - 1);
+                    slot[c] = (meta & kSharedPair) == 0;
+                    wc[c] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pw.w), bit));
+#pragma unroll
+                    for (int j = 0; j < V; ++j) {
+                        e[c][j] = nan8;
+                        if (E != nullptr && L.ok[j]) e[c][j] = ld_stream(E + L.vi[j]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+                if (!has[c]) continue;
+                while (cur < rc[c]) add_partial<V>(cur++, acc, s);
+#pragma unroll
+                for (int j = 0; j < V; ++j) {
+                    float f[8];
+                    widen(e[c][j], f);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        if (slot[c]) {
+                            const float prod = wc[c] * f[i];
+                            acc[j][i] = acc[j][i] + prod;
+                        } else {
+                            acc[j][i] = acc[j][i] + f[i];
+                        }
+                    }
+                }
+            }
+        }
+    }
+    while (cur < a.R) add_partial<V>(cur++, acc, s);
+}
+
 // Epilogue of one row: residual add and norm(s), stores of out and
 // residual_out (or the pass-1 sum).  Every lane of the workgroup takes part
 // (the row-wide sums synchronise the workgroup).
@@ -347,10 +502,15 @@ __device__ __forceinline__ void epilogue(const RowArgs& a, int64_t row, const La
 
 // ------------------------------------------------------------ kernels --- //
 
+// Finalize variants of the one-row kernel.
+enum Fin { kNoFin = 0, kFinTp = 1, kFinEp = 2 };
+
 // One token row per workgroup.  EPI: epilogue; FIN: top-k finalize ahead of
-// the reduction; V: vectors per lane; C: ranks (no finalize) or top-k slots
-// (finalize) loaded per chunk.
-template <int EPI, bool FIN, int V, int C>
+// the reduction (kFinTp: every rank routes every slot, one rank after the
+// other; kFinEp: expert-parallel routing, the work list across ranks); V:
+// vectors per lane; C: ranks (no finalize), top-k slots (kFinTp) or live
+// rows (kFinEp) loaded per chunk.
+template <int EPI, int FIN, int V, int C>
 __global__ __launch_bounds__(1024) void row_kernel(const RowArgs a) {
     __shared__ double slots[2][16];
     const int64_t t = blockIdx.x;
@@ -367,25 +527,17 @@ __global__ __launch_bounds__(1024) void row_kernel(const RowArgs a) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) s[j][i] = 0.0f;
 
-    if constexpr (!FIN) {
+    if constexpr (FIN == kNoFin) {
         reduce_ranks<V, C, true>([&](int r) { return a.src[r] + row; }, a.R, L, s);
+    } else if constexpr (FIN == kFinEp) {
+        // a rank owns few of the token's slots: keep several ranks' rows in flight
+        finalize_reduce<V, C>(a, t, L, s);
     } else {
         for (int r = 0; r < a.R; ++r) {
             float acc[V][8];
             finalize_rank<V, C>(a, r, t, L, acc);
             // The rank's finalized partial is a BF16 tensor: round, then sum.
-#pragma unroll
-            for (int j = 0; j < V; ++j) {
-                float p[8];
-                widen(narrow(acc[j]), p);
-                if (r == 0) {
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) s[j][i] = p[i];
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) s[j][i] = s[j][i] + p[i];
-                }
-            }
+            add_partial<V>(r, acc, s);
         }
     }
     epilogue<EPI, V>(a, row, L, s, xr, slots);
@@ -406,21 +558,24 @@ __global__ __launch_bounds__(kSplitThreads) void finalize_slices_kernel(const Ro
     if (L.ok[0]) a.part_out[r][t * a.nvec + L.vi[0]] = narrow(acc[0]);
 }
 
-template <int EPI, bool FIN, int V, int C>
+template <int EPI, int FIN, int V, int C>
 hipError_t launch(const RowArgs& a, int64_t T, int threads, hipStream_t stream) {
     hipLaunchKernelGGL((row_kernel<EPI, FIN, V, C>), dim3((unsigned)T), dim3(threads), 0,
                        stream, a);
     return hipGetLastError();
 }
 
-// Ranks (or top-k slots) per load chunk: at most 64 VGPRs of loads in
-// flight per lane (32 for a two-vector finalize, which holds more live
-// state and would otherwise spill).
-template <int EPI, bool FIN, int V>
+// Ranks (or top-k slots, or live rows) per load chunk: at most 64 VGPRs of
+// loads in flight per lane (32 for a two-vector finalize and for the
+// expert-parallel work list, which hold more live state and would otherwise
+// spill or lose occupancy).
+template <int EPI, int FIN, int V>
 hipError_t launch_c(const RowArgs& a, int64_t T, int threads, hipStream_t stream) {
     constexpr int CMAX = 16 / V;
-    if constexpr (FIN) {
+    if constexpr (FIN == kFinTp) {
         return launch<EPI, FIN, V, (V == 1 ? 16 : 4)>(a, T, threads, stream);
+    } else if constexpr (FIN == kFinEp) {
+        return launch<EPI, FIN, V, (V == 1 ? 8 : 4)>(a, T, threads, stream);
     } else {
         if (a.R <= 2) return launch<EPI, FIN, V, 2>(a, T, threads, stream);
         if (a.R <= 4) return launch<EPI, FIN, V, 4>(a, T, threads, stream);
@@ -429,13 +584,20 @@ hipError_t launch_c(const RowArgs& a, int64_t T, int threads, hipStream_t stream
     }
 }
 
-template <int EPI, bool FIN>
+template <int EPI, int FIN>
 hipError_t launch_v(const RowArgs& a, int64_t T, LaunchShape sh, hipStream_t stream) {
     if (sh.vec == 1) return launch_c<EPI, FIN, 1>(a, T, sh.threads, stream);
-    if constexpr (!FIN && EPI != kStoreSum) {
+    if constexpr (FIN == kNoFin && EPI != kStoreSum) {
         if (sh.vec == 4) return launch<EPI, FIN, 4, 4>(a, T, sh.threads, stream);
     }
     return launch_c<EPI, FIN, 2>(a, T, sh.threads, stream);
+}
+
+template <int EPI>
+hipError_t launch_fin(const RowArgs& a, int64_t T, LaunchShape sh, hipStream_t stream) {
+    if (a.k == 0) return launch_v<EPI, kNoFin>(a, T, sh, stream);
+    if (a.ep) return launch_v<EPI, kFinEp>(a, T, sh, stream);
+    return launch_v<EPI, kFinTp>(a, T, sh, stream);
 }
 
 }  // namespace
@@ -465,20 +627,13 @@ hipError_t launch_rows(const RowArgs& a_in, int epilogue, int64_t T, hipStream_t
         a.k = 0;
         a.ep = 0;
     }
-    const bool fin = a.k > 0;
+    const int fin = a.k == 0 ? kNoFinalize : (a.ep ? kEpFinalize : kTpFinalize);
     const LaunchShape sh = choose_shape(a.nvec, fin, T, epilogue, a.R, a.k);
     switch (epilogue) {
-        case kRmsNorm:
-            return fin ? launch_v<kRmsNorm, true>(a, T, sh, stream)
-                       : launch_v<kRmsNorm, false>(a, T, sh, stream);
-        case kSandwich:
-            return fin ? launch_v<kSandwich, true>(a, T, sh, stream)
-                       : launch_v<kSandwich, false>(a, T, sh, stream);
-        case kStoreSum:
-            return fin ? launch_v<kStoreSum, true>(a, T, sh, stream)
-                       : launch_v<kStoreSum, false>(a, T, sh, stream);
-        default:
-            return hipErrorInvalidValue;
+        case kRmsNorm: return launch_fin<kRmsNorm>(a, T, sh, stream);
+        case kSandwich: return launch_fin<kSandwich>(a, T, sh, stream);
+        case kStoreSum: return launch_fin<kStoreSum>(a, T, sh, stream);
+        default: return hipErrorInvalidValue;
     }
 }
 

@@ -16,9 +16,10 @@
 namespace frn {
 namespace {
 
-// One tuned rule; -1 in H, R, k, epilogue means "any".  T in [tmin, tmax].
+// One tuned rule; -1 in H, R, k, epilogue, ep means "any".  T in [tmin,
+// tmax].  ep: 1 for calls with expert-parallel routing, 0 for the others.
 struct Rule {
-    int64_t H, R, k, epilogue;
+    int64_t H, R, k, epilogue, ep;
     int64_t tmin, tmax;
     int vec;
 };
@@ -40,11 +41,27 @@ bool parse_field(const char* tok, int64_t* out) {
     return true;
 }
 
-bool parse_epilogue(const char* tok, int64_t* out) {
-    if (strcmp(tok, "*") == 0) *out = -1;
-    else if (strcmp(tok, "rmsnorm") == 0) *out = kRmsNorm;
+// "rmsnorm" | "sandwich" | "sum" match calls without expert-parallel
+// routing; "ep-rmsnorm" | "ep-sandwich" | "ep-*" match the expert-parallel
+// finalize; "*" matches every call.
+bool parse_epilogue(const char* tok, int64_t* out, int64_t* ep) {
+    if (strcmp(tok, "*") == 0) {
+        *out = -1;
+        *ep = -1;
+        return true;
+    }
+    *ep = 0;
+    if (strncmp(tok, "ep-", 3) == 0) {
+        *ep = 1;
+        tok += 3;
+        if (strcmp(tok, "*") == 0) {
+            *out = -1;
+            return true;
+        }
+    }
+    if (strcmp(tok, "rmsnorm") == 0) *out = kRmsNorm;
     else if (strcmp(tok, "sandwich") == 0) *out = kSandwich;
-    else if (strcmp(tok, "sum") == 0) *out = kStoreSum;
+    else if (strcmp(tok, "sum") == 0 && *ep == 0) *out = kStoreSum;
     else return false;
     return true;
 }
@@ -75,12 +92,12 @@ bool parse(const char* text, std::vector<Rule>& out, std::string& err) {
         int64_t vec = 0;
         if (tok.size() != 7 || !parse_field(tok[0].c_str(), &r.H) ||
             !parse_field(tok[1].c_str(), &r.R) || !parse_field(tok[2].c_str(), &r.k) ||
-            !parse_epilogue(tok[3].c_str(), &r.epilogue) ||
+            !parse_epilogue(tok[3].c_str(), &r.epilogue, &r.ep) ||
             !parse_field(tok[4].c_str(), &r.tmin) || !parse_field(tok[5].c_str(), &r.tmax) ||
             !parse_field(tok[6].c_str(), &vec) || !(vec == 1 || vec == 2 || vec == 4)) {
             err = "launch table line " + std::to_string(lineno) +
                   ": expected 'H R k epilogue Tmin Tmax vec' (numbers or *, epilogue "
-                  "rmsnorm|sandwich|sum|*, vec 1|2|4)";
+                  "rmsnorm|sandwich|sum|ep-rmsnorm|ep-sandwich|ep-*|*, vec 1|2|4)";
             return false;
         }
         if (r.tmin < 0) r.tmin = 0;
@@ -132,11 +149,16 @@ void load_env_table_locked() {
 //    beyond that two vectors for rows over 512 vectors;
 //  - with finalize, one vector per lane up to 1024 lanes, except two for
 //    256 < T <= 2048 outside split pass 1 (H=7168 R=2 k=8: T=512 30.0 ->
-//    27.4 us, T=1024 57.4 -> 53.4 us; at T=4096 one vector is ahead again).
+//    27.4 us, T=1024 57.4 -> 53.4 us; at T=4096 one vector is ahead again);
+//  - with the expert-parallel finalize, one vector per lane up to 1024
+//    lanes at every T: its work list is short per rank, and more tokens in
+//    flight per CU matter more (H=6144 R=8 k=10: T=1024 51.6 -> 43.4 us,
+//    T=4096 167.6 -> 151.2 us against two vectors).
 // Four vectors are never used with the finalize (too many live registers)
 // or for split pass 1 (it spills).
-int builtin_vec(int nvec, bool finalize, int64_t T, int epilogue) {
-    if (finalize) {
+int builtin_vec(int nvec, int fin, int64_t T, int epilogue) {
+    if (fin == kEpFinalize) return nvec <= 1024 ? 1 : 2;
+    if (fin == kTpFinalize) {
         if (T > 256 && T <= 2048 && epilogue != kStoreSum && nvec <= 2048) return 2;
         return nvec <= 1024 ? 1 : 2;
     }
@@ -156,7 +178,9 @@ bool vec_fits(int vec, int nvec, bool finalize, int epilogue) {
 
 }  // namespace
 
-LaunchShape choose_shape(int nvec, bool finalize, int64_t T, int epilogue, int R, int k) {
+LaunchShape choose_shape(int nvec, int fin, int64_t T, int epilogue, int R, int k) {
+    const bool finalize = fin != kNoFinalize;
+    const int64_t ep = fin == kEpFinalize ? 1 : 0;
     int vec = 0;
     {
         std::lock_guard<std::mutex> lock(g_mu);
@@ -164,14 +188,15 @@ LaunchShape choose_shape(int nvec, bool finalize, int64_t T, int epilogue, int R
         const int64_t H = (int64_t)nvec * 8;
         for (const Rule& r : g_rules) {
             if ((r.H < 0 || r.H == H) && (r.R < 0 || r.R == R) && (r.k < 0 || r.k == k) &&
-                (r.epilogue < 0 || r.epilogue == epilogue) && T >= r.tmin && T <= r.tmax &&
+                (r.epilogue < 0 || r.epilogue == epilogue) && (r.ep < 0 || r.ep == ep) &&
+                T >= r.tmin && T <= r.tmax &&
                 vec_fits(r.vec, nvec, finalize, epilogue)) {
                 vec = r.vec;
                 break;
             }
         }
     }
-    if (vec == 0) vec = builtin_vec(nvec, finalize, T, epilogue);
+    if (vec == 0) vec = builtin_vec(nvec, fin, T, epilogue);
     LaunchShape sh;
     sh.vec = vec;
     const int lanes = (nvec + vec - 1) / vec;

@@ -14,7 +14,10 @@ the table with ``FRN_LAUNCH_TABLE=<file>`` or ``set_launch_table(text)``.
 
 Shapes without finalize (k = 0) tune every call of that shape; with k > 0
 the rules matter above T = 256 (below it the finalize runs split-row and
-its reduction pass is a k = 0 call of the same H and R).
+its reduction pass is a k = 0 call of the same H and R).  An epilogue named
+``ep-rmsnorm`` or ``ep-sandwich`` tunes the expert-parallel finalize
+(``ep_moe_finalize_reduce_norm``): each of the R ranks owns an equal share of
+4R experts (at least k), and each token picks k distinct ones at random.
 """
 from __future__ import annotations
 
@@ -29,10 +32,11 @@ sys.path.insert(0, os.path.dirname(HERE))
 
 import tp_reduction_rmsnorm_amd as frn  # noqa: E402
 
-EPI = {"rmsnorm": frn.EPI_RMSNORM, "sandwich": frn.EPI_SANDWICH, "sum": frn.EPI_SUM}
+EPI = {"rmsnorm": frn.EPI_RMSNORM, "sandwich": frn.EPI_SANDWICH, "sum": frn.EPI_SUM,
+       "ep-rmsnorm": frn.EPI_RMSNORM, "ep-sandwich": frn.EPI_SANDWICH}
 DEFAULT_SHAPES = [(5120, 4, 0, "sandwich"), (8192, 8, 0, "sandwich"), (512, 2, 0, "rmsnorm"),
                   (6144, 8, 0, "rmsnorm"), (7168, 2, 8, "rmsnorm"), (7168, 2, 0, "rmsnorm"),
-                  (7168, 2, 8, "sum")]
+                  (7168, 2, 8, "sum"), (6144, 8, 10, "ep-rmsnorm")]
 DEFAULT_TOKENS = [1, 8, 64, 256, 512, 1024, 2048, 4096, 16384]
 
 
@@ -46,7 +50,8 @@ class Call:
     def __init__(self, H, R, k, epi, T, dev):
         g = torch.Generator(device=dev)
         g.manual_seed(H * 131 + R * 17 + k * 7 + T)
-        per_set = T * H * 2 * (R * (k + 1 if k else 1) + 3)
+        self.ep = epi.startswith("ep-")
+        per_set = T * H * 2 * ((k + 1 if self.ep else R * (k + 1 if k else 1)) + 3)
         n = max(1, min(16, -(-(1 << 30) // per_set))) if T >= 256 else 1
         self.H, self.R, self.k, self.epi, self.T = H, R, k, epi, T
         self.sets = []
@@ -55,7 +60,20 @@ class Call:
                      g2=torch.rand(H, generator=g, device=dev) + 0.5,
                      out=torch.empty(T, H, dtype=torch.bfloat16, device=dev),
                      rout=torch.empty(T, H, dtype=torch.bfloat16, device=dev))
-            if k:
+            if self.ep:
+                experts = max(4 * R, -(-k // R) * R)
+                chosen = torch.rand((T, experts), generator=g, device=dev).topk(k, dim=1).indices
+                owner = chosen // (experts // R)
+                d["rows"], d["src"] = [], []
+                for r in range(R):
+                    own = owner == r
+                    idx = torch.full((T, k), -1, dtype=torch.int32, device=dev)
+                    idx[own] = torch.arange(int(own.sum()), dtype=torch.int32, device=dev)
+                    d["rows"].append(idx)
+                    d["src"].append(_bf16((max(1, int(own.sum())), H), dev, g))
+                d["shared"] = [_bf16((T, H), dev, g) if r == 0 else None for r in range(R)]
+                d["w"] = torch.softmax(torch.randn(T, k, generator=g, device=dev), -1)
+            elif k:
                 d["src"] = [_bf16((T * k, H), dev, g) for _ in range(R)]
                 d["shared"] = [_bf16((T, H), dev, g) for _ in range(R)]
                 d["w"] = torch.softmax(torch.randn(T, k, generator=g, device=dev), -1)
@@ -66,6 +84,11 @@ class Call:
 
     def __call__(self, i):
         d = self.sets[i % len(self.sets)]
+        if self.ep:
+            return frn.ep_moe_finalize_reduce_norm(d["src"], d["w"], d["rows"], d["residual"],
+                                                   d["g1"], d["g2"], shared=d["shared"],
+                                                   epilogue=EPI[self.epi], out=d["out"],
+                                                   residual_out=d["rout"], workspace=None)
         if self.epi == "sum":
             if self.k:
                 return frn.moe_finalize_reduce_bf16(d["src"], d["w"], d["idx"], shared=d["shared"],
@@ -118,7 +141,7 @@ def tune_shape(H, R, k, epi, tokens, calls, dev, log=print):
         times = {}
         for vec in (1, 2, 4):
             frn.set_launch_table(f"{H} {R} {k} {epi} {T} {T} {vec}")
-            if frn.launch_shape(R, k, T, H, EPI[epi])[1] != vec:
+            if frn.launch_shape(R, k, T, H, EPI[epi], ep=epi.startswith("ep-"))[1] != vec:
                 continue  # does not fit this call
             times[vec] = graph_us(call, calls)
         frn.set_launch_table(None)
