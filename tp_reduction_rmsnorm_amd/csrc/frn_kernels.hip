@@ -51,6 +51,17 @@ __device__ __forceinline__ uint4 ld_stream(const uint4* p) {
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// The same load from a pointer rebuilt from integers (the expert-parallel
+// work list reads row addresses out of lanes): the compiler cannot tell that
+// such a pointer is global, so say so, or it emits flat loads -- which also
+// count against the scalar-load counter and so serialise with s_load waits.
+typedef __attribute__((address_space(1))) const u32x4_t global_u32x4_t;
+
+__device__ __forceinline__ uint4 ld_stream_global(const uint4* p) {
+    const u32x4_t v = __builtin_nontemporal_load((global_u32x4_t*)(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 __device__ __forceinline__ void st_stream(uint4* p, const uint4& q) {
     const u32x4_t v = {q.x, q.y, q.z, q.w};
     __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(p));
@@ -411,7 +422,7 @@ __device__ __forceinline__ void finalize_reduce(const RowArgs& a, int64_t t, con
 #pragma unroll
                     for (int j = 0; j < V; ++j) {
                         e[c][j] = nan8;
-                        if (E != nullptr && L.ok[j]) e[c][j] = ld_stream(E + L.vi[j]);
+                        if (E != nullptr && L.ok[j]) e[c][j] = ld_stream_global(E + L.vi[j]);
                     }
                 }
             }
