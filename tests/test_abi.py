@@ -434,17 +434,17 @@ import sys
 sys.path.insert(0, {root!r})
 import tp_reduction_rmsnorm_amd as frn
 print(frn.launch_shape(4, 0, 4096, 5120, frn.EPI_SANDWICH))
-"""
+"""  # built-in rule: (320, 2)
 
 
 def test_launch_table_from_environment(tmp_path):
     table = tmp_path / "table.txt"
-    table.write_text("5120 4 0 sandwich 0 * 4\n")
+    table.write_text("5120 4 0 sandwich 0 * 1\n")
     env = dict(os.environ, FRN_LAUNCH_TABLE=str(table))
     r = subprocess.run([sys.executable, "-c", ENV_TABLE_SCRIPT.format(root=ROOT)], env=env,
                        capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stderr
-    assert r.stdout.strip() == "(192, 4)"
+    assert r.stdout.strip() == "(640, 1)"
     table.write_text("not a table\n")
     r = subprocess.run([sys.executable, "-c", ENV_TABLE_SCRIPT.format(root=ROOT)], env=env,
                        capture_output=True, text=True, timeout=300)

@@ -210,3 +210,52 @@ def test_ep_full_size_sampled_rows(T):
     parity.compare(f"ep full T={T} residual_out (rows sampled)",
                    workloads.bits(x.index_select(0, ri)), ref.xout)
     assert torch.isfinite(y.float()).all() and torch.isfinite(x.float()).all()
+
+
+@pytest.mark.parametrize("T,workspace", [(24, "auto"), (300, None)])
+def test_ep_graph_capture_and_replay_with_new_data(T, workspace):
+    """Capture the expert-parallel call in a HIP graph and replay it with new
+    row values, weights, shared rows and residual copied in between (the
+    routing keeps its shape), checking every replay against the oracle."""
+    m = frn()
+    log(f"ep graph T={T} workspace={workspace}")
+    host = workloads.make_ep(8, T, 2048, k=6, experts=32, epilogue="sandwich", shared_rank=2,
+                             seed=321 + T)
+    d = dev(host)
+    out = torch.empty(T, 2048, dtype=torch.bfloat16, device=DEV)
+    rout = torch.empty(T, 2048, dtype=torch.bfloat16, device=DEV)
+
+    def call():
+        m.ep_moe_finalize_reduce_norm(d.expert_rows, d.topk_w, d.ep_rows, d.residual, d.gamma1,
+                                      d.gamma2, d.eps, shared=d.shared, epilogue=m.EPI_SANDWICH,
+                                      out=out, residual_out=rout, workspace=workspace)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    gen = torch.Generator().manual_seed(999 + T)
+    rnd = lambda t: torch.randn(t.shape, generator=gen).to(t.dtype)
+    for rep in range(4):
+        for r in range(8):
+            if host.expert_rows[r].numel():
+                host.expert_rows[r] = rnd(host.expert_rows[r])
+                d.expert_rows[r].copy_(host.expert_rows[r].to(DEV))
+        host.shared[2] = rnd(host.shared[2])
+        d.shared[2].copy_(host.shared[2].to(DEV))
+        host.topk_w = torch.softmax(torch.randn(host.topk_w.shape, generator=gen), -1)
+        d.topk_w.copy_(host.topk_w.to(DEV))
+        host.residual = rnd(host.residual)
+        d.residual.copy_(host.residual.to(DEV))
+        torch.sum(d.residual.float()).item()   # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref = oracle_ep(host)
+        parity.compare(f"ep graph T={T} replay {rep} out", workloads.bits(out), ref.y)
+        parity.compare(f"ep graph T={T} replay {rep} residual_out", workloads.bits(rout), ref.xout)

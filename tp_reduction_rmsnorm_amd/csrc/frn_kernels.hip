@@ -5,9 +5,10 @@
 // row_kernel: one token row per workgroup.  Each lane owns V 16-byte vectors
 // of the row (8 BF16 values each), placed `threads` vectors apart so every
 // wave instruction touches 64 consecutive vectors (1 KiB) of a row.  A lane
-// issues all loads of a rank chunk (or of a top-k chunk) before it consumes
-// any of them, keeps the FP32 row slice in registers through the epilogue,
-// and writes each output exactly once.
+// issues all loads of a chunk -- of ranks, of one rank's top-k slots, or
+// (expert-parallel routing) of the token's live rows across ranks -- before
+// it consumes any of them, keeps the FP32 row slice in registers through the
+// epilogue, and writes each output exactly once.
 //
 // finalize_slices_kernel: for the MoE finalize at small T, where one
 // workgroup per token would walk the R ranks one memory round trip after
@@ -28,7 +29,8 @@
 // per-rank BF16 rounding of the finalize; "Details": no FMA contraction --
 // this file is built with -ffp-contract=off):
 //   finalize   acc = 0; acc = acc + w_j * e_j for j ascending; acc = acc + shared;
-//              P_r = bf16(acc)
+//              P_r = bf16(acc)  (expert-parallel routing: j over rank r's own
+//              slots, shared only where rank r holds a shared-expert row)
 //   reduce     s = P_0; s = s + P_r for r ascending
 //   rinv(x)    ms = (float)(sum x^2 (FP64) / H); v = ms + eps; rinv = 1 / sqrt(v)
 //   rmsnorm    h = s + x; y = (h * rinv(h)) * gamma

@@ -144,9 +144,10 @@ void load_env_table_locked() {
 //    (H=5120 T=1: 4.0 us with one vector, 4.4 with two);
 //  - larger T without finalize: four vectors per lane for rows of 512+
 //    vectors up to T = 1024, and for rows of 768+ vectors (H >= 6144) up to
-//    T = 4096 -- fewer waves per row to synchronise (H=5120 T=1024: 15.4 ->
-//    14.7 us; H=8192 T=512: 18.8 -> 17.7 us, T=4096: 119.2 -> 117.4 us);
-//    beyond that two vectors for rows over 512 vectors;
+//    T = 4096 -- fewer waves per row to synchronise (H=5120 T=1024: 15.3 ->
+//    14.7 us; H=8192 T=512: 18.8 -> 17.7 us, T=4096: 119.6 -> 118.3 us);
+//    beyond that two vectors for rows over 512 vectors (H=5120 at T=2048
+//    and 4096: two vectors 29.1 and 51.9 us, four 29.5 and 52.0 us);
 //  - with finalize, one vector per lane up to 1024 lanes, except two for
 //    256 < T <= 2048 outside split pass 1 (H=7168 R=2 k=8: T=512 30.0 ->
 //    27.4 us, T=1024 57.4 -> 53.4 us; at T=4096 one vector is ahead again);
