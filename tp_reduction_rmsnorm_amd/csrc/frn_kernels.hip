@@ -378,13 +378,77 @@ __device__ __forceinline__ void add_partial(int r, float (&acc)[V][8], float (&s
     }
 }
 
+// Up to C live pairs of one token, loaded and waiting to be consumed.
+template <int C, int V>
+struct Chunk {
+    uint4 e[C][V];
+    float w[C];
+    int rank[C];
+    bool slot[C], has[C];
+};
+
+// Issue the loads of the next (up to) C live pairs of word `pw`, taking them
+// off the mask m in pair order.
+template <int C, int V>
+__device__ __forceinline__ void gather(const PairWord& pw, uint64_t& m, const Lanes<V>& L,
+                                       Chunk<C, V>& ch) {
+    const uint4 nan8 = make_uint4(0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u);
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        ch.has[c] = m != 0;
+        ch.slot[c] = false;
+        ch.w[c] = 0.0f;
+        ch.rank[c] = 0;
+        if (ch.has[c]) {
+            const int bit = __builtin_ctzll(m);
+            m &= m - 1;
+            const int meta = __builtin_amdgcn_readlane(pw.meta, bit);
+            const uintptr_t addr = pw.row == nullptr ? 0 : (uintptr_t)pw.row;
+            const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)addr, bit);
+            const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(addr >> 32), bit);
+            const uint4* E = (const uint4*)(((uint64_t)hi << 32) | lo);
+            ch.rank[c] = meta & (kSharedPair - 1);
+            ch.slot[c] = (meta & kSharedPair) == 0;
+            ch.w[c] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pw.w), bit));
+#pragma unroll
+            for (int j = 0; j < V; ++j) {
+                ch.e[c][j] = nan8;
+                if (E != nullptr && L.ok[j]) ch.e[c][j] = ld_stream_global(E + L.vi[j]);
+            }
+        }
+    }
+}
+
+// Consume a chunk in pair order: close (round and add) every rank before the
+// pair's rank, then add the pair into the open rank's accumulator.
+template <int C, int V>
+__device__ __forceinline__ void consume(const Chunk<C, V>& ch, int& cur, float (&acc)[V][8],
+                                        float (&s)[V][8]) {
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        if (!ch.has[c]) continue;
+        while (cur < ch.rank[c]) add_partial<V>(cur++, acc, s);
+#pragma unroll
+        for (int j = 0; j < V; ++j) {
+            float f[8];
+            widen(ch.e[c][j], f);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                if (ch.slot[c]) {
+                    const float prod = ch.w[c] * f[i];
+                    acc[j][i] = acc[j][i] + prod;
+                } else {
+                    acc[j][i] = acc[j][i] + f[i];
+                }
+            }
+        }
+    }
+}
+
 template <int V, int C>
 __device__ __forceinline__ void finalize_reduce(const RowArgs& a, int64_t t, const Lanes<V>& L,
                                                 float (&s)[V][8]) {
-    const uint4 nan8 = make_uint4(0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u);
-    const int k = a.k;
-    const int k1 = k + 1;
-    const int words = (a.R * k1 + 63) >> 6;
+    const int words = (a.R * (a.k + 1) + 63) >> 6;
     float acc[V][8];
 #pragma unroll
     for (int j = 0; j < V; ++j)
@@ -400,53 +464,9 @@ __device__ __forceinline__ void finalize_reduce(const RowArgs& a, int64_t t, con
         if (word + 1 < words) next = pair_word(a, t, word + 1);
         uint64_t m = pw.live;
         while (m != 0) {
-            uint4 e[C][V];
-            float wc[C];
-            int rc[C];
-            bool slot[C], has[C];
-#pragma unroll
-            for (int c = 0; c < C; ++c) {
-                has[c] = m != 0;
-                slot[c] = false;
-                wc[c] = 0.0f;
-                rc[c] = 0;
-                if (has[c]) {
-                    const int bit = __builtin_ctzll(m);
-                    m &= m - 1;
-                    const int meta = __builtin_amdgcn_readlane(pw.meta, bit);
-                    const uintptr_t addr = pw.row == nullptr ? 0 : (uintptr_t)pw.row;
-                    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)addr, bit);
-                    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(addr >> 32), bit);
-                    const uint4* E = (const uint4*)(((uint64_t)hi << 32) | lo);
-                    rc[c] = meta & (kSharedPair - 1);
-                    slot[c] = (meta & kSharedPair) == 0;
-                    wc[c] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pw.w), bit));
-#pragma unroll
-                    for (int j = 0; j < V; ++j) {
-                        e[c][j] = nan8;
-                        if (E != nullptr && L.ok[j]) e[c][j] = ld_stream_global(E + L.vi[j]);
-                    }
-                }
-            }
-#pragma unroll
-            for (int c = 0; c < C; ++c) {
-                if (!has[c]) continue;
-                while (cur < rc[c]) add_partial<V>(cur++, acc, s);
-#pragma unroll
-                for (int j = 0; j < V; ++j) {
-                    float f[8];
-                    widen(e[c][j], f);
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        if (slot[c]) {
-                            const float prod = wc[c] * f[i];
-                            acc[j][i] = acc[j][i] + prod;
-                        } else {
-                            acc[j][i] = acc[j][i] + f[i];
-                        }
-                    }
-                }
-            }
+            Chunk<C, V> ch;
+            gather<C, V>(pw, m, L, ch);
+            consume<C, V>(ch, cur, acc, s);
         }
     }
     while (cur < a.R) add_partial<V>(cur++, acc, s);
@@ -458,7 +478,8 @@ __device__ __forceinline__ void finalize_reduce(const RowArgs& a, int64_t t, con
 template <int EPI, int V>
 __device__ __forceinline__ void epilogue(const RowArgs& a, int64_t row, const Lanes<V>& L,
                                          float (&s)[V][8], const uint4 (&xr)[V],
-                                         double (&slots)[2][16]) {
+                                         double (&slots)[2][16], const float4* gamma1,
+                                         const float4* gamma2) {
     if constexpr (EPI == kStoreSum) {
 #pragma unroll
         for (int j = 0; j < V; ++j)
@@ -474,7 +495,7 @@ __device__ __forceinline__ void epilogue(const RowArgs& a, int64_t row, const La
                 float g[8], x[8];
 #pragma unroll
                 for (int i = 0; i < 8; ++i) g[i] = 0.0f;
-                if (L.ok[j]) load_gamma(a.gamma1, L.vi[j], g);
+                if (L.ok[j]) load_gamma(gamma1, L.vi[j], g);
                 widen(xr[j], x);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
@@ -497,7 +518,7 @@ __device__ __forceinline__ void epilogue(const RowArgs& a, int64_t row, const La
             if (L.ok[j]) st_stream(a.residual_out + row + L.vi[j], narrow(s[j]));
 
         const float r2 = inv_rms(block_sum(sum_squares<V>(s, L), slots[1]), H, eps);
-        const float4* g2 = (EPI == kSandwich) ? a.gamma2 : a.gamma1;
+        const float4* g2 = (EPI == kSandwich) ? gamma2 : gamma1;
 #pragma unroll
         for (int j = 0; j < V; ++j) {
             if (!L.ok[j]) continue;
@@ -553,7 +574,7 @@ __global__ __launch_bounds__(1024) void row_kernel(const RowArgs a) {
             add_partial<V>(r, acc, s);
         }
     }
-    epilogue<EPI, V>(a, row, L, s, xr, slots);
+    epilogue<EPI, V>(a, row, L, s, xr, slots, a.gamma1, a.gamma2);
 }
 
 // Per-rank MoE finalize of T rows, one row slice of one rank per workgroup:
