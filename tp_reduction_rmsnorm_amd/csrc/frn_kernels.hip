@@ -231,7 +231,7 @@ __device__ __forceinline__ void reduce_ranks(RankRow rank_row, int R, const Lane
 // dereferenced; its slot reads as NaN -- except that with expert-parallel
 // routing (a.ep) a negative index marks a slot of another rank's expert,
 // which takes no part in this rank's sum.
-template <int V, int C>
+template <int V, int C, bool EARLY_SHARED>
 __device__ __forceinline__ void finalize_rank(const RowArgs& a, int r, int64_t t,
                                               const Lanes<V>& L, float (&acc)[V][8]) {
     const int k = a.k;
@@ -241,6 +241,16 @@ __device__ __forceinline__ void finalize_rank(const RowArgs& a, int r, int64_t t
     const uint4 nan8 = make_uint4(0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u);
     const uint4* E = a.src[r];
     const int nvec = a.nvec;
+    // EARLY_SHARED: the shared row is loaded with the first chunk of slots
+    // (it is added last, but waiting for it separately costs a memory round
+    // trip); otherwise after the slots (four fewer VGPRs per vector).
+    const uint4* S = a.shared[r];
+    uint4 sh[V];
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+        sh[j] = make_uint4(0, 0, 0, 0);
+        if (EARLY_SHARED && S != nullptr && L.ok[j]) sh[j] = ld_stream(S + t * nvec + L.vi[j]);
+    }
 #pragma unroll
     for (int j = 0; j < V; ++j)
 #pragma unroll
@@ -282,15 +292,12 @@ __device__ __forceinline__ void finalize_rank(const RowArgs& a, int r, int64_t t
             }
         }
     }
-    const uint4* S = a.shared[r];
     if (S != nullptr) {
-        S += t * nvec;
 #pragma unroll
         for (int j = 0; j < V; ++j) {
-            uint4 q = make_uint4(0, 0, 0, 0);
-            if (L.ok[j]) q = ld_stream(S + L.vi[j]);
+            if (!EARLY_SHARED && L.ok[j]) sh[j] = ld_stream(S + t * nvec + L.vi[j]);
             float f[8];
-            widen(q, f);
+            widen(sh[j], f);
 #pragma unroll
             for (int i = 0; i < 8; ++i) acc[j][i] = acc[j][i] + f[i];
         }
@@ -569,7 +576,7 @@ __global__ __launch_bounds__(1024) void row_kernel(const RowArgs a) {
     } else {
         for (int r = 0; r < a.R; ++r) {
             float acc[V][8];
-            finalize_rank<V, C>(a, r, t, L, acc);
+            finalize_rank<V, C, true>(a, r, t, L, acc);
             // The rank's finalized partial is a BF16 tensor: round, then sum.
             add_partial<V>(r, acc, s);
         }
@@ -580,6 +587,7 @@ __global__ __launch_bounds__(1024) void row_kernel(const RowArgs a) {
 // Per-rank MoE finalize of T rows, one row slice of one rank per workgroup:
 // workgroup (t, r, c) writes bf16(finalize) of vectors [c * kSplitThreads,
 // (c + 1) * kSplitThreads) of rank r, token t to row t of part_out[r].
+template <bool EARLY_SHARED>
 __global__ __launch_bounds__(kSplitThreads) void finalize_slices_kernel(const RowArgs a, int S) {
     const int c = blockIdx.x % S;
     const int r = (blockIdx.x / S) % a.R;
@@ -588,7 +596,7 @@ __global__ __launch_bounds__(kSplitThreads) void finalize_slices_kernel(const Ro
     L.vi[0] = c * kSplitThreads + threadIdx.x;
     L.ok[0] = L.vi[0] < a.nvec;
     float acc[1][8];
-    finalize_rank<1, 16>(a, r, t, L, acc);
+    finalize_rank<1, 16, EARLY_SHARED>(a, r, t, L, acc);
     if (L.ok[0]) a.part_out[r][t * a.nvec + L.vi[0]] = narrow(acc[0]);
 }
 
@@ -640,8 +648,14 @@ int split_slices(int nvec) { return (nvec + kSplitThreads - 1) / kSplitThreads; 
 
 hipError_t launch_finalize(const RowArgs& a, int64_t T, hipStream_t stream) {
     const int S = split_slices(a.nvec);
-    hipLaunchKernelGGL(finalize_slices_kernel, dim3((unsigned)(T * a.R * S)), dim3(kSplitThreads),
-                       0, stream, a, S);
+    // Under expert-parallel routing most ranks hold no shared row, and the
+    // registers of an early shared load would cost occupancy for nothing.
+    if (a.ep)
+        hipLaunchKernelGGL(finalize_slices_kernel<false>, dim3((unsigned)(T * a.R * S)),
+                           dim3(kSplitThreads), 0, stream, a, S);
+    else
+        hipLaunchKernelGGL(finalize_slices_kernel<true>, dim3((unsigned)(T * a.R * S)),
+                           dim3(kSplitThreads), 0, stream, a, S);
     return hipGetLastError();
 }
 
