@@ -260,6 +260,17 @@ def _ordered(bits):
     return np.where(b & 0x8000, -(b & 0x7FFF), b)
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(runner, seconds=10.0, single_seconds=5.0):
     """The CPU oracle, as it is, on a bounded sample of the timed workload:
     the first 256 token rows of its first input set, repeated for about
@@ -295,6 +306,7 @@ def cpu_baseline(runner, seconds=10.0, single_seconds=5.0):
     ulp = max(int(np.abs(_ordered(res.y) - _ordered(y_gpu)).max()),
               int(np.abs(_ordered(res.xout) - _ordered(x_gpu)).max()))
     return dict(value=round(byts * reps / el / 1e9, 3), unit="GB/s", cores=cores, kind="oracle",
+                cpu=cpu_model(),
                 sample=f"{rows} of {runner.T} token rows of {w.name} (R={w.R}, H={w.H}), "
                        f"{reps} repetitions in {el:.1f} s, {cores} threads; "
                        f"{el / reps * 1e6 / rows:.1f} us per row",
