@@ -28,7 +28,7 @@
  * - Every device pointer must be 16-byte aligned and H must be a multiple
  *   of 8 (one 128-bit vector holds 8 BF16 values); otherwise the call
  *   returns FRN_ERR_UNSUPPORTED.  1 <= R <= FRN_MAX_R, 1 <= k <= FRN_MAX_K,
- *   8 <= H <= FRN_MAX_H.
+ *   8 <= H <= FRN_MAX_H, 0 <= T <= FRN_MAX_T.
  * - stream is a hipStream_t passed as void*; NULL is the null stream.  Calls
  *   are asynchronous: they enqueue kernels and return.  They never
  *   synchronize, never read device memory from the host and never allocate,
@@ -65,6 +65,8 @@ extern "C" {
 #define FRN_MAX_R 16     /* partials (TP ranks) per call */
 #define FRN_MAX_K 16     /* top-k slots per token */
 #define FRN_MAX_H 16384  /* hidden size */
+#define FRN_MAX_T 4194303 /* token rows per call (a row's workgroup has up to
+                             1024 lanes, and a dispatch holds < 2^32 lanes) */
 
 typedef enum frn_status {
     FRN_OK = 0,

@@ -121,6 +121,7 @@ def call_rms(lib, R=2, T=4, H=64, eps=1e-6, parts=None, residual=None, gamma=Non
     (dict(H=0), INVALID),
     (dict(H=12), UNSUPPORTED),
     (dict(H=16392), UNSUPPORTED),
+    (dict(T=4194304), UNSUPPORTED),               # FRN_MAX_T + 1
     (dict(eps=float("nan")), INVALID),
     (dict(eps=-1e-6), INVALID),
     (dict(eps=float("inf")), INVALID),
@@ -170,6 +171,7 @@ def call_moe(lib, R=2, k=3, T=4, H=64, num_rows=12, epilogue=0, shared=True, w=N
 @pytest.mark.parametrize("kw,status", [
     (dict(k=0), INVALID),
     (dict(k=17), UNSUPPORTED),
+    (dict(T=4194304), UNSUPPORTED),
     (dict(num_rows=0), INVALID),
     (dict(epilogue=7), INVALID),
     (dict(w=0), INVALID),

@@ -65,8 +65,8 @@ frn_status check_sizes(int32_t R, int32_t k, int64_t T, int64_t H, int32_t epilo
         return fail(FRN_ERR_UNSUPPORTED, "H=%lld is not a multiple of 8", (long long)H);
     if (H < 8 || H > FRN_MAX_H)
         return fail(FRN_ERR_UNSUPPORTED, "H=%lld outside [8, %d]", (long long)H, FRN_MAX_H);
-    if (T > 0x7fffffffLL)
-        return fail(FRN_ERR_UNSUPPORTED, "T=%lld exceeds 2^31-1 rows", (long long)T);
+    if (T > FRN_MAX_T)
+        return fail(FRN_ERR_UNSUPPORTED, "T=%lld exceeds %d rows", (long long)T, FRN_MAX_T);
     return FRN_OK;
 }
 

@@ -588,10 +588,11 @@ __global__ __launch_bounds__(1024) void row_kernel(const RowArgs a) {
 // workgroup (t, r, c) writes bf16(finalize) of vectors [c * kSplitThreads,
 // (c + 1) * kSplitThreads) of rank r, token t to row t of part_out[r].
 template <bool EARLY_SHARED>
-__global__ __launch_bounds__(kSplitThreads) void finalize_slices_kernel(const RowArgs a, int S) {
+__global__ __launch_bounds__(kSplitThreads) void finalize_slices_kernel(const RowArgs a, int S,
+                                                                        int64_t t0) {
     const int c = blockIdx.x % S;
     const int r = (blockIdx.x / S) % a.R;
-    const int64_t t = blockIdx.x / (S * a.R);
+    const int64_t t = t0 + blockIdx.x / (S * a.R);
     Lanes<1> L(a.nvec);
     L.vi[0] = c * kSplitThreads + threadIdx.x;
     L.ok[0] = L.vi[0] < a.nvec;
@@ -648,17 +649,25 @@ int split_slices(int nvec) { return (nvec + kSplitThreads - 1) / kSplitThreads; 
 
 hipError_t launch_finalize(const RowArgs& a, int64_t T, hipStream_t stream) {
     const int S = split_slices(a.nvec);
-    // Under expert-parallel routing most ranks hold no shared row, and the
-    // registers of an early shared load would cost occupancy for nothing.
-    if (a.ep)
-        hipLaunchKernelGGL(finalize_slices_kernel<false>, dim3((unsigned)(T * a.R * S)),
-                           dim3(kSplitThreads), 0, stream, a, S);
-    else
-        hipLaunchKernelGGL(finalize_slices_kernel<true>, dim3((unsigned)(T * a.R * S)),
-                           dim3(kSplitThreads), 0, stream, a, S);
-    return hipGetLastError();
+    // A dispatch holds fewer than 2^32 lanes: launch large T in token ranges.
+    const int64_t per_token = (int64_t)a.R * S;
+    const int64_t max_groups = 0xffffffffLL / kSplitThreads;
+    const int64_t chunk = max_groups / per_token;
+    for (int64_t t0 = 0; t0 < T; t0 += chunk) {
+        const int64_t n = (T - t0 < chunk ? T - t0 : chunk) * per_token;
+        // Under expert-parallel routing most ranks hold no shared row, and the
+        // registers of an early shared load would cost occupancy for nothing.
+        if (a.ep)
+            hipLaunchKernelGGL(finalize_slices_kernel<false>, dim3((unsigned)n),
+                               dim3(kSplitThreads), 0, stream, a, S, t0);
+        else
+            hipLaunchKernelGGL(finalize_slices_kernel<true>, dim3((unsigned)n),
+                               dim3(kSplitThreads), 0, stream, a, S, t0);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
-
 
 hipError_t launch_rows(const RowArgs& a_in, int epilogue, int64_t T, hipStream_t stream) {
     RowArgs a = a_in;
