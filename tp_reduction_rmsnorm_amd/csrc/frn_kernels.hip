@@ -1,6 +1,7 @@
 // frn_kernels.hip -- gfx950 kernels of the fused reduce + norm boundary.
 //
-// Two kernels share the per-row building blocks below.
+// Two kernels (row_kernel and finalize_slices_kernel, each in several
+// instantiations) share the per-row building blocks below.
 //
 // row_kernel: one token row per workgroup.  Each lane owns V 16-byte vectors
 // of the row (8 BF16 values each), placed `threads` vectors apart so every
