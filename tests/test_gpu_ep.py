@@ -259,3 +259,23 @@ def test_ep_graph_capture_and_replay_with_new_data(T, workspace):
         ref = oracle_ep(host)
         parity.compare(f"ep graph T={T} replay {rep} out", workloads.bits(out), ref.y)
         parity.compare(f"ep graph T={T} replay {rep} residual_out", workloads.bits(rout), ref.xout)
+
+
+@pytest.mark.parametrize("vec", [1, 2])
+def test_ep_results_do_not_depend_on_launch_shape(vec):
+    """The expert-parallel kernel forced to one or two vectors per lane
+    through a launch table gives the same bits."""
+    m = frn()
+    inp = workloads.make_ep(4, 300, 2056, k=5, experts=16, epilogue="sandwich", shared_rank=3,
+                            seed=4242)
+    d = dev(inp)
+    try:
+        m.set_launch_table(f"* * * ep-* 0 * {vec}\n")
+        assert m.launch_shape(4, 5, 300, 2056, m.EPI_SANDWICH, ep=True)[1] == vec
+        y, x = gpu_ep(d, workspace=None)
+        torch.cuda.synchronize()
+    finally:
+        m.set_launch_table(None)
+    ref = oracle_ep(inp)
+    parity.compare(f"ep vec={vec} out", workloads.bits(y), ref.y, min_exact=1.0)
+    parity.compare(f"ep vec={vec} residual_out", workloads.bits(x), ref.xout, min_exact=1.0)
