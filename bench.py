@@ -24,7 +24,7 @@ Printed: ONE JSON line with the contract fields plus
     GPU, the practical streaming rate, as a second reference line.
 
 The GPU runs one process on one device; ``--gpus N`` with N > 1 exits with a
-message (this build runs on one GPU only).
+message (the library runs on one GPU only).
 """
 from __future__ import annotations
 
@@ -332,7 +332,7 @@ def main():
     ap.add_argument("--split", action="store_true", help="with --workload: the split path")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(use --gpus 1)", file=sys.stderr)
         sys.exit(2)
 

@@ -71,7 +71,7 @@ extern "C" {
 typedef enum frn_status {
     FRN_OK = 0,
     FRN_ERR_INVALID = 1,     /* malformed arguments (null pointer, R < 1, ...) */
-    FRN_ERR_UNSUPPORTED = 2, /* well-formed, but outside what this build serves */
+    FRN_ERR_UNSUPPORTED = 2, /* well-formed, but outside what the library serves */
     FRN_ERR_HIP = 3          /* the HIP launch failed */
 } frn_status;
 
