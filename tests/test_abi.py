@@ -464,3 +464,39 @@ def test_tuner_merges_rules():
     assert tune.rules_for(5120, 4, 0, "sandwich", rows) == [
         "5120 4 0 sandwich 0 8 1", "5120 4 0 sandwich 9 64 2",
         "5120 4 0 sandwich 65 1024 4", "5120 4 0 sandwich 1025 * 2"]
+
+
+def test_launch_table_is_thread_safe():
+    """Threads replacing the table while others ask for shapes: no crash, and
+    every answer is one of the shapes some table gives."""
+    import threading
+    import tp_reduction_rmsnorm_amd as frn
+    tables = ["5120 4 0 sandwich 0 * 1\n", "5120 4 0 sandwich 0 * 2\n", None]
+    allowed = {(640, 1), (320, 2)}
+    seen, errors = set(), []
+
+    def setter():
+        try:
+            for i in range(300):
+                frn.set_launch_table(tables[i % 3])
+        except Exception as e:  # pragma: no cover - reported below
+            errors.append(e)
+
+    def reader():
+        try:
+            for _ in range(300):
+                seen.add(frn.launch_shape(4, 0, 4096, 5120, frn.EPI_SANDWICH))
+        except Exception as e:  # pragma: no cover
+            errors.append(e)
+
+    th = [threading.Thread(target=setter) for _ in range(2)] + \
+         [threading.Thread(target=reader) for _ in range(4)]
+    try:
+        for t in th:
+            t.start()
+        for t in th:
+            t.join()
+    finally:
+        frn.set_launch_table(None)
+    assert not errors, errors
+    assert seen and seen <= allowed, seen

@@ -290,6 +290,32 @@ def test_side_stream():
     check("side stream", y, x, oracle_ref(inp))
 
 
+def test_concurrent_streams_with_their_own_workspaces():
+    """Finalize calls queued on two streams at once (T <= 256, so each uses
+    the split-row workspace the binding keeps per stream) and a plain call
+    on a third: every result matches the oracle."""
+    a = workloads.make_workload(4, 48, salt=3)
+    b = workloads.make_workload(4, 40, salt=4)
+    c = workloads.make_workload(2, 64, salt=5)
+    da, db, dc = to_dev(a), to_dev(b), to_dev(c)
+    streams = [torch.cuda.Stream() for _ in range(3)]
+    torch.cuda.synchronize()
+    outs = []
+    for _ in range(3):  # several rounds, so the streams' calls overlap
+        with torch.cuda.stream(streams[0]):
+            ya, xa = gpu_fused(da)
+        with torch.cuda.stream(streams[1]):
+            yb, xb = gpu_fused(db)
+        with torch.cuda.stream(streams[2]):
+            yc, xc = gpu_fused(dc)
+        outs.append(((ya, xa), (yb, xb), (yc, xc)))
+    torch.cuda.synchronize()
+    refs = (oracle_ref(a), oracle_ref(b), oracle_ref(c))
+    for rnd, trio in enumerate(outs):
+        for name, (y, x), ref in zip("abc", trio, refs):
+            check(f"concurrent streams round {rnd} call {name}", y, x, ref)
+
+
 def test_graph_capture_and_replay_with_new_data():
     """Capture the fused call in a HIP graph; replay it several times with
     new input data copied in between (eager work and synchronisation between
