@@ -40,6 +40,15 @@ def _val(b: np.ndarray) -> np.ndarray:
     return (b.astype(np.uint32) << 16).view(np.float32)
 
 
+def _max_abs(got: np.ndarray, want: np.ndarray) -> float:
+    """Largest |got - want| over elements finite on both sides (an infinity
+    on both sides is compared by its ulp distance, which is 0 or large)."""
+    g = _val(got).astype(np.float64)
+    w = _val(want).astype(np.float64)
+    ok = np.isfinite(g) & np.isfinite(w)
+    return float(np.max(np.abs(g[ok] - w[ok]))) if np.any(ok) else 0.0
+
+
 def compare(name: str, got: np.ndarray, want: np.ndarray, min_exact: float = 0.999) -> Dict:
     got = np.ascontiguousarray(got, dtype=np.uint16)
     want = np.ascontiguousarray(want, dtype=np.uint16)
@@ -56,8 +65,7 @@ def compare(name: str, got: np.ndarray, want: np.ndarray, min_exact: float = 0.9
         n_1ulp=int(np.count_nonzero(d == 1)),
         n_over=int(np.count_nonzero(d > 1)),
         nan_mismatch=nan_mismatch,
-        max_abs=float(np.max(np.abs(_val(got[fin]).astype(np.float64)
-                                    - _val(want[fin]).astype(np.float64)))) if d.size else 0.0,
+        max_abs=_max_abs(got[fin], want[fin]),
     )
     REPORT.append(stats)
     path = os.environ.get("FRN_PARITY_REPORT")

@@ -371,6 +371,21 @@ def test_zero_rows_give_zero_outputs():
     assert not torch.any(y.view(torch.int16) & 0x7FFF) and not torch.any(x.view(torch.int16) & 0x7FFF)
 
 
+def test_non_finite_inputs_follow_ieee_like_the_oracle():
+    """Inf and NaN in the inputs propagate as IEEE arithmetic dictates, the
+    same way on both sides: NaN positions and every finite value match."""
+    for epi in ("rmsnorm", "sandwich"):
+        inp = workloads.make(3, 6, 1024, epilogue=epi, sigma=0.5, seed=606)
+        inf, nan = torch.tensor(float("inf")), torch.tensor(float("nan"))
+        inp.partials[0][1, 7] = inf.to(torch.bfloat16)           # row 1: one +inf
+        inp.partials[1][2, 9] = nan.to(torch.bfloat16)           # row 2: one NaN
+        inp.partials[0][3, 0] = inf.to(torch.bfloat16)           # row 3: +inf - inf
+        inp.partials[2][3, 0] = (-inf).to(torch.bfloat16)
+        inp.residual[4, 5] = inf.to(torch.bfloat16)              # row 4: residual inf
+        y, x = gpu_fused(to_dev(inp))
+        check(f"non-finite {epi}", y, x, oracle_ref(inp))
+
+
 def test_zero_tokens():
     m = frn()
     p = torch.empty(0, 512, dtype=torch.bfloat16, device=DEV)
