@@ -148,6 +148,20 @@ def test_split_matches_oracle(case):
     parity.compare(f"pass1 {mid_id(case)}", workloads.bits(u), u_ref)
 
 
+def test_boundary_threshold_picks_fused_or_split():
+    """frn.boundary: at or below max_fused_tokens the fused result, above it
+    the split path's (each against its own oracle path)."""
+    m = frn()
+    for k in (0, 4):
+        inp = workloads.make(2, 40, 1024, epilogue="rmsnorm", k=k, shared=bool(k), seed=70 + k)
+        d = to_dev(inp)
+        kw = dict(topk_weights=d.topk_w, topk_rows=d.topk_idx, shared=d.shared) if k else {}
+        y, x = m.boundary(d.sources, d.residual, d.gamma1, None, d.eps, max_fused_tokens=40, **kw)
+        check(f"boundary k={k} fused", y, x, oracle_ref(inp))
+        y, x = m.boundary(d.sources, d.residual, d.gamma1, None, d.eps, max_fused_tokens=39, **kw)
+        check(f"boundary k={k} split", y, x, oracle_ref(inp, split=True))
+
+
 # ------------------------------------------------------ full sizes --- #
 
 def sample_rows(T, n=48, seed=0):

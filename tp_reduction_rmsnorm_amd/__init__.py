@@ -21,6 +21,8 @@ Function names are the C entry points without their ``frn_`` prefix:
                                  some experts; per-rank row indices)
 * ``query``, ``workspace_bytes``, ``version``
 * ``set_launch_table``, ``launch_shape``  tuned launch shapes (tune.py)
+* ``boundary``                   fused or split by a token threshold (a
+                                 Python-side policy over the calls above)
 
 Every call returns its outputs.  A declined call raises
 ``FusedReduceNormUnsupported``; it never returns unreduced data.  (The pages
@@ -582,3 +584,35 @@ def split_reduce_norm(src: TensorList, residual: torch.Tensor, gamma1: torch.Ten
                     T, H, scratch.data_ptr(), out.data_ptr(), residual_out.data_ptr(),
                     _stream(stream, device)))
     return out, residual_out
+
+
+def boundary(src: TensorList, residual: torch.Tensor, gamma1: torch.Tensor,
+             gamma2: Optional[torch.Tensor] = None, eps: float = 1e-6, *,
+             topk_weights=None, topk_rows=None, shared=None, epilogue: int = EPI_RMSNORM,
+             max_fused_tokens: Optional[int] = None, out=None, residual_out=None,
+             stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """The layer boundary with a large-batch threshold, the analogue of the
+    pages' maximum fused batch size (SGLang PR #34134, first commit message:
+    a 16k-token prefill chunk is above it and takes another path).  Calls of
+    up to ``max_fused_tokens`` tokens (None: every call) run the fused
+    kernel; larger ones the split path (reduce -- with the finalize when
+    topk_weights are given -- to a BF16 tensor, then the boundary kernel),
+    which rounds the sum to BF16 once more.  Measured on MI355X the fused
+    kernel is the faster one at every size tried (split/fused 1.05 at
+    H=7168, T=4096 and 16384), hence the default.  src: partials, or the
+    expert-row buffers when topk_weights/topk_rows are given."""
+    T = (topk_weights.shape[0] if topk_weights is not None
+         else _as_list(src, "src")[0].shape[0])
+    if max_fused_tokens is not None and T > max_fused_tokens:
+        return split_reduce_norm(src, residual, gamma1, gamma2, eps, topk_weights=topk_weights,
+                                 topk_rows=topk_rows, shared=shared, epilogue=epilogue,
+                                 out=out, residual_out=residual_out, stream=stream)
+    if topk_weights is not None:
+        return moe_finalize_reduce_norm(src, topk_weights, topk_rows, residual, gamma1, gamma2,
+                                        eps, shared=shared, epilogue=epilogue, out=out,
+                                        residual_out=residual_out, stream=stream)
+    if epilogue == EPI_SANDWICH:
+        return reduce_sandwich_norm(src, residual, gamma1, gamma2, eps, out=out,
+                                    residual_out=residual_out, stream=stream)
+    return reduce_residual_rmsnorm(src, residual, gamma1, eps, out=out,
+                                   residual_out=residual_out, stream=stream)
