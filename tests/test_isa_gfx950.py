@@ -21,21 +21,32 @@ LIB = os.path.join(ROOT, "tp_reduction_rmsnorm_amd", "libfused_reduce_norm.so")
 LLVM = "/opt/rocm/llvm/bin"
 
 
-@pytest.fixture(scope="module")
-def mnemonics(tmp_path_factory):
+_DIS = {}
+
+
+def _disassembly():
+    """llvm-objdump of the library's gfx950 code object (cached)."""
+    if "text" in _DIS:
+        return _DIS["text"]
     if not os.path.exists(LIB):
         import __graft_entry__
         __graft_entry__.hip_build_module().build()
-    d = tmp_path_factory.mktemp("isa")
-    fatbin, co = str(d / "fatbin.bin"), str(d / "gfx950.co")
-    subprocess.run([f"{LLVM}/llvm-objcopy", f"--dump-section=.hip_fatbin={fatbin}", LIB,
-                    str(d / "copy.so")], check=True)
-    subprocess.run([f"{LLVM}/clang-offload-bundler", "--unbundle", "--type=o",
-                    f"--input={fatbin}", "--targets=hipv4-amdgcn-amd-amdhsa--gfx950",
-                    f"--output={co}"], check=True)
-    dis = subprocess.run([f"{LLVM}/llvm-objdump", "-d", "--mcpu=gfx950", co],
-                         capture_output=True, text=True, check=True).stdout
-    ops = [m.group(1) for m in re.finditer(r"^\s+([a-z_0-9]+)\b", dis, re.M)]
+    import tempfile
+    with tempfile.TemporaryDirectory() as d:
+        fatbin, co = os.path.join(d, "fatbin.bin"), os.path.join(d, "gfx950.co")
+        subprocess.run([f"{LLVM}/llvm-objcopy", f"--dump-section=.hip_fatbin={fatbin}", LIB,
+                        os.path.join(d, "copy.so")], check=True)
+        subprocess.run([f"{LLVM}/clang-offload-bundler", "--unbundle", "--type=o",
+                        f"--input={fatbin}", "--targets=hipv4-amdgcn-amd-amdhsa--gfx950",
+                        f"--output={co}"], check=True)
+        _DIS["text"] = subprocess.run([f"{LLVM}/llvm-objdump", "-d", "--mcpu=gfx950", co],
+                                      capture_output=True, text=True, check=True).stdout
+    return _DIS["text"]
+
+
+@pytest.fixture(scope="module")
+def mnemonics():
+    ops = [m.group(1) for m in re.finditer(r"^\s+([a-z_0-9]+)\b", _disassembly(), re.M)]
     assert len(ops) > 1000, "disassembly looks empty"
     return ops
 
@@ -60,3 +71,19 @@ def test_no_scratch_spills(mnemonics):
 
 def test_bf16_narrowing_uses_hardware_rne(mnemonics):
     assert "v_cvt_pk_bf16_f32" in set(mnemonics)
+
+
+def test_no_flat_memory_instructions(mnemonics):
+    """Every memory access names its address space (global or LDS): a flat
+    access would also count against the scalar-load counter, so waiting for
+    a scalar load would wait for it too (the expert-parallel work list
+    rebuilds row addresses from lanes and must cast them back to global)."""
+    bad = sorted({op for op in mnemonics if op.startswith(("flat_load", "flat_store"))})
+    assert not bad, f"flat memory instructions: {bad}"
+
+
+def test_streamed_rows_use_non_temporal_accesses():
+    """The streamed tensors are loaded and stored non-temporally (nt bit)."""
+    dis = _disassembly()
+    assert re.search(r"global_load_dwordx4 .* nt\b", dis), "no non-temporal row loads"
+    assert re.search(r"global_store_dwordx4 .* nt\b", dis), "no non-temporal row stores"
