@@ -500,3 +500,25 @@ def test_launch_table_is_thread_safe():
         frn.set_launch_table(None)
     assert not errors, errors
     assert seen and seen <= allowed, seen
+
+
+def test_builtin_launch_shapes_always_fit():
+    """Over every H, R, k, epilogue and a spread of T: at most 1024 lanes, a
+    multiple of 64, enough lanes for the row, and four vectors never with a
+    finalize or in split pass 1."""
+    import tp_reduction_rmsnorm_amd as frn
+    frn.set_launch_table(None)
+    for H in list(range(8, 16385, 8 * 97)) + [8, 512, 5120, 6144, 7168, 8192, 16384]:
+        nvec = H // 8
+        for R in (1, 2, 8, 16):
+            for k in (0, 1, 10, 16):
+                for epi in (frn.EPI_RMSNORM, frn.EPI_SANDWICH, frn.EPI_SUM):
+                    for ep in ((False, True) if k and epi != frn.EPI_SUM else (False,)):
+                        for T in (1, 8, 256, 257, 1024, 1025, 2048, 4096, 4097, 16384):
+                            th, v = frn.launch_shape(R, k, T, H, epi, ep=ep)
+                            assert th % 64 == 0 and 64 <= th <= 1024, (H, R, k, epi, T, th)
+                            assert th * v >= nvec, (H, R, k, epi, T, th, v)
+                            assert th - 64 < -(-nvec // v), (H, R, k, epi, T, th, v)
+                            assert v in (1, 2, 4)
+                            if k or epi == frn.EPI_SUM:
+                                assert v != 4, (H, R, k, epi, T)
