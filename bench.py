@@ -58,6 +58,74 @@ def hip_build_module():
     return mod
 
 
+PROBE_SRC = os.path.join(ROOT, "bench_probe.hip")
+PROBE_LIB = os.path.join(ROOT, "bench_probe.so")
+
+
+def build_probe() -> str:
+    """Compile bench_probe.hip (the access pattern alone) with the library's
+    code-generation flags."""
+    import subprocess
+    b = hip_build_module()
+    tmp = PROBE_LIB + f".tmp{os.getpid()}"
+    proc = subprocess.run([b.HIPCC, *b.CODEGEN_FLAGS, PROBE_SRC, "-o", tmp],
+                          capture_output=True, text=True)
+    if proc.returncode != 0:
+        raise RuntimeError(f"hipcc failed on bench_probe.hip:\n{proc.stderr}")
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
+
+
+def pattern_probe(dev, cid=2, Ts=(1024, 4096)):
+    """The headline workload's access pattern alone (bench_probe.hip: the
+    same rows read and written, the same lanes, no arithmetic, no row-wide
+    sums), graph-timed beside the fused call on the same rotating buffers."""
+    import ctypes
+    import torch
+    import tp_reduction_rmsnorm_amd as frn
+    if not os.path.exists(PROBE_LIB):
+        build_probe()
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.probe_rows.restype = ctypes.c_int
+    lib.probe_rows.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+                               ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+    rows = []
+    for T in Ts:
+        r = Runner(cid, T, dev, cold=True)
+        w = r.w
+        vec = frn.launch_shape(w.R, 0, T, w.H, r.epi)[1]
+        arrays = []
+        for d, (o, ro) in zip(r.sets, r.outs):
+            srcs = (ctypes.c_void_p * (w.R + 1))(*[p.data_ptr() for p in d.partials],
+                                                  d.residual.data_ptr())
+            dsts = (ctypes.c_void_p * 2)(o.data_ptr(), ro.data_ptr())
+            arrays.append((srcs, dsts))
+
+        def probe(i, arrays=arrays, T=T, H=w.H, nsrc=w.R + 1, vec=vec):
+            srcs, dsts = arrays[i % len(arrays)]
+            st = lib.probe_rows(ctypes.cast(srcs, ctypes.c_void_p), nsrc,
+                                ctypes.cast(dsts, ctypes.c_void_p), 2, T, H, vec,
+                                torch.cuda.current_stream().cuda_stream)
+            if st != 0:
+                raise RuntimeError(f"probe_rows failed ({st})")
+
+        kernel_us = r.graph_us()
+        call = r.call
+        r.call = probe
+        probe_us = r.graph_us()
+        r.call = call
+        pattern_bytes = T * w.H * 2 * (w.R + 3)
+        rows.append(dict(workload=w.name, T=T, vectors_per_lane=vec,
+                         kernel_us=round(kernel_us, 3), pattern_us=round(probe_us, 3),
+                         pattern_GBps=round(pattern_bytes / probe_us / 1e3, 1),
+                         pattern_frac_of_peak=round(pattern_bytes / probe_us / 1e3 / PEAK_GBS, 4),
+                         kernel_over_pattern=round(kernel_us / probe_us, 4)))
+        print(json.dumps(dict(pattern_probe=rows[-1])), file=sys.stderr, flush=True)
+        del r
+        torch.cuda.empty_cache()
+    return rows
+
+
 def kernel_source_digest() -> str:
     """SHA-256 over the kernel sources, the public header and the code
     generation flags: counter data taken for another version of the kernels
@@ -330,6 +398,8 @@ def main():
                          "profiling runs -- the contract line is the default)")
     ap.add_argument("--tokens", type=int, default=None, help="T for --workload")
     ap.add_argument("--split", action="store_true", help="with --workload: the split path")
+    ap.add_argument("--pattern-probe", action="store_true",
+                    help="also time the headline access pattern alone (bench_probe.hip)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the library has no multi-GPU path "
@@ -419,6 +489,8 @@ def main():
         out["sweep"] = sweep(dev)
     if args.all:
         out["other_configs"] = extra_configs(dev)
+    if args.pattern_probe:
+        out["pattern_probe"] = pattern_probe(dev)
     if "cpu_baseline" in out:  # keep the contract's key order readable
         out["cpu_baseline"] = out.pop("cpu_baseline")
     print(json.dumps(out), flush=True)
