@@ -328,42 +328,89 @@ struct PairWord {
     int32_t meta;       // lane l: its rank, plus kSharedPair for a shared-expert row
 };
 
+// A word of pairs whose indices and weights are still on their way.
+struct PairLoad {
+    int32_t row;   // lane l: its slot's row index (slots)
+    float w;       // lane l: its slot's weight (slots)
+    int32_t meta;  // lane l: rank, plus kSharedPair for a shared row; -1 past the last pair
+};
+
 constexpr int32_t kSharedPair = 256;
 
-// One word of token t's pairs (see finalize_reduce).  Each lane resolves its
-// pair's row address, so the loop that loads the rows only reads lanes.
-__device__ __forceinline__ PairWord pair_word(const RowArgs& a, int64_t t, int word) {
+// A kernel argument read as a wave-uniform value.  The per-rank arrays of
+// RowArgs are picked from per lane (pick below); reading each rank's entry
+// uniformly keeps those reads scalar loads of the kernel arguments, where the
+// compiler would otherwise fold the selection into a per-lane vector load --
+// a memory round trip in front of every index load.
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// arr[r] with r per lane (0 <= r < R); call in wave-uniform control flow.
+// Entries are read kPickBatch at a time (one scalar load of the batch).
+constexpr int kPickBatch = 4;
+static_assert(FRN_MAX_R % kPickBatch == 0, "pick reads whole batches");
+
+template <class P>
+__device__ __forceinline__ P pick(const P (&arr)[FRN_MAX_R], int R, int r) {
+    uint64_t out = 0;
+    for (int r0 = 0; r0 < R; r0 += kPickBatch) {
+#pragma unroll
+        for (int q = 0; q < kPickBatch; ++q) {
+            const uint64_t v = uniform_u64(__builtin_bit_cast(uint64_t, arr[r0 + q]));
+            out = r == r0 + q ? v : out;
+        }
+    }
+    return __builtin_bit_cast(P, out);
+}
+
+typedef __attribute__((address_space(1))) const int32_t global_i32_t;
+
+// Issue the index and weight loads of one word of token t's pairs (see
+// finalize_reduce); resolve_pairs turns them into a PairWord once they land.
+__device__ __forceinline__ PairLoad load_pairs(const RowArgs& a, int64_t t, int word) {
     const int k = a.k;
     const int k1 = k + 1;
     const int p = word * 64 + (int)(threadIdx.x & 63);
+    const int r = p / k1 < a.R ? p / k1 : a.R - 1;
+    const int j = p - r * k1;
+    const int32_t* rows = pick(a.topk_row, a.R, r);
+    PairLoad pl;
+    pl.row = 0;
+    pl.w = 0.0f;
+    pl.meta = -1;
+    if (p < a.R * k1) {
+        if (j < k) {
+            pl.row = *((global_i32_t*)rows + t * k + j);
+            pl.w = a.topk_w[t * k + j];
+            pl.meta = r;
+        } else {
+            pl.meta = r | kSharedPair;
+        }
+    }
+    return pl;
+}
+
+// Each lane resolves its pair's row address, so the loop that loads the rows
+// only reads lanes.
+__device__ __forceinline__ PairWord resolve_pairs(const RowArgs& a, int64_t t,
+                                                  const PairLoad& pl) {
+    const int r = pl.meta < 0 ? 0 : (pl.meta & (kSharedPair - 1));
+    const uint4* src = pick(a.src, a.R, r);
+    const uint4* shared = pick(a.shared, a.R, r);
+    const int64_t num_rows = pick(a.num_rows, a.R, r);
     bool live = false;
     PairWord pw;
     pw.row = nullptr;
-    pw.w = 0.0f;
-    pw.meta = 0;
-    if (p < a.R * k1) {
-        const int r = p / k1;
-        const int j = p - r * k1;
-        const int32_t* rows = nullptr;
-        const uint4* src = nullptr;
-        const uint4* shared = nullptr;
-        int64_t num_rows = 0;
-        for (int rr = 0; rr < a.R; ++rr) {
-            if (rr == r) {
-                rows = a.topk_row[rr];
-                src = a.src[rr];
-                shared = a.shared[rr];
-                num_rows = a.num_rows[rr];
-            }
-        }
-        if (j < k) {
-            const int32_t row = rows[t * k + j];
-            pw.w = a.topk_w[t * k + j];
-            pw.meta = r;
-            live = !a.ep || row >= 0;
-            if (row >= 0 && (int64_t)row < num_rows) pw.row = src + (int64_t)row * a.nvec;
+    pw.w = pl.w;
+    pw.meta = pl.meta;
+    if (pl.meta >= 0) {
+        if ((pl.meta & kSharedPair) == 0) {
+            live = !a.ep || pl.row >= 0;
+            if (pl.row >= 0 && (int64_t)pl.row < num_rows) pw.row = src + (int64_t)pl.row * a.nvec;
         } else {
-            pw.meta = r | kSharedPair;
             live = shared != nullptr;
             if (live) pw.row = shared + t * a.nvec;
         }
@@ -463,13 +510,16 @@ __device__ __forceinline__ void finalize_reduce(const RowArgs& a, int64_t t, con
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[j][i] = 0.0f;
     int cur = 0;  // rank whose accumulator is open
-    // The next word's indices and weights are loaded one word ahead, before
-    // this word's rows: loads complete in order, so by the time the next
-    // word is needed (every row load of this one consumed) they have arrived.
-    PairWord next = pair_word(a, t, 0);
+    // The indices and weights of the first two words go out together, and
+    // each later word's one word ahead of its use: the first row loads wait
+    // for one memory round trip, and loads complete in order, so a word's
+    // indices have landed by the time the previous word's rows are consumed.
+    PairLoad cur_load = load_pairs(a, t, 0);
+    PairLoad next_load = load_pairs(a, t, 1);  // no lane loads if there is one word
     for (int word = 0; word < words; ++word) {
-        const PairWord pw = next;
-        if (word + 1 < words) next = pair_word(a, t, word + 1);
+        const PairWord pw = resolve_pairs(a, t, cur_load);
+        cur_load = next_load;
+        if (word + 2 < words) next_load = load_pairs(a, t, word + 2);
         uint64_t m = pw.live;
         while (m != 0) {
             Chunk<C, V> ch;
