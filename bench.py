@@ -77,9 +77,12 @@ def build_probe() -> str:
 
 
 def pattern_probe(dev, cid=2, Ts=(1024, 4096)):
-    """The headline workload's access pattern alone (bench_probe.hip: the
-    same rows read and written, the same lanes, no arithmetic, no row-wide
-    sums), graph-timed beside the fused call on the same rotating buffers."""
+    """A workload's access pattern alone (bench_probe.hip: the same rows read
+    and written, the same lanes, no arithmetic, no row-wide sums), graph-timed
+    beside the fused call.  Reduction workloads: on the call's own rotating
+    buffers.  Expert-parallel workload: its k routed rows, the shared row and
+    the residual of each token read as k + 2 contiguous [T,H] streams of
+    their own (the same bytes without the gather, indices or weights)."""
     import ctypes
     import torch
     import tp_reduction_rmsnorm_amd as frn
@@ -93,15 +96,26 @@ def pattern_probe(dev, cid=2, Ts=(1024, 4096)):
     for T in Ts:
         r = Runner(cid, T, dev, cold=True)
         w = r.w
-        vec = frn.launch_shape(w.R, 0, T, w.H, r.epi)[1]
-        arrays = []
-        for d, (o, ro) in zip(r.sets, r.outs):
-            srcs = (ctypes.c_void_p * (w.R + 1))(*[p.data_ptr() for p in d.partials],
-                                                  d.residual.data_ptr())
-            dsts = (ctypes.c_void_p * 2)(o.data_ptr(), ro.data_ptr())
-            arrays.append((srcs, dsts))
+        arrays, keep = [], []
+        if w.ep:
+            nsrc = w.k + 2
+            vec = frn.launch_shape(w.R, w.k, T, w.H, r.epi, ep=True)[1]
+            for o, ro in r.outs:
+                bufs = [torch.empty(T, w.H, dtype=torch.bfloat16, device=dev) for _ in range(nsrc)]
+                keep.append(bufs)
+                arrays.append(((ctypes.c_void_p * nsrc)(*[b.data_ptr() for b in bufs]),
+                               (ctypes.c_void_p * 2)(o.data_ptr(), ro.data_ptr())))
+        else:
+            if w.k:
+                raise ValueError("the pattern probe covers reductions and the expert-parallel call")
+            nsrc = w.R + 1
+            vec = frn.launch_shape(w.R, 0, T, w.H, r.epi)[1]
+            for d, (o, ro) in zip(r.sets, r.outs):
+                srcs = (ctypes.c_void_p * nsrc)(*[p.data_ptr() for p in d.partials],
+                                                d.residual.data_ptr())
+                arrays.append((srcs, (ctypes.c_void_p * 2)(o.data_ptr(), ro.data_ptr())))
 
-        def probe(i, arrays=arrays, T=T, H=w.H, nsrc=w.R + 1, vec=vec):
+        def probe(i, arrays=arrays, T=T, H=w.H, nsrc=nsrc, vec=vec):
             srcs, dsts = arrays[i % len(arrays)]
             st = lib.probe_rows(ctypes.cast(srcs, ctypes.c_void_p), nsrc,
                                 ctypes.cast(dsts, ctypes.c_void_p), 2, T, H, vec,
@@ -114,14 +128,15 @@ def pattern_probe(dev, cid=2, Ts=(1024, 4096)):
         r.call = probe
         probe_us = r.graph_us()
         r.call = call
-        pattern_bytes = T * w.H * 2 * (w.R + 3)
-        rows.append(dict(workload=w.name, T=T, vectors_per_lane=vec,
-                         kernel_us=round(kernel_us, 3), pattern_us=round(probe_us, 3),
+        pattern_bytes = T * w.H * 2 * (nsrc + 2)
+        rows.append(dict(workload=w.name, T=T, vectors_per_lane=vec, rows_read=nsrc,
+                         kernel_us=round(kernel_us, 3), kernel_GBps=round(r.bytes / kernel_us / 1e3, 1),
+                         pattern_us=round(probe_us, 3),
                          pattern_GBps=round(pattern_bytes / probe_us / 1e3, 1),
                          pattern_frac_of_peak=round(pattern_bytes / probe_us / 1e3 / PEAK_GBS, 4),
                          kernel_over_pattern=round(kernel_us / probe_us, 4)))
         print(json.dumps(dict(pattern_probe=rows[-1])), file=sys.stderr, flush=True)
-        del r
+        del r, keep, arrays
         torch.cuda.empty_cache()
     return rows
 
@@ -399,7 +414,8 @@ def main():
     ap.add_argument("--tokens", type=int, default=None, help="T for --workload")
     ap.add_argument("--split", action="store_true", help="with --workload: the split path")
     ap.add_argument("--pattern-probe", action="store_true",
-                    help="also time the headline access pattern alone (bench_probe.hip)")
+                    help="also time the access pattern alone (bench_probe.hip): the "
+                         "headline workload at T=1024 and 4096, or --workload at its T")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the library has no multi-GPU path "
@@ -490,7 +506,8 @@ def main():
     if args.all:
         out["other_configs"] = extra_configs(dev)
     if args.pattern_probe:
-        out["pattern_probe"] = pattern_probe(dev)
+        out["pattern_probe"] = (pattern_probe(dev, cid, (T,)) if args.workload is not None
+                                else pattern_probe(dev))
     if "cpu_baseline" in out:  # keep the contract's key order readable
         out["cpu_baseline"] = out.pop("cpu_baseline")
     print(json.dumps(out), flush=True)
