@@ -273,11 +273,15 @@ frn_status frn_query(int32_t R, int32_t k, int64_t T, int64_t H, int32_t epilogu
  * H, R, k, Tmin, Tmax: integers or '*' (any); k = 0 means no finalize;
  * epilogue: rmsnorm | sandwich | sum (split pass 1) for calls without
  * expert-parallel routing, ep-rmsnorm | ep-sandwich | ep-* for
- * frn_ep_moe_finalize_reduce_norm, or * (every call); vec: 1 | 2 | 4.
- * The first rule that matches a call and fits it (at most 1024 lanes; vec 4
- * only without finalize and outside split pass 1) decides.  Results are
- * identical for every shape; only speed changes.  tp_reduction_rmsnorm_amd/
- * tune.py measures a table.  frn_set_launch_table(NULL) restores the
+ * frn_ep_moe_finalize_reduce_norm, or * (every call); vec: 1 | 2 | 4, or
+ * split | fused.  A numeric vec sets the one-row kernel's shape: the first
+ * such rule that matches a call and fits it (at most 1024 lanes; vec 4
+ * only without finalize and outside split pass 1) decides.  split / fused
+ * decide, for a finalize call (k >= 1) given a large enough workspace,
+ * whether it takes the split-row finalize (see frn_workspace_bytes) or the
+ * one-row kernel: the first such rule that matches decides, and T above 256
+ * is never split.  Results are identical for every choice; only speed
+ * changes.  tp_reduction_rmsnorm_amd/tune.py measures a table.  frn_set_launch_table(NULL) restores the
  * built-in rule; an unparsable text returns FRN_ERR_INVALID (the line is in
  * frn_last_error) and leaves the table as it was.  If no table was set
  * before the first launch, the file named by the environment variable
@@ -297,23 +301,38 @@ frn_status frn_launch_shape(int32_t R, int32_t k, int64_t T, int64_t H, int32_t 
 
 /*
  * Bytes of the optional workspace argument of the fused calls for calls of
- * up to max_T tokens (0: the call never uses one).  Today only the MoE
- * finalize (k > 0) uses it: for T <= 256 the finalize of each (token, rank,
+ * up to max_T tokens (0: no call of these sizes uses one).  Only the MoE
+ * finalize (k > 0) uses it, at small T: the finalize of each (token, rank,
  * 2048-column slice) then runs in a workgroup of its own and writes its
  * BF16 partial to the workspace, and a second kernel on the same stream
  * reduces the R partials and runs the epilogue.  This spreads a token's row
  * over many workgroups at small batch, the analogue of the pages' row
  * spread over several blocks (SGLang PR #34134, the publish-granularity
- * discussion).  Results are bit-identical with and without it (the
- * partials are the same BF16 values, summed in the same order).  Layout: R
- * x T x H BF16.  The caller allocates it (256-byte aligned); it needs no
- * initialisation and holds nothing between calls.  Calls that share one
- * workspace must not run concurrently.  A workspace that is NULL or smaller
- * than needed for a call is ignored (the call then uses the
- * one-row-per-workgroup kernel); one that is used must not overlap any
- * other argument (FRN_ERR_INVALID).
+ * discussion).  Which calls take it is frn_split_rows; the size returned
+ * covers both routings and every epilogue under the current launch table.
+ * Results are bit-identical with and without it (the partials are the same
+ * BF16 values, summed in the same order).  Layout: R x T x H BF16.  The
+ * caller allocates it (256-byte aligned); it needs no initialisation and
+ * holds nothing between calls.  Calls that share one workspace must not run
+ * concurrently.  A workspace that is NULL, smaller than needed for a call,
+ * or given to a call that does not take the split-row finalize is ignored
+ * (the call then uses the one-row-per-workgroup kernel); one that is used
+ * must not overlap any other argument (FRN_ERR_INVALID).
  */
 size_t frn_workspace_bytes(int64_t max_T, int64_t H, int32_t R, int32_t k);
+
+/*
+ * 1 if a finalize call of these sizes that is given a large enough
+ * workspace takes the split-row finalize, else 0 (also for k = 0 and for
+ * sizes outside what the library serves).  epilogue: FRN_EPI_RMSNORM or
+ * FRN_EPI_SANDWICH, OR'ed with FRN_SHAPE_EP for a call of
+ * frn_ep_moe_finalize_reduce_norm.  The split-row finalize writes and
+ * re-reads R partial rows per token, so it pays only while the one-row
+ * kernel is bound by its memory round trips: the built-in rule, measured on
+ * MI355X, takes it up to 8 to 192 tokens depending on R, H and the routing;
+ * launch-table split / fused rules override it.
+ */
+int32_t frn_split_rows(int32_t R, int32_t k, int64_t T, int64_t H, int32_t epilogue);
 
 /* Static text for a status code. */
 const char* frn_status_string(frn_status s);

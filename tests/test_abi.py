@@ -55,8 +55,8 @@ def lib():
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:const char\*|frn_status|size_t)\s+(frn_\w+)\(",
-                                 text, re.M)))
+    pattern = r"^\s*(?:const char\*|frn_status|size_t|int32_t)\s+(frn_\w+)\("
+    return sorted(set(re.findall(pattern, text, re.M)))
 
 
 def test_header_declares_the_boundary_calls():
@@ -87,6 +87,9 @@ def test_python_binding_names_match_the_c_entry_points():
     for name in frn.C_FUNCTIONS:
         if name not in ("frn_status_string", "frn_last_error"):
             assert hasattr(frn, name[len("frn_"):]), name
+    # every C entry point has its own ctypes handle (none rebound by another)
+    bound = sorted(getattr(frn, a).__name__ for a in dir(frn) if a.startswith("_c_"))
+    assert bound == sorted(frn.C_FUNCTIONS)
 
 
 def test_version_and_status_strings(lib):
@@ -267,10 +270,68 @@ def test_pass1_rejects(lib):
 
 def test_workspace_bytes(lib):
     assert lib.frn_workspace_bytes(8, 6144, 8, 10) == 8 * 8 * 6144 * 2
-    assert lib.frn_workspace_bytes(5000, 7168, 2, 8) == 256 * 2 * 7168 * 2
+    # covers the largest T either routing splits at: R=8 H=6144 -> 96 (TP)
+    assert lib.frn_workspace_bytes(5000, 6144, 8, 10) == 96 * 8 * 6144 * 2
+    assert lib.frn_workspace_bytes(5000, 7168, 2, 8) == 32 * 2 * 7168 * 2
+    assert lib.frn_workspace_bytes(5000, 4096, 2, 4) == 8 * 2 * 4096 * 2   # EP only
     assert lib.frn_workspace_bytes(64, 5120, 4, 0) == 0      # no finalize: none used
     assert lib.frn_workspace_bytes(64, 5124, 4, 2) == 0      # unsupported H
     assert lib.frn_workspace_bytes(0, 5120, 4, 2) == 0
+    assert lib.frn_workspace_bytes(8, 5120, 4, 17) == 0      # k beyond FRN_MAX_K
+
+
+def test_split_rows_builtin_rule():
+    """The built-in choice of the split-row finalize at its measured edges."""
+    import tp_reduction_rmsnorm_amd as frn
+    S, EP = frn.EPI_SANDWICH, True
+    frn.set_launch_table(None)
+    cases = [  # R, k, H, ep, T, expected
+        (8, 10, 6144, False, 1, True), (8, 10, 6144, False, 96, True),
+        (8, 10, 6144, False, 97, False), (8, 10, 6144, False, 256, False),
+        (2, 8, 7168, False, 32, True), (2, 8, 7168, False, 33, False),
+        (2, 4, 4096, False, 1, False), (4, 8, 2048, False, 192, True),
+        (4, 8, 2048, False, 193, False), (16, 8, 4096, False, 128, True),
+        (8, 10, 6144, EP, 16, True), (8, 10, 6144, EP, 17, False),
+        (2, 10, 6144, EP, 8, True), (2, 10, 6144, EP, 9, False),
+        (16, 8, 4096, EP, 48, True), (16, 8, 4096, EP, 49, False),
+        (8, 8, 2048, EP, 48, True),
+    ]
+    for R, k, H, ep, T, want in cases:
+        assert frn.split_rows(R, k, T, H, ep=ep) is want, (R, k, H, ep, T)
+        assert frn.split_rows(R, k, T, H, S, ep=ep) is want, (R, k, H, ep, T)
+    assert not frn.split_rows(8, 0, 8, 6144)                 # no finalize
+    assert not frn.split_rows(8, 10, 0, 6144)                # empty call
+    assert not frn.split_rows(8, 10, 8, 6148)                # unsupported H
+    assert not frn.split_rows(8, 10, 8, 6144, frn.EPI_SUM)   # split pass 1 has no workspace
+
+
+def test_launch_table_split_and_fused_rules(lib):
+    """split / fused rules override the built-in choice, leave the vec
+    rules alone, never split above 256 tokens, and widen the workspace size
+    to what they route to the split-row finalize."""
+    import tp_reduction_rmsnorm_amd as frn
+    try:
+        frn.set_launch_table(None)
+        base = frn.launch_shape(8, 10, 200, 6144, ep=True)
+        frn.set_launch_table("6144 8 10 ep-rmsnorm 0 200 split\n"
+                             "6144 8 10 rmsnorm 0 * fused\n"
+                             "* * * * 0 * split\n")
+        assert frn.split_rows(8, 10, 200, 6144, ep=True)
+        assert frn.split_rows(8, 10, 201, 6144, ep=True)                # the '*' split rule
+        assert not frn.split_rows(8, 10, 8, 6144)                       # fused rule first
+        assert frn.split_rows(8, 10, 8, 6144, frn.EPI_SANDWICH)         # sandwich: '*' rule
+        assert not frn.split_rows(8, 10, 257, 6144, ep=True)            # never above 256
+        assert frn.launch_shape(8, 10, 200, 6144, ep=True) == base      # vec rules untouched
+        assert lib.frn_workspace_bytes(5000, 6144, 8, 10) == 256 * 8 * 6144 * 2
+        frn.set_launch_table("6144 8 10 * 0 * fused\n")
+        assert not frn.split_rows(8, 10, 1, 6144)
+        assert not frn.split_rows(8, 10, 1, 6144, ep=True)
+        assert lib.frn_workspace_bytes(5000, 6144, 8, 10) == 96 * 8 * 6144 * 2  # built-in bound
+        for bad in ("6144 8 10 rmsnorm 0 * splits", "6144 8 10 rmsnorm 0 * 3"):
+            with pytest.raises(ValueError):
+                frn.set_launch_table(bad)
+    finally:
+        frn.set_launch_table(None)
 
 
 def test_misaligned_or_overlapping_workspace_rejected(lib):
@@ -281,9 +342,20 @@ def test_misaligned_or_overlapping_workspace_rejected(lib):
         return lib.frn_moe_finalize_reduce_norm(src, sh, 2, addr(5), addr(6), 3, 12, 0, addr(1),
                                                 addr(2), None, 1e-6, 4, 64, addr(3), addr(4),
                                                 ws, wsb, None)
-    assert moe(addr(40, 16), need) == UNSUPPORTED   # not 256-byte aligned
-    assert moe(addr(10), need) == INVALID           # overlaps expert rows of rank 0
-    assert moe(addr(3), need) == INVALID            # overlaps out
+    import tp_reduction_rmsnorm_amd as frn
+    lib.frn_set_launch_table.argtypes = [ctypes.c_char_p]
+    try:
+        # The built-in rule keeps R=2, H*k=192 on the one-row kernel, whose
+        # calls ignore the workspace (not called here: it would launch); a
+        # table routes it to the split-row finalize, which checks it.
+        assert not frn.split_rows(2, 3, 4, 64)
+        assert lib.frn_set_launch_table(b"* * * * 0 * split\n") == OK
+        assert frn.split_rows(2, 3, 4, 64)
+        assert moe(addr(40, 16), need) == UNSUPPORTED   # not 256-byte aligned
+        assert moe(addr(10), need) == INVALID           # overlaps expert rows of rank 0
+        assert moe(addr(3), need) == INVALID            # overlaps out
+    finally:
+        lib.frn_set_launch_table(None)
 
 
 def test_standalone_finalize_rejects(lib):
@@ -464,6 +536,16 @@ def test_tuner_merges_rules():
     assert tune.rules_for(5120, 4, 0, "sandwich", rows) == [
         "5120 4 0 sandwich 0 8 1", "5120 4 0 sandwich 9 64 2",
         "5120 4 0 sandwich 65 1024 4", "5120 4 0 sandwich 1025 * 2"]
+    split = [(1, "split", {}), (16, "split", {}), (32, "fused", {}), (256, "fused", {})]
+    lines = tune.rules_for(6144, 8, 10, "ep-rmsnorm", split, last="256")
+    assert lines == ["6144 8 10 ep-rmsnorm 0 16 split", "6144 8 10 ep-rmsnorm 17 256 fused"]
+    import tp_reduction_rmsnorm_amd as frn
+    try:
+        frn.set_launch_table("\n".join(lines))   # the tuner's output parses
+        assert frn.split_rows(8, 10, 16, 6144, ep=True)
+        assert not frn.split_rows(8, 10, 17, 6144, ep=True)
+    finally:
+        frn.set_launch_table(None)
 
 
 def test_launch_table_is_thread_safe():

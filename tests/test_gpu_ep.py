@@ -2,8 +2,9 @@
 owns a share of the experts, a negative row index marks another rank's slot)
 against the CPU oracle, through the C ABI (via the Python binding).
 
-Moderate sizes run whole batches through the oracle, across the split-row
-range (T <= 256 with the workspace) and the one-row kernel; the full-size
+Moderate sizes run whole batches through the oracle, through the split-row
+finalize (where the built-in rule takes it, and at every T <= 256 when a
+launch table forces it) and the one-row kernel; the full-size
 workload (H=6144, top-10 of 256 experts over 8 ranks, T=4096) runs in the
 launch configuration the benchmark times and the oracle recomputes sampled
 rows.
@@ -89,13 +90,25 @@ def cid(c):
 
 
 @pytest.mark.parametrize("case", CASES, ids=[cid(c) for c in CASES])
-@pytest.mark.parametrize("workspace", ["auto", None])
+@pytest.mark.parametrize("workspace", ["auto", None, "forced-split"])
 def test_ep_fused_matches_oracle(case, workspace):
+    """"auto": the built-in choice; None: the one-row kernel; "forced-split":
+    a launch table routes every T <= 256 to the split-row finalize."""
     R, T, H, e, k, E, s = case
+    m = frn()
     log(f"ep fused {cid(case)} workspace={workspace}")
     inp = workloads.make_ep(R, T, H, k=k, experts=E, epilogue=e, shared_rank=s,
                             seed=5000 + R * 7 + T * 13 + H)
-    y, x = gpu_ep(dev(inp), workspace=workspace)
+    d = dev(inp)
+    if workspace == "forced-split":
+        try:
+            m.set_launch_table("* * * * 0 * split\n")
+            assert m.split_rows(R, k, T, H, epi(d, m), ep=True) == (T <= 256)
+            y, x = gpu_ep(d, workspace="auto")
+        finally:
+            m.set_launch_table(None)
+    else:
+        y, x = gpu_ep(d, workspace=workspace)
     torch.cuda.synchronize()
     ref = oracle_ep(inp)
     parity.compare(f"ep {cid(case)} ws={workspace} out", workloads.bits(y), ref.y)
@@ -219,6 +232,7 @@ def test_ep_graph_capture_and_replay_with_new_data(T, workspace):
     routing keeps its shape), checking every replay against the oracle."""
     m = frn()
     log(f"ep graph T={T} workspace={workspace}")
+    assert m.split_rows(8, 6, T, 2048, m.EPI_SANDWICH, ep=True) == (workspace == "auto")
     host = workloads.make_ep(8, T, 2048, k=6, experts=32, epilogue="sandwich", shared_rank=2,
                              seed=321 + T)
     d = dev(host)

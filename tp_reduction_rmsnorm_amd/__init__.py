@@ -20,7 +20,9 @@ Function names are the C entry points without their ``frn_`` prefix:
                                  expert-parallel routing (each rank owns
                                  some experts; per-rank row indices)
 * ``query``, ``workspace_bytes``, ``version``
-* ``set_launch_table``, ``launch_shape``  tuned launch shapes (tune.py)
+* ``set_launch_table``, ``launch_shape``, ``split_rows``  tuned launch
+                                 shapes and the split-row finalize choice
+                                 (tune.py)
 * ``boundary``                   fused or split by a token threshold (a
                                  Python-side policy over the calls above)
 
@@ -107,6 +109,7 @@ _c_set_table = _sig("frn_set_launch_table", ctypes.c_int, [ctypes.c_char_p])
 _c_shape = _sig("frn_launch_shape", ctypes.c_int,
                 [_I32, _I32, _I64, _I64, _I32, ctypes.POINTER(_I32), ctypes.POINTER(_I32)])
 _c_ws = _sig("frn_workspace_bytes", _SZ, [_I64, _I64, _I32, _I32])
+_c_split_rows = _sig("frn_split_rows", _I32, [_I32, _I32, _I64, _I64, _I32])
 _c_status = _sig("frn_status_string", ctypes.c_char_p, [ctypes.c_int])
 _c_last = _sig("frn_last_error", ctypes.c_char_p, [])
 _c_version = _sig("frn_version", ctypes.c_char_p, [])
@@ -116,7 +119,8 @@ C_FUNCTIONS = ("frn_reduce_residual_rmsnorm", "frn_reduce_sandwich_norm",
                "frn_moe_finalize_reduce_bf16", "frn_split_reduce_norm", "frn_moe_finalize",
                "frn_ep_moe_finalize_reduce_norm", "frn_ep_moe_finalize",
                "frn_query", "frn_set_launch_table", "frn_launch_shape",
-               "frn_workspace_bytes", "frn_status_string", "frn_last_error", "frn_version")
+               "frn_workspace_bytes", "frn_split_rows", "frn_status_string", "frn_last_error",
+               "frn_version")
 
 
 def version() -> str:
@@ -150,8 +154,9 @@ EPI_SUM = 2  # split pass 1, for launch tables and launch_shape
 
 
 def set_launch_table(text: Optional[str]) -> None:
-    """Load tuned launch rules ('H R k epilogue Tmin Tmax vec' per line), or
-    None to restore the built-in rule.  Raises ValueError on bad text."""
+    """Load tuned launch rules ('H R k epilogue Tmin Tmax vec' per line, vec
+    1 | 2 | 4 | split | fused), or None to restore the built-in rules.
+    Raises ValueError on bad text."""
     _check(_c_set_table(None if text is None else text.encode()))
 
 
@@ -163,6 +168,13 @@ def launch_shape(R: int, k: int, T: int, H: int, epilogue: int = EPI_RMSNORM, *,
     _check(_c_shape(R, k, T, H, epilogue | (SHAPE_EP if ep else 0), ctypes.byref(th),
                     ctypes.byref(v)))
     return th.value, v.value
+
+
+def split_rows(R: int, k: int, T: int, H: int, epilogue: int = EPI_RMSNORM, *,
+               ep: bool = False) -> bool:
+    """True if a finalize call of these sizes that is given a large enough
+    workspace takes the split-row finalize (no launch)."""
+    return bool(_c_split_rows(R, k, T, H, epilogue | (SHAPE_EP if ep else 0)))
 
 
 # ---------------------------------------------------------------- helpers --- #
@@ -226,16 +238,19 @@ def _outputs(T, H, device, out, residual_out):
 _AUTO_WS = {}
 
 
-def _workspace(workspace, T=0, H=0, R=0, k=0, device=None, stream=None):
+def _workspace(workspace, T=0, H=0, R=0, k=0, device=None, stream=None,
+               epilogue=EPI_RMSNORM, ep=False):
     """(pointer, bytes) of the workspace argument.  ``"auto"``: a buffer
     cached per (device, stream) and grown on demand (it holds nothing between
-    calls).  ``None``: none."""
+    calls), passed only to a call that takes the split-row finalize.
+    ``None``: none."""
     if workspace is None:
         return None, 0
     if isinstance(workspace, str):
         if workspace != "auto":
             raise ValueError("workspace must be a tensor, None or 'auto'")
-        need = workspace_bytes(T, H, R, k) if k > 0 else 0
+        use = k > 0 and split_rows(R, k, T, H, epilogue, ep=ep)
+        need = workspace_bytes(T, H, R, k) if use else 0
         if need == 0:
             return None, 0
         key = (device.index, stream)
@@ -346,7 +361,8 @@ def moe_finalize_reduce_norm(expert_rows: TensorList, topk_weights: torch.Tensor
                              workspace="auto", stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Per rank r: P_r = bf16(sum_j w[t,j] * E_r[rows[t,j]] (+ shared_r[t])); then
     the epilogue on sum_r P_r.  Returns (out, residual_out).  ``workspace``:
-    "auto" (a buffer cached per device and stream, used for T <= 256), None
+    "auto" (a buffer cached per device and stream, used where ``split_rows``
+    holds: small T), None
     (never), or a uint8 GPU tensor of at least ``workspace_bytes(T, H, R, k)``
     bytes, 256-byte aligned."""
     if residual is None:
@@ -363,7 +379,7 @@ def moe_finalize_reduce_norm(expert_rows: TensorList, topk_weights: torch.Tensor
         _check_gamma(gamma2, H, device, "gamma2")
     out, residual_out = _outputs(T, H, device, out, residual_out)
     st = _stream(stream, device)
-    ws, wsb = _workspace(workspace, T, H, len(es), k, device, st)
+    ws, wsb = _workspace(workspace, T, H, len(es), k, device, st, epilogue)
     earr = _ptr_array(es)
     sarr = _ptr_array(sh) if sh is not None else None
     _check(_c_moe(ctypes.cast(earr, _P), ctypes.cast(sarr, _P) if sarr is not None else None,
@@ -505,7 +521,7 @@ def ep_moe_finalize_reduce_norm(expert_rows: Sequence[Optional[torch.Tensor]],
     out, residual_out = _outputs(T, H, device, out, residual_out)
     st = _stream(stream, device)
     R = len(es)
-    ws, wsb = _workspace(workspace, T, H, R, k, device, st)
+    ws, wsb = _workspace(workspace, T, H, R, k, device, st, epilogue, ep=True)
     earr = _ptr_array_opt(es)
     sarr = _ptr_array_opt(sh) if sh is not None else None
     rarr = _ptr_array(rows)

@@ -81,7 +81,8 @@ struct Call {
 
 frn_status add_in(Call& c, const char* name, const void* p, size_t bytes, bool need16 = true) {
     if (p == nullptr) return fail(FRN_ERR_INVALID, "%s is NULL", name);
-    if (need16 && !aligned16(p)) return fail(FRN_ERR_UNSUPPORTED, "%s is not 16-byte aligned", name);
+    if (need16 && !aligned16(p))
+        return fail(FRN_ERR_UNSUPPORTED, "%s is not 16-byte aligned", name);
     if (!need16 && (reinterpret_cast<uintptr_t>(p) & 3u))
         return fail(FRN_ERR_UNSUPPORTED, "%s is not 4-byte aligned", name);
     c.in[c.n_in++] = span(name, p, bytes);
@@ -242,14 +243,16 @@ frn_status run(const Call& c, int32_t epilogue, int64_t T, void* stream) {
     return FRN_OK;
 }
 
-// The optional workspace serves the split-row finalize when it is large
-// enough for this T; otherwise it is ignored (the one-row kernel needs none).
+// The optional workspace serves the split-row finalize where that is the
+// chosen path for this call and the workspace is large enough for its T;
+// otherwise it is ignored (the one-row kernel needs none).
 frn_status set_workspace(Call& c, void* workspace, size_t workspace_bytes, int32_t k, int64_t T,
-                         int64_t H, int32_t R) {
+                         int64_t H, int32_t R, int32_t epilogue) {
     c.a.ws_p = nullptr;
     if (k == 0 || workspace == nullptr) return FRN_OK;
+    if (!frn::use_split_rows(R, H, k, c.a.ep != 0, epilogue, T)) return FRN_OK;
     const size_t need = frn::split_workspace_bytes(T, H, R);
-    if (need == 0 || workspace_bytes < need) return FRN_OK;
+    if (workspace_bytes < need) return FRN_OK;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
         return fail(FRN_ERR_UNSUPPORTED, "workspace is not 256-byte aligned");
     frn_status st = add_out(c, "workspace", workspace, need);
@@ -259,9 +262,9 @@ frn_status set_workspace(Call& c, void* workspace, size_t workspace_bytes, int32
 }
 
 frn_status fused(const void* const* src, const void* const* shared, int32_t R,
-                 const Routing& g, int32_t k, int32_t epilogue, const void* residual_in, const float* g1, const float* g2,
-                 float eps, int64_t T, int64_t H, void* out, void* residual_out,
-                 void* workspace, size_t workspace_bytes, void* stream) {
+                 const Routing& g, int32_t k, int32_t epilogue, const void* residual_in,
+                 const float* g1, const float* g2, float eps, int64_t T, int64_t H, void* out,
+                 void* residual_out, void* workspace, size_t workspace_bytes, void* stream) {
     g_last_error[0] = '\0';
     frn_status st = check_sizes(R, k, T, H, epilogue);
     if (st != FRN_OK || T == 0) return st;  // empty tensors may carry null pointers
@@ -270,7 +273,8 @@ frn_status fused(const void* const* src, const void* const* shared, int32_t R,
     if ((st = set_epilogue(c, epilogue, residual_in, g1, g2, eps, T, H, out, residual_out)) !=
         FRN_OK)
         return st;
-    if ((st = set_workspace(c, workspace, workspace_bytes, k, T, H, R)) != FRN_OK) return st;
+    if ((st = set_workspace(c, workspace, workspace_bytes, k, T, H, R, epilogue)) != FRN_OK)
+        return st;
     if ((st = check_alias(c)) != FRN_OK) return st;
     return run(c, epilogue, T, stream);
 }
@@ -486,10 +490,21 @@ FRN_API frn_status frn_query(int32_t R, int32_t k, int64_t T, int64_t H, int32_t
 }
 
 FRN_API size_t frn_workspace_bytes(int64_t max_T, int64_t H, int32_t R, int32_t k) {
-    if (k < 1 || R < 1 || R > FRN_MAX_R || H < 8 || H > FRN_MAX_H || H % 8 != 0 || max_T < 1)
+    if (k < 1 || k > FRN_MAX_K || R < 1 || R > FRN_MAX_R || H < 8 || H > FRN_MAX_H ||
+        H % 8 != 0 || max_T < 1)
         return 0;
-    const int64_t t = max_T < frn::kSplitMaxT ? max_T : frn::kSplitMaxT;
-    return frn::split_workspace_bytes(t, H, R);
+    const int64_t cap = frn::split_rows_cap(R, H, k);
+    const int64_t t = max_T < cap ? max_T : cap;
+    return t < 1 ? 0 : frn::split_workspace_bytes(t, H, R);
+}
+
+FRN_API int32_t frn_split_rows(int32_t R, int32_t k, int64_t T, int64_t H, int32_t epilogue) {
+    const bool ep = (epilogue & FRN_SHAPE_EP) != 0;
+    epilogue &= ~FRN_SHAPE_EP;
+    if (k < 1 || (epilogue != FRN_EPI_RMSNORM && epilogue != FRN_EPI_SANDWICH)) return 0;
+    if (R < 1 || R > FRN_MAX_R || k > FRN_MAX_K || H < 8 || H > FRN_MAX_H || H % 8 != 0)
+        return 0;
+    return frn::use_split_rows(R, H, k, ep, epilogue, T) ? 1 : 0;
 }
 
 FRN_API const char* frn_status_string(frn_status s) {

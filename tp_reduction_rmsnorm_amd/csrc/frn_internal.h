@@ -44,18 +44,28 @@ struct RowArgs {
                                      // marks a slot of another rank's expert
 };
 
-// Split-row finalize (small T): workgroup size, the largest T it serves and
-// its workspace, R x T x H BF16 finalized partials (no other state: the
-// workspace needs no initialisation and keeps nothing between calls).
+// Split-row finalize (small T): workgroup size, the largest T any call may
+// take it at, and its workspace, R x T x H BF16 finalized partials (no other
+// state: the workspace needs no initialisation and keeps nothing between
+// calls).
 constexpr int kSplitThreads = 256;
-constexpr int64_t kSplitMaxT = 256;
+constexpr int64_t kSplitCapT = 256;
 
-// Workspace bytes the split-row finalize needs for T rows (0 if T is too
-// large for it).
+// Workspace bytes the split-row finalize needs for T rows.
 inline size_t split_workspace_bytes(int64_t T, int64_t H, int32_t R) {
-    if (T < 1 || T > kSplitMaxT) return 0;
     return (size_t)T * (size_t)R * (size_t)H * 2;
 }
+
+// Whether a finalize call (k >= 1) that is given a large enough workspace
+// takes the split-row finalize: the first matching split/fused rule of the
+// tuned table, else the built-in rule.  ep: expert-parallel routing.
+// Thread-safe.
+bool use_split_rows(int32_t R, int64_t H, int32_t k, bool ep, int epilogue, int64_t T);
+
+// The largest T at which use_split_rows can hold for these sizes, under
+// either routing and any epilogue (at most kSplitCapT): what a workspace
+// must cover.  Thread-safe.
+int64_t split_rows_cap(int32_t R, int64_t H, int32_t k);
 
 // Column slices of one row in the split-row finalize.
 int split_slices(int nvec);

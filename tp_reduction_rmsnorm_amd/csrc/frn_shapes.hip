@@ -1,5 +1,6 @@
-// frn_shapes.hip -- launch shapes of row_kernel: the built-in rule measured
-// on MI355X, and an optional table of tuned rules that overrides it.  Launch
+// frn_shapes.hip -- launch shapes of row_kernel and the choice between the
+// split-row and the one-row finalize: built-in rules measured on MI355X,
+// and an optional table of tuned rules that overrides them.  Launch
 // profiles tuned for one hidden size do not carry over to another (SGLang PR
 // #34134: shipped profiles for H=8192 misfit H=6144), so a deployment can
 // measure its own shapes (tp_reduction_rmsnorm_amd/tune.py) and load them.
@@ -18,11 +19,17 @@ namespace {
 
 // One tuned rule; -1 in H, R, k, epilogue, ep means "any".  T in [tmin,
 // tmax].  ep: 1 for calls with expert-parallel routing, 0 for the others.
+// vec 1, 2 or 4: vectors per lane of row_kernel; kSplitRule / kFusedRule:
+// a finalize call given a workspace takes the split-row / the one-row
+// finalize.
 struct Rule {
     int64_t H, R, k, epilogue, ep;
     int64_t tmin, tmax;
     int vec;
 };
+
+constexpr int kSplitRule = -1;
+constexpr int kFusedRule = -2;
 
 std::mutex g_mu;
 std::vector<Rule> g_rules;
@@ -90,14 +97,19 @@ bool parse(const char* text, std::vector<Rule>& out, std::string& err) {
         if (tok.empty()) continue;
         Rule r{};
         int64_t vec = 0;
-        if (tok.size() != 7 || !parse_field(tok[0].c_str(), &r.H) ||
+        const bool last_ok =
+            tok.size() == 7 &&
+            (tok[6] == "split"   ? (vec = kSplitRule, true)
+             : tok[6] == "fused" ? (vec = kFusedRule, true)
+                                 : parse_field(tok[6].c_str(), &vec) &&
+                                       (vec == 1 || vec == 2 || vec == 4));
+        if (!last_ok || !parse_field(tok[0].c_str(), &r.H) ||
             !parse_field(tok[1].c_str(), &r.R) || !parse_field(tok[2].c_str(), &r.k) ||
             !parse_epilogue(tok[3].c_str(), &r.epilogue, &r.ep) ||
-            !parse_field(tok[4].c_str(), &r.tmin) || !parse_field(tok[5].c_str(), &r.tmax) ||
-            !parse_field(tok[6].c_str(), &vec) || !(vec == 1 || vec == 2 || vec == 4)) {
+            !parse_field(tok[4].c_str(), &r.tmin) || !parse_field(tok[5].c_str(), &r.tmax)) {
             err = "launch table line " + std::to_string(lineno) +
                   ": expected 'H R k epilogue Tmin Tmax vec' (numbers or *, epilogue "
-                  "rmsnorm|sandwich|sum|ep-rmsnorm|ep-sandwich|ep-*|*, vec 1|2|4)";
+                  "rmsnorm|sandwich|sum|ep-rmsnorm|ep-sandwich|ep-*|*, vec 1|2|4|split|fused)";
             return false;
         }
         if (r.tmin < 0) r.tmin = 0;
@@ -118,7 +130,8 @@ void load_env_table_locked() {
     if (path == nullptr || path[0] == '\0') return;
     FILE* f = fopen(path, "rb");
     if (f == nullptr) {
-        fprintf(stderr, "fused_reduce_norm: cannot open FRN_LAUNCH_TABLE=%s; using built-in shapes\n",
+        fprintf(stderr,
+                "fused_reduce_norm: cannot open FRN_LAUNCH_TABLE=%s; using built-in shapes\n",
                 path);
         return;
     }
@@ -177,7 +190,70 @@ bool vec_fits(int vec, int nvec, bool finalize, int epilogue) {
     return true;
 }
 
+// The built-in choice of the split-row finalize (a workgroup per (token,
+// rank, 2048-column slice), then the reduction pass) over the one-row
+// finalize, from graph-replay sweeps on MI355X with inputs rotated over
+// 1 GiB.  The one-row kernel waits on one memory round trip per rank (TP
+// routing) or per chunk of live rows (expert-parallel), so at small T its
+// time is nearly flat in T; the split-row finalize writes and re-reads R
+// partial rows per token, so its time grows with T from a lower start.
+// Largest T at which the split-row finalize still won:
+//  - TP routing, R <= 2: 32 at H*k >= 32768 (H=7168 k=8: 9.1 against 9.8
+//    us at T=32, 10.0 against 9.9 at T=48); none below (H=4096 k=4 and
+//    H=2048 k=8 are within 5% either way);
+//  - TP routing, R >= 3: 96 (H=6144 R=8 k=10: 28.1 against 33.0 us at
+//    T=96, 35.9 against 33.2 at T=128; the same at H=5120 R=4, H=7168 R=8,
+//    H=8192 R=4 and H=16384 R=8); 128 at R=16 (H=4096); 192 at H <= 2048;
+//  - expert-parallel routing, where the one-row kernel loads several
+//    ranks' rows at once: 8 at R <= 2, 16 at R <= 8 (H=6144 R=8 k=10:
+//    9.8 against 10.9 us at T=16, 11.0 each at T=32, 13.8 against 11.2 at
+//    T=64), 48 at R=16 or H <= 2048.
+int64_t builtin_split_max_t(int32_t R, int64_t H, int32_t k, bool ep) {
+    if (ep) {
+        if (R <= 2) return 8;
+        if (R >= 16 || H <= 2048) return 48;
+        return 16;
+    }
+    if (R <= 2) return H * k >= 32768 ? 32 : 0;
+    if (H <= 2048) return 192;
+    return R >= 16 ? 128 : 96;
+}
+
+bool matches(const Rule& r, int64_t H, int64_t R, int64_t k, int64_t epilogue, int64_t ep) {
+    return (r.H < 0 || r.H == H) && (r.R < 0 || r.R == R) && (r.k < 0 || r.k == k) &&
+           (r.epilogue < 0 || r.epilogue == epilogue) && (r.ep < 0 || r.ep == ep);
+}
+
 }  // namespace
+
+bool use_split_rows(int32_t R, int64_t H, int32_t k, bool ep, int epilogue, int64_t T) {
+    if (k < 1 || T < 1 || T > kSplitCapT) return false;
+    {
+        std::lock_guard<std::mutex> lock(g_mu);
+        load_env_table_locked();
+        for (const Rule& r : g_rules) {
+            if (r.vec >= 0 || !matches(r, H, R, k, epilogue, ep ? 1 : 0)) continue;
+            if (T >= r.tmin && T <= r.tmax) return r.vec == kSplitRule;
+        }
+    }
+    return T <= builtin_split_max_t(R, H, k, ep);
+}
+
+int64_t split_rows_cap(int32_t R, int64_t H, int32_t k) {
+    if (k < 1) return 0;
+    int64_t cap = builtin_split_max_t(R, H, k, false);
+    const int64_t cap_ep = builtin_split_max_t(R, H, k, true);
+    if (cap_ep > cap) cap = cap_ep;
+    {
+        std::lock_guard<std::mutex> lock(g_mu);
+        load_env_table_locked();
+        for (const Rule& r : g_rules)
+            if (r.vec == kSplitRule && (r.H < 0 || r.H == H) && (r.R < 0 || r.R == R) &&
+                (r.k < 0 || r.k == k) && r.tmax > cap)
+                cap = r.tmax;
+    }
+    return cap < kSplitCapT ? cap : kSplitCapT;
+}
 
 LaunchShape choose_shape(int nvec, int fin, int64_t T, int epilogue, int R, int k) {
     const bool finalize = fin != kNoFinalize;
@@ -188,9 +264,7 @@ LaunchShape choose_shape(int nvec, int fin, int64_t T, int epilogue, int R, int 
         load_env_table_locked();
         const int64_t H = (int64_t)nvec * 8;
         for (const Rule& r : g_rules) {
-            if ((r.H < 0 || r.H == H) && (r.R < 0 || r.R == R) && (r.k < 0 || r.k == k) &&
-                (r.epilogue < 0 || r.epilogue == epilogue) && (r.ep < 0 || r.ep == ep) &&
-                T >= r.tmin && T <= r.tmax &&
+            if (r.vec > 0 && matches(r, H, R, k, epilogue, ep) && T >= r.tmin && T <= r.tmax &&
                 vec_fits(r.vec, nvec, finalize, epilogue)) {
                 vec = r.vec;
                 break;

@@ -6,18 +6,21 @@
 For every shape and token count, each vectors-per-lane choice that fits is
 forced through ``set_launch_table`` and timed the way the pages time this
 operation (vLLM PR #62366, kernel microbenchmark table): a HIP graph holding
-``--calls`` calls, median of 5 replays.  Inputs are random BF16 tensors
-rotated over at least 1 GiB from T >= 256, so the timings are not served
+``--calls`` calls, median of 5 replays.  Inputs rotate over up to 64 sets,
+at least 1 GiB where that many sets reach it, so large calls are not served
 from the Infinity Cache.  The fastest choice per T becomes a rule covering
 the T range up to it; neighbouring ranges with the same choice merge.  Load
 the table with ``FRN_LAUNCH_TABLE=<file>`` or ``set_launch_table(text)``.
 
-Shapes without finalize (k = 0) tune every call of that shape; with k > 0
-the rules matter above T = 256 (below it the finalize runs split-row and
-its reduction pass is a k = 0 call of the same H and R).  An epilogue named
-``ep-rmsnorm`` or ``ep-sandwich`` tunes the expert-parallel finalize
-(``ep_moe_finalize_reduce_norm``): each of the R ranks owns an equal share of
-4R experts (at least k), and each token picks k distinct ones at random.
+Shapes with a finalize (k > 0, not ``sum``) are also timed at
+``--split-tokens`` (T <= 256) with the split-row finalize forced (a
+workspace and a ``split`` rule) against the one-row kernel (no workspace);
+the winner per T becomes ``split`` / ``fused`` rules.  The vec rules of a
+finalize shape describe the one-row kernel; where the split-row finalize
+runs, its reduction pass is a k = 0 call of the same H and R.  An epilogue
+named ``ep-rmsnorm`` or ``ep-sandwich`` tunes the expert-parallel finalize
+(``ep_moe_finalize_reduce_norm``): each of the R ranks owns an equal share
+of 4R experts (at least k), and each token picks k distinct ones at random.
 """
 from __future__ import annotations
 
@@ -35,9 +38,10 @@ import tp_reduction_rmsnorm_amd as frn  # noqa: E402
 EPI = {"rmsnorm": frn.EPI_RMSNORM, "sandwich": frn.EPI_SANDWICH, "sum": frn.EPI_SUM,
        "ep-rmsnorm": frn.EPI_RMSNORM, "ep-sandwich": frn.EPI_SANDWICH}
 DEFAULT_SHAPES = [(5120, 4, 0, "sandwich"), (8192, 8, 0, "sandwich"), (512, 2, 0, "rmsnorm"),
-                  (6144, 8, 0, "rmsnorm"), (7168, 2, 8, "rmsnorm"), (7168, 2, 0, "rmsnorm"),
-                  (7168, 2, 8, "sum"), (6144, 8, 10, "ep-rmsnorm")]
+                  (6144, 8, 0, "rmsnorm"), (6144, 8, 10, "rmsnorm"), (7168, 2, 8, "rmsnorm"),
+                  (7168, 2, 0, "rmsnorm"), (7168, 2, 8, "sum"), (6144, 8, 10, "ep-rmsnorm")]
 DEFAULT_TOKENS = [1, 8, 64, 256, 512, 1024, 2048, 4096, 16384]
+DEFAULT_SPLIT_TOKENS = [1, 8, 16, 32, 48, 64, 96, 128, 192, 256]
 
 
 def _bf16(shape, dev, g):
@@ -52,8 +56,9 @@ class Call:
         g.manual_seed(H * 131 + R * 17 + k * 7 + T)
         self.ep = epi.startswith("ep-")
         per_set = T * H * 2 * ((k + 1 if self.ep else R * (k + 1 if k else 1)) + 3)
-        n = max(1, min(16, -(-(1 << 30) // per_set))) if T >= 256 else 1
+        n = max(1, min(64, -(-(1 << 30) // per_set)))
         self.H, self.R, self.k, self.epi, self.T = H, R, k, epi, T
+        self.workspace = None
         self.sets = []
         for _ in range(n):
             d = dict(residual=_bf16((T, H), dev, g), g1=torch.rand(H, generator=g, device=dev) + 0.5,
@@ -88,7 +93,8 @@ class Call:
             return frn.ep_moe_finalize_reduce_norm(d["src"], d["w"], d["rows"], d["residual"],
                                                    d["g1"], d["g2"], shared=d["shared"],
                                                    epilogue=EPI[self.epi], out=d["out"],
-                                                   residual_out=d["rout"], workspace=None)
+                                                   residual_out=d["rout"],
+                                                   workspace=self.workspace)
         if self.epi == "sum":
             if self.k:
                 return frn.moe_finalize_reduce_bf16(d["src"], d["w"], d["idx"], shared=d["shared"],
@@ -98,7 +104,7 @@ class Call:
             return frn.moe_finalize_reduce_norm(d["src"], d["w"], d["idx"], d["residual"], d["g1"],
                                                 d["g2"], shared=d["shared"], epilogue=EPI[self.epi],
                                                 out=d["out"], residual_out=d["rout"],
-                                                workspace=None)
+                                                workspace=self.workspace)
         if self.epi == "sandwich":
             return frn.reduce_sandwich_norm(d["src"], d["residual"], d["g1"], d["g2"],
                                             out=d["out"], residual_out=d["rout"])
@@ -154,12 +160,38 @@ def tune_shape(H, R, k, epi, tokens, calls, dev, log=print):
     return rows
 
 
-def rules_for(H, R, k, epi, rows):
-    """Merge per-T winners into 'H R k epilogue Tmin Tmax vec' lines."""
+def tune_split(H, R, k, epi, tokens, calls, dev, log=print):
+    """[(T, 'split' | 'fused', {choice: us})] for one finalize shape: the
+    split-row finalize (forced by a rule, with a workspace) against the
+    one-row kernel (no workspace)."""
+    rows = []
+    for T in tokens:
+        call = Call(H, R, k, epi, T, dev)
+        times = {}
+        try:
+            frn.set_launch_table(f"{H} {R} {k} {epi} {T} {T} split")
+            call.workspace = "auto"
+            times["split"] = graph_us(call, calls)
+        finally:
+            frn.set_launch_table(None)
+        call.workspace = None
+        times["fused"] = graph_us(call, calls)
+        best = min(times, key=times.get)
+        rows.append((T, best, times))
+        log(f"H={H} R={R} k={k} {epi} T={T}: split {times['split']:.2f} us, "
+            f"fused {times['fused']:.2f} us -> {best}")
+        del call
+        torch.cuda.empty_cache()
+    return rows
+
+
+def rules_for(H, R, k, epi, rows, last="*"):
+    """Merge per-T winners into 'H R k epilogue Tmin Tmax vec' lines; the
+    last range ends at ``last``."""
     out = []
     lo = 0
     for i, (T, best, _) in enumerate(rows):
-        hi = "*" if i == len(rows) - 1 else str(T)
+        hi = last if i == len(rows) - 1 else str(T)
         if out and out[-1][2] == best:
             out[-1][1] = hi
         else:
@@ -173,8 +205,12 @@ def main():
     ap.add_argument("--out", required=True)
     ap.add_argument("--shape", nargs=4, action="append", metavar=("H", "R", "k", "EPILOGUE"))
     ap.add_argument("--tokens", nargs="+", type=int, default=DEFAULT_TOKENS)
+    ap.add_argument("--split-tokens", nargs="+", type=int, default=DEFAULT_SPLIT_TOKENS,
+                    help="T values (<= 256) at which finalize shapes time the split-row "
+                         "finalize against the one-row kernel")
     ap.add_argument("--calls", type=int, default=20)
     args = ap.parse_args()
+    split_tokens = sorted(t for t in set(args.split_tokens) if 1 <= t <= 256)
     shapes = ([(int(h), int(r), int(k), e) for h, r, k, e in args.shape] if args.shape
               else DEFAULT_SHAPES)
     dev = torch.device("cuda:0")
@@ -185,6 +221,9 @@ def main():
     for H, R, k, epi in shapes:
         rows = tune_shape(H, R, k, epi, sorted(set(args.tokens)), args.calls, dev)
         lines += rules_for(H, R, k, epi, rows)
+        if k > 0 and epi != "sum" and split_tokens:
+            rows = tune_split(H, R, k, epi, split_tokens, args.calls, dev)
+            lines += rules_for(H, R, k, epi, rows, last="256")
     with open(args.out, "w") as f:
         f.write("\n".join(lines) + "\n")
     frn.set_launch_table(open(args.out).read())  # validates the file
