@@ -437,20 +437,28 @@ def test_launch_shape_builtin_rule():
     import tp_reduction_rmsnorm_amd as frn
     frn.set_launch_table(None)
     S = frn.EPI_SANDWICH
-    assert frn.launch_shape(4, 0, 1, 5120, S) == (640, 1)      # small T: <= 640 lanes
-    assert frn.launch_shape(8, 0, 8, 8192, S) == (512, 2)
+    assert frn.launch_shape(4, 0, 1, 5120, S) == (640, 1)      # small T: one vector ...
+    assert frn.launch_shape(8, 0, 8, 8192, S) == (1024, 1)     # ... up to 1024 lanes at T <= 64
+    assert frn.launch_shape(8, 0, 256, 8192, S) == (512, 2)    # ... up to 896 at T <= 256
+    assert frn.launch_shape(8, 0, 200, 6144, 0) == (768, 1)
+    assert frn.launch_shape(4, 0, 512, 5120, S) == (320, 2)    # T <= 512: two below 1024 vectors
+    assert frn.launch_shape(8, 0, 512, 8192, S) == (256, 4)
     assert frn.launch_shape(4, 0, 1024, 5120, S) == (192, 4)   # mid T: four vectors
     assert frn.launch_shape(4, 0, 4096, 5120, S) == (320, 2)   # large T
     assert frn.launch_shape(8, 0, 4096, 8192, S) == (256, 4)   # long rows: four up to 4096
     assert frn.launch_shape(8, 0, 16384, 8192, S) == (512, 2)
     assert frn.launch_shape(2, 8, 4096, 7168, 0) == (896, 1)   # finalize: one vector
-    assert frn.launch_shape(2, 8, 1024, 7168, 0) == (448, 2)   # ... two at mid T
-    assert frn.launch_shape(2, 8, 1024, 7168, frn.EPI_SUM) == (896, 1)
+    assert frn.launch_shape(2, 8, 1024, 7168, 0) == (448, 2)   # ... two at mid T for R <= 2
+    assert frn.launch_shape(8, 10, 512, 6144, 0) == (384, 2)   # ... and up to 512 above
+    assert frn.launch_shape(8, 10, 1024, 6144, 0) == (768, 1)
+    assert frn.launch_shape(2, 8, 1024, 7168, frn.EPI_SUM) == (448, 2)
+    assert frn.launch_shape(2, 8, 2048, 7168, frn.EPI_SUM) == (896, 1)
     assert frn.launch_shape(2, 0, 1024, 7168, frn.EPI_SUM) == (448, 2)  # no 4 in pass 1
     assert frn.launch_shape(2, 0, 8, 16384, S) == (1024, 2)
-    # expert-parallel finalize: one vector per lane at every T
+    # expert-parallel finalize: one vector per lane, two for 256 < T <= 512
     assert frn.launch_shape(8, 10, 1024, 6144, 0, ep=True) == (768, 1)
-    assert frn.launch_shape(8, 10, 1024, 6144, 0) == (384, 2)
+    assert frn.launch_shape(8, 10, 512, 6144, 0, ep=True) == (384, 2)
+    assert frn.launch_shape(8, 10, 64, 6144, 0, ep=True) == (768, 1)
     assert frn.launch_shape(2, 4, 64, 16384, S, ep=True) == (1024, 2)
     with pytest.raises(ValueError):
         frn.launch_shape(8, 0, 1024, 6144, 0, ep=True)      # no finalize
@@ -604,3 +612,19 @@ def test_builtin_launch_shapes_always_fit():
                             assert v in (1, 2, 4)
                             if k or epi == frn.EPI_SUM:
                                 assert v != 4, (H, R, k, epi, T)
+
+
+def test_shipped_launch_table_parses_and_routes():
+    """The measured table shipped with the package loads, and its split /
+    fused rules route the finalize workloads as measured."""
+    import tp_reduction_rmsnorm_amd as frn
+    path = os.path.join(ROOT, "tp_reduction_rmsnorm_amd", "launch_table_mi355x.txt")
+    try:
+        frn.set_launch_table(open(path).read())
+        assert frn.split_rows(8, 10, 96, 6144) and not frn.split_rows(8, 10, 97, 6144)
+        assert frn.split_rows(2, 8, 32, 7168) and not frn.split_rows(2, 8, 33, 7168)
+        assert frn.split_rows(8, 10, 1, 6144, ep=True)
+        assert not frn.split_rows(8, 10, 64, 6144, ep=True)
+        assert frn.launch_shape(4, 0, 4096, 5120, frn.EPI_SANDWICH)[1] in (2, 4)
+    finally:
+        frn.set_launch_table(None)

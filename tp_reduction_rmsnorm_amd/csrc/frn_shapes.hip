@@ -150,35 +150,48 @@ void load_env_table_locked() {
 }
 
 // The built-in rule, from graph-replay sweeps on MI355X (the sandwich
-// workloads H=5120 R=4 and H=8192 R=8 by hand, then tune.py over the five
-// measured shapes):
-//  - small T (<= 256, latency-bound): the fewest vectors that keep a row
-//    within 640 lanes -- more lanes issue the row's loads at once
-//    (H=5120 T=1: 4.0 us with one vector, 4.4 with two);
-//  - larger T without finalize: four vectors per lane for rows of 512+
-//    vectors up to T = 1024, and for rows of 768+ vectors (H >= 6144) up to
-//    T = 4096 -- fewer waves per row to synchronise (H=5120 T=1024: 15.3 ->
-//    14.7 us; H=8192 T=512: 18.8 -> 17.7 us, T=4096: 119.6 -> 118.3 us);
-//    beyond that two vectors for rows over 512 vectors (H=5120 at T=2048
-//    and 4096: two vectors 29.1 and 51.9 us, four 29.5 and 52.0 us);
+// workloads by hand, then tune.py over nine shapes with inputs rotated over
+// 1 GiB, the disputed cells A/B/B/A-interleaved):
+//  - small T (latency-bound): one vector per lane up to 1024 lanes for
+//    T <= 64 and up to 896 lanes for T <= 256, else two -- more lanes issue
+//    the row's loads at once (H=6144 R=8 T=1: 3.8 us with one vector, 4.2
+//    with two; H=5120 T=64: 5.1 against 5.5); at 1024 lanes two vectors
+//    win again from T ~ 256 (H=8192 T=256: 10.6 against 10.9 us);
+//  - larger T without finalize: four vectors per lane for rows of 1024+
+//    vectors from T = 257 and of 512+ vectors from T = 513, up to T = 1024,
+//    and for rows of 768+ vectors (H >= 6144) up to T = 4096 -- fewer waves
+//    per row to synchronise (H=5120 T=1024: 16.0 -> 15.3 us; H=8192 T=512:
+//    18.8 -> 17.7 us); two vectors below 1024 vectors at T <= 512 (H=5120:
+//    9.1 -> 8.7 us, H=7168 R=2: 8.7 -> 8.3 us at T=512); beyond that two
+//    vectors for rows over 512 vectors (H=5120 at T=2048 and 4096: two
+//    vectors 29.1 and 51.9 us, four 29.5 and 52.0 us);
 //  - with finalize, one vector per lane up to 1024 lanes, except two for
-//    256 < T <= 2048 outside split pass 1 (H=7168 R=2 k=8: T=512 30.0 ->
-//    27.4 us, T=1024 57.4 -> 53.4 us; at T=4096 one vector is ahead again);
+//    256 < T <= 1024 at R <= 2 and for split pass 1, and for 256 < T <= 512
+//    at R > 2 (H=7168 R=2 k=8: T=512 29.0 -> 27.6 us, T=1024 57.4 -> 53.4
+//    us; H=6144 R=8 k=10: T=512 91.9 -> 88.8 us with two, T=1024 195.9 ->
+//    181.9 us with one);
 //  - with the expert-parallel finalize, one vector per lane up to 1024
-//    lanes at every T: its work list is short per rank, and more tokens in
-//    flight per CU matter more (H=6144 R=8 k=10: T=1024 51.6 -> 43.4 us,
-//    T=4096 167.6 -> 151.2 us against two vectors).
+//    lanes except two for 256 < T <= 512: its work list is short per rank,
+//    and more tokens in flight per CU matter more (H=6144 R=8 k=10: T=4096
+//    131 against 145 us with two; T=512 21.1 against 20.4).
 // Four vectors are never used with the finalize (too many live registers)
 // or for split pass 1 (it spills).
-int builtin_vec(int nvec, int fin, int64_t T, int epilogue) {
-    if (fin == kEpFinalize) return nvec <= 1024 ? 1 : 2;
-    if (fin == kTpFinalize) {
-        if (T > 256 && T <= 2048 && epilogue != kStoreSum && nvec <= 2048) return 2;
+int builtin_vec(int nvec, int fin, int64_t T, int epilogue, int R) {
+    if (fin == kEpFinalize) {
+        if (T > 256 && T <= 512 && nvec <= 2048) return 2;
         return nvec <= 1024 ? 1 : 2;
     }
-    if (T <= 256) return nvec <= 640 ? 1 : 2;
-    if (epilogue != kStoreSum && nvec >= 512 && (T <= 1024 || (nvec >= 768 && T <= 4096)))
-        return 4;
+    if (fin == kTpFinalize) {
+        const int64_t two_up_to = (epilogue == kStoreSum || R <= 2) ? 1024 : 512;
+        if (T > 256 && T <= two_up_to && nvec <= 2048) return 2;
+        return nvec <= 1024 ? 1 : 2;
+    }
+    if (T <= 64) return nvec <= 1024 ? 1 : 2;
+    if (T <= 256) return nvec <= 896 ? 1 : 2;
+    if (epilogue != kStoreSum && nvec >= 512) {
+        if (T <= 512) return nvec >= 1024 ? 4 : 2;
+        if (T <= 1024 || (nvec >= 768 && T <= 4096)) return 4;
+    }
     return nvec <= 512 ? 1 : 2;
 }
 
@@ -271,7 +284,7 @@ LaunchShape choose_shape(int nvec, int fin, int64_t T, int epilogue, int R, int 
             }
         }
     }
-    if (vec == 0) vec = builtin_vec(nvec, fin, T, epilogue);
+    if (vec == 0) vec = builtin_vec(nvec, fin, T, epilogue, R);
     LaunchShape sh;
     sh.vec = vec;
     const int lanes = (nvec + vec - 1) / vec;
