@@ -438,9 +438,9 @@ def test_launch_shape_builtin_rule():
     frn.set_launch_table(None)
     S = frn.EPI_SANDWICH
     assert frn.launch_shape(4, 0, 1, 5120, S) == (640, 1)      # small T: one vector ...
-    assert frn.launch_shape(8, 0, 8, 8192, S) == (1024, 1)     # ... up to 1024 lanes at T <= 64
-    assert frn.launch_shape(8, 0, 256, 8192, S) == (512, 2)    # ... up to 896 at T <= 256
-    assert frn.launch_shape(8, 0, 200, 6144, 0) == (768, 1)
+    assert frn.launch_shape(8, 0, 200, 6144, 0) == (768, 1)    # ... up to 896 lanes
+    assert frn.launch_shape(2, 0, 256, 7168, 0) == (896, 1)
+    assert frn.launch_shape(8, 0, 8, 8192, S) == (512, 2)
     assert frn.launch_shape(4, 0, 512, 5120, S) == (320, 2)    # T <= 512: two below 1024 vectors
     assert frn.launch_shape(8, 0, 512, 8192, S) == (256, 4)
     assert frn.launch_shape(4, 0, 1024, 5120, S) == (192, 4)   # mid T: four vectors

@@ -152,11 +152,12 @@ void load_env_table_locked() {
 // The built-in rule, from graph-replay sweeps on MI355X (the sandwich
 // workloads by hand, then tune.py over nine shapes with inputs rotated over
 // 1 GiB, the disputed cells A/B/B/A-interleaved):
-//  - small T (latency-bound): one vector per lane up to 1024 lanes for
-//    T <= 64 and up to 896 lanes for T <= 256, else two -- more lanes issue
-//    the row's loads at once (H=6144 R=8 T=1: 3.8 us with one vector, 4.2
-//    with two; H=5120 T=64: 5.1 against 5.5); at 1024 lanes two vectors
-//    win again from T ~ 256 (H=8192 T=256: 10.6 against 10.9 us);
+//  - small T (T <= 256, latency-bound): one vector per lane up to 896
+//    lanes, else two -- more lanes issue the row's loads at once (H=6144
+//    R=8 T=1: 3.8 us with one vector, 4.2 with two; H=5120 T=64: 5.0
+//    against 5.3); at 1024 lanes (H=8192) it is a wash at T <= 64, 1.5%
+//    either way with hot or cold inputs, and two vectors win at T = 256
+//    (10.6 against 10.9 us);
 //  - larger T without finalize: four vectors per lane for rows of 1024+
 //    vectors from T = 257 and of 512+ vectors from T = 513, up to T = 1024,
 //    and for rows of 768+ vectors (H >= 6144) up to T = 4096 -- fewer waves
@@ -186,7 +187,6 @@ int builtin_vec(int nvec, int fin, int64_t T, int epilogue, int R) {
         if (T > 256 && T <= two_up_to && nvec <= 2048) return 2;
         return nvec <= 1024 ? 1 : 2;
     }
-    if (T <= 64) return nvec <= 1024 ? 1 : 2;
     if (T <= 256) return nvec <= 896 ? 1 : 2;
     if (epilogue != kStoreSum && nvec >= 512) {
         if (T <= 512) return nvec >= 1024 ? 4 : 2;
