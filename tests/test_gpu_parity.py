@@ -548,6 +548,52 @@ def test_split_row_graph_replay():
         check(f"split-row graph replay {rep}", out, rout, oracle_ref(new))
 
 
+def test_auto_workspace_graphs_survive_a_larger_capture():
+    """Two graphs captured with the automatic workspace on torch's shared
+    capture stream, the second needing a larger buffer: the first graph's
+    buffer stays alive, and every replay of both matches the oracle."""
+    m = frn()
+    R, H, k = 8, 6144, 10
+    graphs = []
+    for T, seed in ((4, 610), (64, 620)):
+        assert m.split_rows(R, k, T, H)
+        base = to_dev(workloads.make(R, T, H, k=k, shared=True, seed=seed))
+        out = torch.empty(T, H, dtype=torch.bfloat16, device=DEV)
+        rout = torch.empty(T, H, dtype=torch.bfloat16, device=DEV)
+
+        def call(base=base, out=out, rout=rout):
+            m.moe_finalize_reduce_norm(base.expert_rows, base.topk_w, base.topk_idx,
+                                       base.residual, base.gamma1, None, base.eps,
+                                       shared=base.shared, out=out, residual_out=rout,
+                                       workspace="auto")
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            call()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            call()
+        graphs.append((T, base, out, rout, g))
+    assert any(len(kept) >= 2 for kept in m._AUTO_WS.values())   # grown, old one kept
+    scratch = [torch.full((1 << 22,), 7, dtype=torch.uint8, device=DEV) for _ in range(8)]
+    for rep in range(3):
+        for T, base, out, rout, g in graphs:
+            new = workloads.make(R, T, H, k=k, shared=True, seed=900 + 10 * T + rep)
+            for dst, src in zip(base.expert_rows + base.shared, new.expert_rows + new.shared):
+                dst.copy_(src.to(DEV))
+            base.topk_w.copy_(new.topk_w.to(DEV))
+            base.topk_idx.copy_(new.topk_idx.to(DEV))
+            base.residual.copy_(new.residual.to(DEV))
+            base.gamma1.copy_(new.gamma1.to(DEV))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            check(f"auto-workspace graph T={T} replay {rep}", out, rout, oracle_ref(new))
+    del scratch
+
+
 # ------------------------------------------------------ launch shapes --- #
 
 SHAPE_CASES = [(4, 300, 5120, "sandwich", 0, False), (3, 7, 5128, "rmsnorm", 0, False),

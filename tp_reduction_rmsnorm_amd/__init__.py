@@ -235,15 +235,21 @@ def _outputs(T, H, device, out, residual_out):
     return out, residual_out
 
 
+# Automatic workspaces per (device, stream): every buffer ever handed out is
+# kept until the process ends, because a HIP graph captured with one keeps
+# its address; a larger need allocates a new buffer (at least twice the last
+# one, so there are few) instead of freeing the old.
 _AUTO_WS = {}
 
 
 def _workspace(workspace, T=0, H=0, R=0, k=0, device=None, stream=None,
                epilogue=EPI_RMSNORM, ep=False):
     """(pointer, bytes) of the workspace argument.  ``"auto"``: a buffer
-    cached per (device, stream) and grown on demand (it holds nothing between
-    calls), passed only to a call that takes the split-row finalize.
-    ``None``: none."""
+    kept per (device, stream) of the call and grown on demand (it holds
+    nothing between calls), passed only to a call that takes the split-row
+    finalize.  Calls on one stream run in order, so they can share it; graphs
+    captured on one stream share it too and must not be replayed
+    concurrently (give those explicit workspaces).  ``None``: none."""
     if workspace is None:
         return None, 0
     if isinstance(workspace, str):
@@ -253,11 +259,11 @@ def _workspace(workspace, T=0, H=0, R=0, k=0, device=None, stream=None,
         need = workspace_bytes(T, H, R, k) if use else 0
         if need == 0:
             return None, 0
-        key = (device.index, stream)
-        ws = _AUTO_WS.get(key)
-        if ws is None or ws.numel() < need:
-            ws = torch.empty(need, dtype=torch.uint8, device=device)
-            _AUTO_WS[key] = ws
+        kept = _AUTO_WS.setdefault((device.index, stream), [])
+        if not kept or kept[-1].numel() < need:
+            size = max(need, 2 * kept[-1].numel()) if kept else need
+            kept.append(torch.empty(size, dtype=torch.uint8, device=device))
+        ws = kept[-1]
         return ws.data_ptr(), ws.numel()
     if not workspace.is_cuda or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous GPU tensor")
