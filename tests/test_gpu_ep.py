@@ -115,6 +115,24 @@ def test_ep_fused_matches_oracle(case, workspace):
     parity.compare(f"ep {cid(case)} ws={workspace} residual_out", workloads.bits(x), ref.xout)
 
 
+@pytest.mark.parametrize("T", [16, 17])
+def test_ep_at_the_split_row_edge(T):
+    """Either side of the built-in split-row edge of the expert-parallel
+    workload (16 tokens at R=8): automatic workspace, one-row kernel and
+    oracle agree bit for bit."""
+    m = frn()
+    assert m.split_rows(8, 10, T, 6144, ep=True) == (T <= 16)
+    inp = workloads.make_ep(8, T, 6144, k=10, experts=256, shared_rank=0, seed=6400 + T)
+    d = dev(inp)
+    y, x = gpu_ep(d)
+    y2, x2 = gpu_ep(d, workspace=None)
+    torch.cuda.synchronize()
+    assert same(y, y2) and same(x, x2)
+    ref = oracle_ep(inp)
+    parity.compare(f"ep edge T={T} out", workloads.bits(y), ref.y)
+    parity.compare(f"ep edge T={T} residual_out", workloads.bits(x), ref.xout)
+
+
 @pytest.mark.parametrize("case", CASES[:2] + CASES[4:7], ids=[cid(c) for c in CASES[:2] + CASES[4:7]])
 def test_ep_standalone_finalize_matches_oracle(case):
     R, T, H, e, k, E, s = case

@@ -548,6 +548,23 @@ def test_split_row_graph_replay():
         check(f"split-row graph replay {rep}", out, rout, oracle_ref(new))
 
 
+@pytest.mark.parametrize("T", [96, 97])
+def test_finalize_at_the_split_row_edge(T):
+    """Either side of the built-in split-row edge (96 tokens at R=8, H=6144,
+    k=10): the automatic workspace's path, the one-row kernel and the
+    oracle agree bit for bit."""
+    m = frn()
+    assert m.split_rows(8, 10, T, 6144) == (T <= 96)
+    inp = workloads.make(8, T, 6144, k=10, shared=True, seed=640 + T)
+    d = to_dev(inp)
+    y, x = gpu_fused(d)
+    y2, x2 = gpu_fused(d, workspace=None)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    assert torch.equal(x.view(torch.int16), x2.view(torch.int16))
+    check(f"split-row edge T={T}", y, x, oracle_ref(inp))
+
+
 def test_auto_workspace_graphs_survive_a_larger_capture():
     """Two graphs captured with the automatic workspace on torch's shared
     capture stream, the second needing a larger buffer: the first graph's

@@ -367,10 +367,9 @@ def moe_finalize_reduce_norm(expert_rows: TensorList, topk_weights: torch.Tensor
                              workspace="auto", stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Per rank r: P_r = bf16(sum_j w[t,j] * E_r[rows[t,j]] (+ shared_r[t])); then
     the epilogue on sum_r P_r.  Returns (out, residual_out).  ``workspace``:
-    "auto" (a buffer cached per device and stream, used where ``split_rows``
-    holds: small T), None
-    (never), or a uint8 GPU tensor of at least ``workspace_bytes(T, H, R, k)``
-    bytes, 256-byte aligned."""
+    "auto" (a buffer kept per device and stream, passed where ``split_rows``
+    holds: small T), None (never), or a uint8 GPU tensor of at least
+    ``workspace_bytes(T, H, R, k)`` bytes, 256-byte aligned."""
     if residual is None:
         raise ValueError("residual is required: this boundary always adds the residual")
     es, sh, T, H, k, num_rows, device = _check_finalize(expert_rows, topk_weights, topk_rows,
