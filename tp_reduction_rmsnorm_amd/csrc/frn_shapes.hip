@@ -206,10 +206,12 @@ bool vec_fits(int vec, int nvec, bool finalize, int epilogue) {
 // The built-in choice of the split-row finalize (a workgroup per (token,
 // rank, 2048-column slice), then the reduction pass) over the one-row
 // finalize, from graph-replay sweeps on MI355X with inputs rotated over
-// 1 GiB.  The one-row kernel waits on one memory round trip per rank (TP
-// routing) or per chunk of live rows (expert-parallel), so at small T its
-// time is nearly flat in T; the split-row finalize writes and re-reads R
-// partial rows per token, so its time grows with T from a lower start.
+// 1 GiB.  With one workgroup per token, all R * (k + 1) rows of a token pass
+// through one CU, whose throughput bounds the one-row kernel at small T
+// (about 37 GB/s per CU at T=16, R=8, k=10), so its time is nearly flat in
+// T; the split-row finalize spreads a token over many workgroups but writes
+// and re-reads R partial rows per token, so its time grows with T from a
+// lower start.
 // Largest T at which the split-row finalize still won:
 //  - TP routing, R <= 2: 32 at H*k >= 32768 (H=7168 k=8: 9.1 against 9.8
 //    us at T=32, 10.0 against 9.9 at T=48); none below (H=4096 k=4 and
