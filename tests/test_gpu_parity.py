@@ -657,3 +657,31 @@ def test_tuner_writes_a_loadable_table(tmp_path):
         assert m.launch_shape(2, 0, 300, 512)[1] == rows[1][1]
     finally:
         m.set_launch_table(None)
+
+
+def test_tuner_runs_and_its_table_drives_calls(tmp_path):
+    """tune.py on one small finalize shape: it times the vec choices and the
+    split-row finalize against the one-row kernel, writes a table that
+    loads, and calls under that table still match the oracle."""
+    import importlib.util
+    import os
+    m = frn()
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    spec = importlib.util.spec_from_file_location(
+        "frn_tune", os.path.join(root, "tp_reduction_rmsnorm_amd", "tune.py"))
+    tune = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(tune)
+    H, R, k, epi = 1024, 4, 3, "rmsnorm"
+    rows = tune.tune_shape(H, R, k, epi, [8, 300], calls=4, dev=DEV, log=log)
+    split = tune.tune_split(H, R, k, epi, [8, 64], calls=4, dev=DEV, log=log)
+    lines = tune.rules_for(H, R, k, epi, rows) + tune.rules_for(H, R, k, epi, split, last="256")
+    try:
+        m.set_launch_table("\n".join(lines))
+        for T, best, _ in split:
+            assert m.split_rows(R, k, T, H) == (best == "split")
+        for T in (8, 64, 300):
+            inp = workloads.make(R, T, H, k=k, shared=True, seed=880 + T)
+            y, x = gpu_fused(to_dev(inp))
+            check(f"tuned table T={T}", y, x, oracle_ref(inp))
+    finally:
+        m.set_launch_table(None)
