@@ -23,8 +23,7 @@
  *   finalize + shared-expert add + all-reduce + residual + RMSNorm.
  *
  * The pages fix FP32 arithmetic and BF16 storage but never write a formula
- * or an operation order.  This file takes one plain order and sticks to it;
- * every reading is listed in the design notes of the repository:
+ * or an operation order.  This file takes one plain order and sticks to it:
  *
  *   finalize   acc = +0; for j = 0..k-1: acc = acc + (w[t,j] * E[idx[t,j],i]);
  *              then acc = acc + S[t,i] when a shared expert is given;
