@@ -14,6 +14,17 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 
+@pytest.fixture(scope="session", autouse=True)
+def built_library():
+    """Build the HIP library once if nothing is built yet (a fresh checkout);
+    a library already in the tree is used as it is."""
+    lib = os.path.join(ROOT, "tp_reduction_rmsnorm_amd", "libfused_reduce_norm.so")
+    if not os.path.exists(lib):
+        import __graft_entry__
+        __graft_entry__.hip_build_module().build()
+    return lib
+
+
 def pytest_runtest_setup(item):
     if item.get_closest_marker("gpu") is not None:
         import torch
