@@ -295,6 +295,10 @@ def test_split_rows_builtin_rule():
         (2, 10, 6144, EP, 8, True), (2, 10, 6144, EP, 9, False),
         (16, 8, 4096, EP, 48, True), (16, 8, 4096, EP, 49, False),
         (8, 8, 2048, EP, 48, True),
+        (16, 8, 7168, False, 96, True), (16, 8, 7168, False, 97, False),
+        (8, 6, 3072, False, 192, True), (8, 6, 3072, False, 193, False),
+        (8, 10, 5120, False, 96, True), (8, 10, 5120, False, 97, False),
+        (16, 6, 3072, EP, 32, True), (16, 6, 3072, EP, 33, False),
     ]
     for R, k, H, ep, T, want in cases:
         assert frn.split_rows(R, k, T, H, ep=ep) is want, (R, k, H, ep, T)

@@ -212,26 +212,31 @@ bool vec_fits(int vec, int nvec, bool finalize, int epilogue) {
 // T; the split-row finalize spreads a token over many workgroups but writes
 // and re-reads R partial rows per token, so its time grows with T from a
 // lower start.
-// Largest T at which the split-row finalize still won:
+// Largest T at which the split-row finalize still won (25 shapes):
 //  - TP routing, R <= 2: 32 at H*k >= 32768 (H=7168 k=8: 9.1 against 9.8
-//    us at T=32, 10.0 against 9.9 at T=48); none below (H=4096 k=4 and
-//    H=2048 k=8 are within 5% either way);
-//  - TP routing, R >= 3: 96 (H=6144 R=8 k=10: 28.1 against 33.0 us at
-//    T=96, 35.9 against 33.2 at T=128; the same at H=5120 R=4, H=7168 R=8,
-//    H=8192 R=4 and H=16384 R=8); 128 at R=16 (H=4096); 192 at H <= 2048;
-//  - expert-parallel routing, where the one-row kernel loads several
-//    ranks' rows at once: 8 at R <= 2, 16 at R <= 8 (H=6144 R=8 k=10:
-//    9.8 against 10.9 us at T=16, 11.0 each at T=32, 13.8 against 11.2 at
-//    T=64), 48 at R=16 or H <= 2048.
+//    us at T=32, 10.0 against 9.9 at T=48; H=5120 k=16 the same); none
+//    below (H=4096 k=4 and H=2048 k=8 are within 5% either way);
+//  - TP routing, 3 <= R <= 8: 96 at H > 4096 (H=6144 R=8 k=10: 28.1 against
+//    33.0 us at T=96, 35.9 against 33.2 at T=128; the same at H=5120 R=4,
+//    H=7168 R=8, H=8192 R=4 and H=16384 R=8); 192 at H <= 4096 (H=4096 R=8
+//    k=8: 25.9 against 26.9 us at T=192; H=3072 R=8, H=2048 R=4 and R=8);
+//  - TP routing, R=16: 128 at H <= 4096, 96 above (H=7168: 66.9 against
+//    57.4 us at T=128);
+//  - expert-parallel routing, where the one-row kernel already keeps
+//    several ranks' rows in flight: 8 at R <= 2, 16 at R <= 8 (H=6144 R=8
+//    k=10: 9.8 against 10.9 us at T=16, 11.0 each at T=32, 13.8 against
+//    11.2 at T=64), 48 at H <= 2048, and at R=16 48 for k >= 8 and 32 below
+//    (H=3072 k=6: 11.6 against 10.7 us at T=48).
 int64_t builtin_split_max_t(int32_t R, int64_t H, int32_t k, bool ep) {
     if (ep) {
         if (R <= 2) return 8;
-        if (R >= 16 || H <= 2048) return 48;
+        if (H <= 2048) return 48;
+        if (R >= 16) return k >= 8 ? 48 : 32;
         return 16;
     }
     if (R <= 2) return H * k >= 32768 ? 32 : 0;
-    if (H <= 2048) return 192;
-    return R >= 16 ? 128 : 96;
+    if (R >= 16) return H <= 4096 ? 128 : 96;
+    return H <= 4096 ? 192 : 96;
 }
 
 bool matches(const Rule& r, int64_t H, int64_t R, int64_t k, int64_t epilogue, int64_t ep) {
