@@ -309,6 +309,26 @@ def test_split_rows_builtin_rule():
     assert not frn.split_rows(8, 10, 8, 6144, frn.EPI_SUM)   # split pass 1 has no workspace
 
 
+def test_split_rows_is_covered_by_workspace_bytes(lib):
+    """Over a grid of shapes and both routings: the calls that take the
+    split-row finalize form a prefix of T, and frn_workspace_bytes for a
+    larger max_T covers every one of them."""
+    import tp_reduction_rmsnorm_amd as frn
+    frn.set_launch_table(None)
+    for R in (1, 2, 3, 4, 8, 9, 16):
+        for H in (8, 520, 2048, 2056, 4096, 6144, 16384):
+            for k in (1, 4, 8, 16):
+                cap_bytes = lib.frn_workspace_bytes(100000, H, R, k)
+                for ep in (False, True):
+                    seen_fused = False
+                    for T in list(range(1, 200, 7)) + [256, 257, 1000]:
+                        split = frn.split_rows(R, k, T, H, ep=ep)
+                        assert not (split and seen_fused), (R, H, k, ep, T)
+                        seen_fused |= not split
+                        if split:
+                            assert T * R * H * 2 <= cap_bytes, (R, H, k, ep, T)
+
+
 def test_launch_table_split_and_fused_rules(lib):
     """split / fused rules override the built-in choice, leave the vec
     rules alone, never split above 256 tokens, and widen the workspace size
