@@ -214,8 +214,9 @@ def main():
     shapes = ([(int(h), int(r), int(k), e) for h, r, k, e in args.shape] if args.shape
               else DEFAULT_SHAPES)
     dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(dev)
     lines = ["# fused_reduce_norm launch table: H R k epilogue Tmin Tmax vec",
-             f"# measured on {torch.cuda.get_device_name(dev)} ({torch.cuda.get_device_properties(dev).gcnArchName.split(':')[0]})"
+             f"# measured on a {props.gcnArchName.split(':')[0]} GPU with {props.multi_processor_count} CUs"
              f" with: python tp_reduction_rmsnorm_amd/tune.py {' '.join(sys.argv[1:])}",
              f"# graph replay of {args.calls} calls, median of 5.  Load with FRN_LAUNCH_TABLE=<file>."]
     for H, R, k, epi in shapes:
