@@ -262,21 +262,26 @@ frn_status frn_ep_moe_finalize(const void* const* expert_rows, const void* const
 frn_status frn_query(int32_t R, int32_t k, int64_t T, int64_t H, int32_t epilogue);
 
 /*
- * Tuned launch shapes.  Each call launches one workgroup per token row
- * whose lanes own 1, 2 or 4 vectors of 8 BF16 values ("vec"); the best vec
- * depends on H, R, k, the epilogue and T, and shapes tuned for one hidden
- * size do not carry over to another (SGLang PR #34134: the shipped H=8192
- * profiles misfit H=6144).  A built-in rule, measured on MI355X, applies
- * unless a table of tuned rules overrides it.  Table text: one rule per
- * line, '#' starts a comment:
+ * Tuned launch shapes.  A call launches either one workgroup per token row
+ * (the one-row kernel) or, without finalize, one workgroup per compute
+ * unit that walks the rows with the next row's loads in flight (the
+ * row-pipelined kernel, see frn_launch_pipelined); the lanes own 1, 2 or 4
+ * vectors of 8 BF16 values ("vec").  The best choice depends on H, R, k,
+ * the epilogue and T, and shapes tuned for one hidden size do not carry
+ * over to another (SGLang PR #34134: the shipped H=8192 profiles misfit
+ * H=6144).  A built-in rule, measured on MI355X, applies unless a table of
+ * tuned rules overrides it.  Table text: one rule per line, '#' starts a
+ * comment:
  *     H  R  k  epilogue  Tmin  Tmax  vec
  * H, R, k, Tmin, Tmax: integers or '*' (any); k = 0 means no finalize;
  * epilogue: rmsnorm | sandwich | sum (split pass 1) for calls without
  * expert-parallel routing, ep-rmsnorm | ep-sandwich | ep-* for
- * frn_ep_moe_finalize_reduce_norm, or * (every call); vec: 1 | 2 | 4, or
- * split | fused.  A numeric vec sets the one-row kernel's shape: the first
- * such rule that matches a call and fits it (at most 1024 lanes; vec 4
- * only without finalize and outside split pass 1) decides.  split / fused
+ * frn_ep_moe_finalize_reduce_norm, or * (every call); vec: 1 | 2 | 4,
+ * p1 | p2, or split | fused.  A numeric vec sets the one-row kernel's
+ * shape, p1 / p2 the row-pipelined kernel with 1 / 2 vectors per lane: the
+ * first such rule that matches a call and fits it decides (one-row kernel:
+ * at most 1024 lanes, vec 4 only without finalize and outside split pass 1;
+ * row-pipelined kernel: see frn_launch_pipelined).  split / fused
  * decide, for a finalize call (k >= 1) given a large enough workspace,
  * whether it takes the split-row finalize (see frn_workspace_bytes) or the
  * one-row kernel: the first such rule that matches decides, and T above 256
@@ -290,8 +295,9 @@ frn_status frn_query(int32_t R, int32_t k, int64_t T, int64_t H, int32_t epilogu
  */
 frn_status frn_set_launch_table(const char* text);
 
-/* The shape (lanes per workgroup, vectors per lane) the one-row kernel gets
- * for a call of these sizes, without launching.  epilogue: FRN_EPI_RMSNORM,
+/* The shape (lanes per workgroup, vectors per lane) a call of these sizes
+ * gets, without launching: that of the row-pipelined kernel where the call
+ * takes it (frn_launch_pipelined), else that of the one-row kernel.  epilogue: FRN_EPI_RMSNORM,
  * FRN_EPI_SANDWICH or 2 (split pass 1), OR'ed with FRN_SHAPE_EP for a call
  * of frn_ep_moe_finalize_reduce_norm (k >= 1).  threads, vectors: host
  * pointers to receive the values. */
@@ -333,6 +339,25 @@ size_t frn_workspace_bytes(int64_t max_T, int64_t H, int32_t R, int32_t k);
  * launch-table split / fused rules override it.
  */
 int32_t frn_split_rows(int32_t R, int32_t k, int64_t T, int64_t H, int32_t epilogue);
+
+/*
+ * 1 if a call of these sizes without finalize (k = 0; epilogue
+ * FRN_EPI_RMSNORM or FRN_EPI_SANDWICH) runs the row-pipelined kernel, else
+ * 0 (also for k > 0, split pass 1 and sizes outside what the library
+ * serves).  That kernel launches one workgroup per compute unit; each walks
+ * the rows b, b + G, b + 2G, ... with the gamma rows held in LDS and the
+ * next row's residual and partials in flight during the current row's
+ * epilogue, so a CU keeps reading while it writes (with one row per
+ * workgroup, the reads of all resident rows come first and the writes
+ * after).  It serves 1 <= R <= 4, H/8 a multiple of 64 * vec (at most 1024
+ * lanes with one vector per lane, 512 with two) and gamma rows of at most
+ * 64 KiB.  The built-in rule, measured on MI355X, takes it with two
+ * vectors per lane from T = 1536 for 4096 < H < 8192 (where it measured
+ * faster or even); launch-table p1 / p2 rules and numeric vec rules
+ * override it.  Results are bit-identical either
+ * way: the same arithmetic in the same order, row by row.
+ */
+int32_t frn_launch_pipelined(int32_t R, int32_t k, int64_t T, int64_t H, int32_t epilogue);
 
 /* Static text for a status code. */
 const char* frn_status_string(frn_status s);

@@ -490,6 +490,57 @@ def test_launch_shape_builtin_rule():
         frn.launch_shape(8, 10, 1024, 6144, frn.EPI_SUM, ep=True)
 
 
+def test_pipelined_builtin_rule():
+    """Calls without finalize take the row-pipelined kernel (one workgroup
+    per CU walking the rows) from T = 1536 where it serves them."""
+    import tp_reduction_rmsnorm_amd as frn
+    frn.set_launch_table(None)
+    S, N = frn.EPI_SANDWICH, frn.EPI_RMSNORM
+    assert frn.launch_pipelined(4, 0, 4096, 5120, S)
+    assert frn.launch_shape(4, 0, 4096, 5120, S) == (320, 2)
+    assert frn.launch_pipelined(4, 0, 1536, 5120, S)
+    assert not frn.launch_pipelined(4, 0, 1535, 5120, S)       # below the measured crossover
+    assert frn.launch_shape(4, 0, 1535, 5120, S) == (320, 2)   # one-row kernel, two vectors
+    assert frn.launch_pipelined(1, 0, 16384, 7168, N)          # split pass 2
+    assert frn.launch_shape(1, 0, 16384, 7168, N) == (448, 2)
+    assert frn.launch_pipelined(3, 0, 2048, 6144, S)           # 768 vectors, R = 3
+    assert frn.launch_shape(3, 0, 2048, 6144, S) == (384, 2)
+    assert not frn.launch_pipelined(4, 0, 4096, 8192, S)       # 1024 vectors: one row per group
+    assert not frn.launch_pipelined(2, 0, 4096, 4096, N)       # 512 vectors: the same
+    assert not frn.launch_pipelined(8, 0, 4096, 8192, S)       # R > 4
+    assert not frn.launch_pipelined(4, 10, 4096, 6144, N)      # finalize
+    assert not frn.launch_pipelined(4, 0, 4096, 5128, S)       # 641 vectors: idle lanes
+    assert not frn.launch_pipelined(2, 0, 4096, 16384, N)      # more lanes than it takes
+    assert not frn.launch_pipelined(4, 0, 4096, 5120, frn.EPI_SUM)   # split pass 1
+    assert not frn.launch_pipelined(0, 0, 4096, 5120, S)       # malformed sizes: no
+    assert not frn.launch_pipelined(4, 0, 4096, 5124, S)
+
+
+def test_launch_table_pipelined_rules():
+    import tp_reduction_rmsnorm_amd as frn
+    S, N = frn.EPI_SANDWICH, frn.EPI_RMSNORM
+    try:
+        frn.set_launch_table("5120 4 0 sandwich 0 * p1\n")
+        assert frn.launch_pipelined(4, 0, 8, 5120, S)
+        assert frn.launch_shape(4, 0, 8, 5120, S) == (640, 1)
+        frn.set_launch_table("5120 4 0 sandwich 0 * 4\n")        # a numeric rule: one row
+        assert not frn.launch_pipelined(4, 0, 4096, 5120, S)
+        assert frn.launch_shape(4, 0, 4096, 5120, S) == (192, 4)
+        frn.set_launch_table("* * * * 0 * p2\n")
+        assert frn.launch_pipelined(2, 0, 8, 1024, N)              # 128 vectors: 64 lanes
+        assert frn.launch_shape(2, 0, 8, 1024, N) == (64, 2)
+        assert not frn.launch_pipelined(8, 0, 4096, 8192, S)       # does not fit: built-in
+        assert frn.launch_shape(8, 0, 4096, 8192, S) == (256, 4)
+        assert not frn.launch_pipelined(2, 0, 8, 520, N)           # 65 vectors: skipped
+        assert not frn.launch_pipelined(4, 10, 8, 6144, N)         # finalize: skipped
+        for bad in ("5120 4 0 sandwich 0 * p3\n", "5120 4 0 sandwich 0 * p\n",
+                    "5120 4 0 sandwich 0 * P2\n"):
+            with pytest.raises(ValueError):
+                frn.set_launch_table(bad)
+    finally:
+        frn.set_launch_table(None)
+
+
 def test_launch_table_expert_parallel_rules():
     import tp_reduction_rmsnorm_amd as frn
     try:
@@ -571,11 +622,26 @@ def test_tuner_merges_rules():
     split = [(1, "split", {}), (16, "split", {}), (32, "fused", {}), (256, "fused", {})]
     lines = tune.rules_for(6144, 8, 10, "ep-rmsnorm", split, last="256")
     assert lines == ["6144 8 10 ep-rmsnorm 0 16 split", "6144 8 10 ep-rmsnorm 17 256 fused"]
+    rows = [(1024, "4", {}), (2048, "p2", {}), (4096, "p2", {})]
+    piped = tune.rules_for(5120, 4, 0, "sandwich", rows)
+    assert piped == ["5120 4 0 sandwich 0 1024 4", "5120 4 0 sandwich 1025 * p2"]
     import tp_reduction_rmsnorm_amd as frn
     try:
         frn.set_launch_table("\n".join(lines))   # the tuner's output parses
         assert frn.split_rows(8, 10, 16, 6144, ep=True)
         assert not frn.split_rows(8, 10, 17, 6144, ep=True)
+        frn.set_launch_table("\n".join(piped))
+        assert frn.launch_pipelined(4, 0, 1025, 5120, frn.EPI_SANDWICH)
+        assert not frn.launch_pipelined(4, 0, 1024, 5120, frn.EPI_SANDWICH)
+        # what the tuner times is what a call of that size takes under the rule
+        for choice, ok in (("1", True), ("4", True), ("p1", True), ("p2", True)):
+            frn.set_launch_table(f"5120 4 0 sandwich 4096 4096 {choice}")
+            assert tune.fits(5120, 4, 0, "sandwich", 4096, choice) == ok
+        for choice in ("p1", "p2"):                 # R = 8 or a finalize: not served
+            frn.set_launch_table(f"* * * * 0 * {choice}")
+            assert not tune.fits(8192, 8, 0, "sandwich", 4096, choice)
+            assert not tune.fits(6144, 8, 10, "rmsnorm", 4096, choice)
+            assert not tune.fits(6144, 8, 10, "ep-rmsnorm", 4096, choice)
     finally:
         frn.set_launch_table(None)
 

@@ -654,7 +654,9 @@ def test_tuner_writes_a_loadable_table(tmp_path):
     m = frn()
     try:
         m.set_launch_table(text)
-        assert m.launch_shape(2, 0, 300, 512)[1] == rows[1][1]
+        best = rows[1][1]  # a rule value: '1', '2', '4', 'p1' or 'p2'
+        assert m.launch_shape(2, 0, 300, 512)[1] == int(best[-1])
+        assert m.launch_pipelined(2, 0, 300, 512) == best.startswith("p")
     finally:
         m.set_launch_table(None)
 

@@ -87,3 +87,26 @@ def test_streamed_rows_use_non_temporal_accesses():
     dis = _disassembly()
     assert re.search(r"global_load_dwordx4 .* nt\b", dis), "no non-temporal row loads"
     assert re.search(r"global_store_dwordx4 .* nt\b", dis), "no non-temporal row stores"
+
+
+def _function(dis, symbol):
+    """The disassembly of one kernel (from its label to the next label)."""
+    m = re.search(rf"^[0-9a-f]+ <{re.escape(symbol)}>:\n(.*?)(?=^[0-9a-f]+ <|\Z)", dis, re.M | re.S)
+    assert m, f"{symbol} not found"
+    return m.group(1)
+
+
+def test_pipelined_kernel_keeps_the_next_row_in_flight():
+    """rows_pipelined_kernel (sandwich, two vectors per lane, R = 4): the
+    gamma rows go to LDS by direct global->LDS loads; the only full wait on
+    the vector memory counter is the one before the first barrier (those
+    copies must have landed); in the row loop the partials are consumed
+    with the row's four output stores still in flight (vmcnt(4)), so no
+    wait covers the stores, and the epilogue never waits on the next row's
+    loads (no lane predicate hides a memory access from the count)."""
+    f = _function(_disassembly(), "_ZN3frn12_GLOBAL__N_121rows_pipelined_kernelILi1ELi2ELi4EEEvNS_7RowArgsE")
+    assert "global_load_lds_dwordx4" in f
+    assert len(re.findall(r"s_waitcnt vmcnt\(0\)", f)) == 1
+    assert re.search(r"s_waitcnt vmcnt\(4\)", f)
+    first_barrier = f.index("s_barrier")
+    assert f.index("vmcnt(0)") < first_barrier

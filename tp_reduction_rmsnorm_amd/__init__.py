@@ -20,8 +20,9 @@ Function names are the C entry points without their ``frn_`` prefix:
                                  expert-parallel routing (each rank owns
                                  some experts; per-rank row indices)
 * ``query``, ``workspace_bytes``, ``version``
-* ``set_launch_table``, ``launch_shape``, ``split_rows``  tuned launch
-                                 shapes and the split-row finalize choice
+* ``set_launch_table``, ``launch_shape``, ``split_rows``,
+  ``launch_pipelined``           tuned launch shapes, the split-row finalize
+                                 choice and the row-pipelined kernel choice
                                  (tune.py)
 * ``boundary``                   fused or split by a token threshold (a
                                  Python-side policy over the calls above)
@@ -110,6 +111,7 @@ _c_shape = _sig("frn_launch_shape", ctypes.c_int,
                 [_I32, _I32, _I64, _I64, _I32, ctypes.POINTER(_I32), ctypes.POINTER(_I32)])
 _c_ws = _sig("frn_workspace_bytes", _SZ, [_I64, _I64, _I32, _I32])
 _c_split_rows = _sig("frn_split_rows", _I32, [_I32, _I32, _I64, _I64, _I32])
+_c_pipelined = _sig("frn_launch_pipelined", _I32, [_I32, _I32, _I64, _I64, _I32])
 _c_status = _sig("frn_status_string", ctypes.c_char_p, [ctypes.c_int])
 _c_last = _sig("frn_last_error", ctypes.c_char_p, [])
 _c_version = _sig("frn_version", ctypes.c_char_p, [])
@@ -119,8 +121,8 @@ C_FUNCTIONS = ("frn_reduce_residual_rmsnorm", "frn_reduce_sandwich_norm",
                "frn_moe_finalize_reduce_bf16", "frn_split_reduce_norm", "frn_moe_finalize",
                "frn_ep_moe_finalize_reduce_norm", "frn_ep_moe_finalize",
                "frn_query", "frn_set_launch_table", "frn_launch_shape",
-               "frn_workspace_bytes", "frn_split_rows", "frn_status_string", "frn_last_error",
-               "frn_version")
+               "frn_workspace_bytes", "frn_split_rows", "frn_launch_pipelined",
+               "frn_status_string", "frn_last_error", "frn_version")
 
 
 def version() -> str:
@@ -162,8 +164,10 @@ def set_launch_table(text: Optional[str]) -> None:
 
 def launch_shape(R: int, k: int, T: int, H: int, epilogue: int = EPI_RMSNORM, *,
                  ep: bool = False):
-    """(lanes per workgroup, vectors per lane) the one-row kernel would use;
-    ``ep=True`` for an ``ep_moe_finalize_reduce_norm`` call."""
+    """(lanes per workgroup, vectors per lane) the call would use -- of the
+    row-pipelined kernel where it takes that (``launch_pipelined``), else of
+    the one-row kernel; ``ep=True`` for an ``ep_moe_finalize_reduce_norm``
+    call."""
     th, v = _I32(), _I32()
     _check(_c_shape(R, k, T, H, epilogue | (SHAPE_EP if ep else 0), ctypes.byref(th),
                     ctypes.byref(v)))
@@ -175,6 +179,14 @@ def split_rows(R: int, k: int, T: int, H: int, epilogue: int = EPI_RMSNORM, *,
     """True if a finalize call of these sizes that is given a large enough
     workspace takes the split-row finalize (no launch)."""
     return bool(_c_split_rows(R, k, T, H, epilogue | (SHAPE_EP if ep else 0)))
+
+
+def launch_pipelined(R: int, k: int, T: int, H: int, epilogue: int = EPI_RMSNORM) -> bool:
+    """True if a call of these sizes (no finalize) runs the row-pipelined
+    kernel -- one workgroup per compute unit walking the rows, the next
+    row's loads in flight during the current row's epilogue -- rather than
+    one workgroup per row (no launch)."""
+    return bool(_c_pipelined(R, k, T, H, epilogue))
 
 
 # ---------------------------------------------------------------- helpers --- #

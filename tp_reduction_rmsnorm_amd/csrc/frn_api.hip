@@ -507,6 +507,16 @@ FRN_API int32_t frn_split_rows(int32_t R, int32_t k, int64_t T, int64_t H, int32
     return frn::use_split_rows(R, H, k, ep, epilogue, T) ? 1 : 0;
 }
 
+FRN_API int32_t frn_launch_pipelined(int32_t R, int32_t k, int64_t T, int64_t H,
+                                     int32_t epilogue) {
+    if (k != 0 || (epilogue != FRN_EPI_RMSNORM && epilogue != FRN_EPI_SANDWICH)) return 0;
+    if (R < 1 || R > FRN_MAX_R || H < 8 || H > FRN_MAX_H || H % 8 != 0 || T < 1 ||
+        T > FRN_MAX_T)
+        return 0;
+    return frn::choose_shape((int)(H / 8), frn::kNoFinalize, T, epilogue, R, 0).pipelined ? 1
+                                                                                         : 0;
+}
+
 FRN_API const char* frn_status_string(frn_status s) {
     switch (s) {
         case FRN_OK: return "FRN_OK";

@@ -70,12 +70,18 @@ int64_t split_rows_cap(int32_t R, int64_t H, int32_t k);
 // Column slices of one row in the split-row finalize.
 int split_slices(int nvec);
 
-// Launch shape of one call: one token row per workgroup, `threads` lanes
-// per row, each lane owning `vec` 16-byte vectors of the row.
+// Launch shape of one call: `threads` lanes per row, each lane owning `vec`
+// 16-byte vectors of the row.  pipelined = false: row_kernel, one token row
+// per workgroup; true: rows_pipelined_kernel, one workgroup per compute
+// unit walking rows (threads * vec == H / 8 exactly).
 struct LaunchShape {
     int threads;
     int vec;
+    bool pipelined;
 };
+
+// Compute units of the current device (queried once per device).
+int64_t compute_units();
 
 // Finalize kind of a call: none, TP routing, or expert-parallel routing.
 enum FinKind { kNoFinalize = 0, kTpFinalize = 1, kEpFinalize = 2 };

@@ -1,7 +1,8 @@
 // frn_kernels.hip -- gfx950 kernels of the fused reduce + norm boundary.
 //
-// Two kernels (row_kernel and finalize_slices_kernel, each in several
-// instantiations) share the per-row building blocks below.
+// Three kernels (row_kernel, rows_pipelined_kernel and
+// finalize_slices_kernel, each in several instantiations) share the per-row
+// building blocks below.
 //
 // row_kernel: one token row per workgroup.  Each lane owns V 16-byte vectors
 // of the row (8 BF16 values each), placed `threads` vectors apart so every
@@ -10,6 +11,12 @@
 // (expert-parallel routing) of the token's live rows across ranks -- before
 // it consumes any of them, keeps the FP32 row slice in registers through the
 // epilogue, and writes each output exactly once.
+//
+// rows_pipelined_kernel: for calls without finalize at large T.  One
+// workgroup per compute unit walks rows b, b + G, b + 2G, ...; the gamma
+// rows sit in LDS for the workgroup's lifetime, and the next row's residual
+// and partials are in flight while the current row runs its epilogue, so
+// every CU keeps reading while it writes.
 //
 // finalize_slices_kernel: for the MoE finalize at small T, where one
 // workgroup per token would walk the R ranks one memory round trip after
@@ -652,6 +659,180 @@ __global__ __launch_bounds__(kSplitThreads) void finalize_slices_kernel(const Ro
     if (L.ok[0]) a.part_out[r][t * a.nvec + L.vi[0]] = narrow(acc[0]);
 }
 
+// Gamma rows staged in LDS (rows_pipelined_kernel): FP32 vectors in the
+// LDS address space, so the reads are ds_read and never wait on the vector
+// memory counter that the in-flight row loads hold.
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) f32x4_t lds_f32x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ __forceinline__ void load_gamma(const lds_f32x4_t* g, int v, float (&out)[8]) {
+    const f32x4_t a = g[2 * v];
+    const f32x4_t b = g[2 * v + 1];
+    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+    out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+}
+
+// The residual and the R partial rows of one token: the residual loads go
+// out first (the compiler barrier keeps them ahead of the partials, so a
+// wait for the partials covers them too).
+template <int V, int R>
+__device__ __forceinline__ void issue_row(const RowArgs& a, int64_t row, const Lanes<V>& L,
+                                          uint4 (&xr)[V], uint4 (&q)[R][V]) {
+    load_residual<V>(a, row, L, xr);
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int j = 0; j < V; ++j) q[r][j] = ld_stream(a.src[r] + row + L.vi[j]);
+}
+
+// s = P_0 + P_1 + ... + P_{R-1} (FP32, rank order), consuming each rank's
+// loads as they land.
+template <int V, int R>
+__device__ __forceinline__ void sum_ranks(const uint4 (&q)[R][V], float (&s)[V][8]) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int j = 0; j < V; ++j) {
+            float f[8];
+            widen(q[r][j], f);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) s[j][i] = (r == 0) ? f[i] : s[j][i] + f[i];
+        }
+}
+
+// The epilogue of `epilogue` with the gamma rows read from LDS.  Same
+// arithmetic, in the same order.
+template <int EPI, int V>
+__device__ __forceinline__ void epilogue_lds(const RowArgs& a, int64_t row, const Lanes<V>& L,
+                                             float (&s)[V][8], const uint4 (&xr)[V],
+                                             double (&slots)[2][16], const lds_f32x4_t* gamma1,
+                                             const lds_f32x4_t* gamma2) {
+    const float eps = a.eps;
+    const int H = a.H;
+    if constexpr (EPI == kSandwich) {
+        const float r1 = inv_rms(block_sum(sum_squares<V>(s, L), slots[0]), H, eps);
+#pragma unroll
+        for (int j = 0; j < V; ++j) {
+            float g[8], x[8];
+            load_gamma(gamma1, L.vi[j], g);
+            widen(xr[j], x);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float n = s[j][i] * r1;
+                const float av = n * g[i];
+                s[j][i] = av + x[i];
+            }
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < V; ++j) {
+            float x[8];
+            widen(xr[j], x);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) s[j][i] = s[j][i] + x[i];
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < V; ++j) st_stream(a.residual_out + row + L.vi[j], narrow(s[j]));
+    const float r2 = inv_rms(block_sum(sum_squares<V>(s, L), slots[1]), H, eps);
+    const lds_f32x4_t* g2 = (EPI == kSandwich) ? gamma2 : gamma1;
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+        float g[8], y[8];
+        load_gamma(g2, L.vi[j], g);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float n = s[j][i] * r2;
+            y[i] = n * g[i];
+        }
+        st_stream(a.out + row + L.vi[j], narrow(y));
+    }
+}
+
+// Row-pipelined boundary kernel: workgroup b takes rows b, b + G, b + 2G,
+// ... (G = gridDim.x, one workgroup per CU).  The gamma rows are copied to
+// LDS once, straight from global memory (global_load_lds, no registers),
+// and the next row's loads are issued before the current row's epilogue.
+// The launch guarantees blockDim.x * V == nvec (no tail lanes, so no lane
+// predicate hides a load or store from the compiler's wait counting), R
+// ranks exactly, and gridDim.x <= T.  Dynamic LDS: 16 * 2 * nvec bytes per
+// gamma row.
+template <int EPI, int V, int R>
+__global__ __launch_bounds__(V == 1 ? 1024 : 512) void rows_pipelined_kernel(const RowArgs a) {
+    extern __shared__ f32x4_t gamma_lds_raw[];
+    __shared__ double slots[2][16];
+    lds_f32x4_t* gamma_lds = (lds_f32x4_t*)gamma_lds_raw;
+    const int nvec = a.nvec;
+    const int n4 = 2 * nvec;  // FP32 vectors per gamma row (a multiple of 64)
+    Lanes<V> L(nvec);
+#pragma unroll
+    for (int j = 0; j < V; ++j) L.ok[j] = true;  // no tail lanes (see above)
+    {
+        const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, nw = blockDim.x >> 6;
+        for (int base = w * 64; base < n4; base += nw * 64) {
+            __builtin_amdgcn_global_load_lds((const void*)(a.gamma1 + base + lane),
+                                             (lds_void_t*)(gamma_lds + base), 16, 0, 0);
+            if constexpr (EPI == kSandwich)
+                __builtin_amdgcn_global_load_lds((const void*)(a.gamma2 + base + lane),
+                                                 (lds_void_t*)(gamma_lds + n4 + base), 16, 0,
+                                                 0);
+        }
+    }
+    int64_t t = blockIdx.x;
+    uint4 xr[V];
+    uint4 q[R][V];
+    issue_row<V, R>(a, t * nvec, L, xr, q);
+    float s[V][8];
+    sum_ranks<V, R>(q, s);
+    // Make the first row's residual land here too: otherwise the loop's
+    // epilogue would carry a wait for it into every later row.
+#pragma unroll
+    for (int j = 0; j < V; ++j)
+        asm volatile("" ::"v"(xr[j].x), "v"(xr[j].y), "v"(xr[j].z), "v"(xr[j].w));
+    __syncthreads();  // the gamma rows are in LDS (the compiler waits for the copies here)
+    for (;;) {
+        const int64_t tn = t + gridDim.x;
+        const bool more = tn < a.T;
+        uint4 xn[V];
+        if (more) issue_row<V, R>(a, tn * nvec, L, xn, q);
+        epilogue_lds<EPI, V>(a, t * nvec, L, s, xr, slots, gamma_lds, gamma_lds + n4);
+        if (!more) break;
+        sum_ranks<V, R>(q, s);
+        for (int j = 0; j < V; ++j) xr[j] = xn[j];
+        t = tn;
+    }
+}
+
+template <int EPI, int V, int R>
+hipError_t launch_pipelined(const RowArgs& a, int threads, int64_t groups, hipStream_t stream) {
+    const size_t lds = (size_t)(EPI == kSandwich ? 2 : 1) * 2 * a.nvec * 16;
+    hipLaunchKernelGGL((rows_pipelined_kernel<EPI, V, R>), dim3((unsigned)groups),
+                       dim3(threads), lds, stream, a);
+    return hipGetLastError();
+}
+
+template <int EPI, int V>
+hipError_t launch_pipelined_r(const RowArgs& a, int threads, int64_t groups,
+                              hipStream_t stream) {
+    switch (a.R) {
+        case 1: return launch_pipelined<EPI, V, 1>(a, threads, groups, stream);
+        case 2: return launch_pipelined<EPI, V, 2>(a, threads, groups, stream);
+        case 3: return launch_pipelined<EPI, V, 3>(a, threads, groups, stream);
+        case 4: return launch_pipelined<EPI, V, 4>(a, threads, groups, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int EPI>
+hipError_t launch_pipelined_v(const RowArgs& a, int64_t T, LaunchShape sh, hipStream_t stream) {
+    const int64_t cus = compute_units();
+    const int64_t groups = T < cus ? T : cus;
+    if (sh.vec == 1) return launch_pipelined_r<EPI, 1>(a, sh.threads, groups, stream);
+    return launch_pipelined_r<EPI, 2>(a, sh.threads, groups, stream);
+}
+
 template <int EPI, int FIN, int V, int C>
 hipError_t launch(const RowArgs& a, int64_t T, int threads, hipStream_t stream) {
     hipLaunchKernelGGL((row_kernel<EPI, FIN, V, C>), dim3((unsigned)T), dim3(threads), 0,
@@ -737,6 +918,10 @@ hipError_t launch_rows(const RowArgs& a_in, int epilogue, int64_t T, hipStream_t
     }
     const int fin = a.k == 0 ? kNoFinalize : (a.ep ? kEpFinalize : kTpFinalize);
     const LaunchShape sh = choose_shape(a.nvec, fin, T, epilogue, a.R, a.k);
+    if (sh.pipelined) {
+        if (epilogue == kSandwich) return launch_pipelined_v<kSandwich>(a, T, sh, stream);
+        return launch_pipelined_v<kRmsNorm>(a, T, sh, stream);
+    }
     switch (epilogue) {
         case kRmsNorm: return launch_fin<kRmsNorm>(a, T, sh, stream);
         case kSandwich: return launch_fin<kSandwich>(a, T, sh, stream);

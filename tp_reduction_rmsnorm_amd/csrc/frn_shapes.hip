@@ -8,6 +8,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -19,13 +20,14 @@ namespace {
 
 // One tuned rule; -1 in H, R, k, epilogue, ep means "any".  T in [tmin,
 // tmax].  ep: 1 for calls with expert-parallel routing, 0 for the others.
-// vec 1, 2 or 4: vectors per lane of row_kernel; kSplitRule / kFusedRule:
-// a finalize call given a workspace takes the split-row / the one-row
-// finalize.
+// vec 1, 2 or 4: vectors per lane of row_kernel, or with pipe set, of
+// rows_pipelined_kernel (1 or 2); kSplitRule / kFusedRule: a finalize call
+// given a workspace takes the split-row / the one-row finalize.
 struct Rule {
     int64_t H, R, k, epilogue, ep;
     int64_t tmin, tmax;
     int vec;
+    bool pipe;
 };
 
 constexpr int kSplitRule = -1;
@@ -101,6 +103,8 @@ bool parse(const char* text, std::vector<Rule>& out, std::string& err) {
             tok.size() == 7 &&
             (tok[6] == "split"   ? (vec = kSplitRule, true)
              : tok[6] == "fused" ? (vec = kFusedRule, true)
+             : tok[6] == "p1"    ? (vec = 1, r.pipe = true, true)
+             : tok[6] == "p2"    ? (vec = 2, r.pipe = true, true)
                                  : parse_field(tok[6].c_str(), &vec) &&
                                        (vec == 1 || vec == 2 || vec == 4));
         if (!last_ok || !parse_field(tok[0].c_str(), &r.H) ||
@@ -109,7 +113,7 @@ bool parse(const char* text, std::vector<Rule>& out, std::string& err) {
             !parse_field(tok[4].c_str(), &r.tmin) || !parse_field(tok[5].c_str(), &r.tmax)) {
             err = "launch table line " + std::to_string(lineno) +
                   ": expected 'H R k epilogue Tmin Tmax vec' (numbers or *, epilogue "
-                  "rmsnorm|sandwich|sum|ep-rmsnorm|ep-sandwich|ep-*|*, vec 1|2|4|split|fused)";
+                  "rmsnorm|sandwich|sum|ep-rmsnorm|ep-sandwich|ep-*|*, vec 1|2|4|p1|p2|split|fused)";
             return false;
         }
         if (r.tmin < 0) r.tmin = 0;
@@ -203,6 +207,43 @@ bool vec_fits(int vec, int nvec, bool finalize, int epilogue) {
     return true;
 }
 
+// Whether rows_pipelined_kernel serves a call with `vec` vectors per lane:
+// no finalize, the residual + RMSNorm or sandwich epilogue, 1 <= R <= 4
+// (the next row's loads stay in registers), rows that split into whole
+// waves (H/8 a multiple of 64 * vec, so no lane is idle), at most 1024
+// lanes with one vector and 512 with two (the register budget of two), and
+// gamma rows that fit in 64 KiB of LDS.
+bool pipe_fits(int vec, int nvec, int fin, int epilogue, int R) {
+    if (fin != kNoFinalize || (epilogue != kRmsNorm && epilogue != kSandwich)) return false;
+    if (R < 1 || R > 4 || (vec != 1 && vec != 2)) return false;
+    if (nvec % (64 * vec) != 0 || nvec / vec > (vec == 1 ? 1024 : 512)) return false;
+    const int64_t gamma_bytes = (int64_t)(epilogue == kSandwich ? 2 : 1) * nvec * 32;
+    return gamma_bytes <= 65536;
+}
+
+// The built-in choice of rows_pipelined_kernel, from graph-replay runs on
+// MI355X with inputs rotated over 1 GiB, each graph replayed for a warm-up
+// first (bit-identical outputs either way).  With two vectors per lane and
+// one workgroup per CU it beat one row per workgroup from T = 1536 on rows
+// of 640 and 896 vectors -- sandwich H=5120 R=4 (A/B/B/A): T=1536 22.1
+// against 23.6 us, T=2048 27.7 against 29.0, T=4096 49.7-50.5 against
+// 51.5-51.9, T=8192 94.7 against 97.2; residual + RMSNorm H=7168: R=1
+// T=4096 40.2 against 41.0, T=16384 153.6 against 156.4, R=2 T=4096 49.3
+// against 50.4 -- and came out even at 768 vectors (H=6144 R=4, within 1%
+// either way from T=1536).  It lost at T <= 1024 (H=5120: 15.6 against
+// 14.7 us; every row is resident at once there already), with two or three
+// workgroups per CU (up to 1.06x slower), at R=8 (H=8192 T=4096: 125-128
+// against 119 us), and on rows of 512 and 1024 vectors, where the one-row
+// kernel's four vectors per lane fit the row in few waves (H=4096 R=2
+// T=1536-2048: 3-7% behind; H=8192 R=4: 1-3% behind).  Returns the vec,
+// or 0 for the one-row kernel.
+int builtin_pipe_vec(int nvec, int fin, int64_t T, int epilogue, int R) {
+    if (T < 1536 || nvec <= 512 || nvec >= 1024) return 0;
+    if (pipe_fits(2, nvec, fin, epilogue, R)) return 2;
+    if (pipe_fits(1, nvec, fin, epilogue, R)) return 1;
+    return 0;
+}
+
 // The built-in choice of the split-row finalize (a workgroup per (token,
 // rank, 2048-column slice), then the reduction pass) over the one-row
 // finalize, from graph-replay sweeps on MI355X with inputs rotated over
@@ -279,24 +320,48 @@ LaunchShape choose_shape(int nvec, int fin, int64_t T, int epilogue, int R, int 
     const bool finalize = fin != kNoFinalize;
     const int64_t ep = fin == kEpFinalize ? 1 : 0;
     int vec = 0;
+    bool pipe = false;
     {
         std::lock_guard<std::mutex> lock(g_mu);
         load_env_table_locked();
         const int64_t H = (int64_t)nvec * 8;
         for (const Rule& r : g_rules) {
-            if (r.vec > 0 && matches(r, H, R, k, epilogue, ep) && T >= r.tmin && T <= r.tmax &&
-                vec_fits(r.vec, nvec, finalize, epilogue)) {
+            if (r.vec <= 0 || !matches(r, H, R, k, epilogue, ep) || T < r.tmin || T > r.tmax)
+                continue;
+            if (r.pipe ? pipe_fits(r.vec, nvec, fin, epilogue, R)
+                       : vec_fits(r.vec, nvec, finalize, epilogue)) {
                 vec = r.vec;
+                pipe = r.pipe;
                 break;
             }
         }
     }
+    if (vec == 0) {
+        vec = builtin_pipe_vec(nvec, fin, T, epilogue, R);
+        pipe = vec != 0;
+    }
     if (vec == 0) vec = builtin_vec(nvec, fin, T, epilogue, R);
     LaunchShape sh;
     sh.vec = vec;
+    sh.pipelined = pipe;
     const int lanes = (nvec + vec - 1) / vec;
     sh.threads = ((lanes + 63) / 64) * 64;
     return sh;
+}
+
+int64_t compute_units() {
+    static std::atomic<int> cus[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = -1;
+    int v = dev >= 0 ? cus[dev].load(std::memory_order_relaxed) : 0;
+    if (v <= 0) {
+        if (dev < 0 ||
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            v <= 0)
+            v = 256;  // MI355X
+        if (dev >= 0) cus[dev].store(v, std::memory_order_relaxed);
+    }
+    return v;
 }
 
 const char* set_launch_table(const char* text) {

@@ -3,8 +3,10 @@
     python tp_reduction_rmsnorm_amd/tune.py --out frn_launch_table.txt \\
         [--shape H R k epilogue ...] [--tokens T ...] [--calls 20]
 
-For every shape and token count, each vectors-per-lane choice that fits is
-forced through ``set_launch_table`` and timed the way the pages time this
+For every shape and token count, each launch choice that fits is forced
+through ``set_launch_table`` -- the one-row kernel with 1, 2 or 4 vectors
+per lane, and for calls without finalize the row-pipelined kernel with 1 or
+2 (``p1``, ``p2``) -- and timed the way the pages time this
 operation (vLLM PR #62366, kernel microbenchmark table): a HIP graph holding
 ``--calls`` calls, median of 5 replays.  Inputs rotate over up to 64 sets,
 at least 1 GiB where that many sets reach it, so large calls are not served
@@ -139,15 +141,27 @@ def graph_us(call: Call, calls: int) -> float:
     return sorted(ts)[2]
 
 
+def fits(H, R, k, epi, T, choice):
+    """Whether the rule value `choice` ('1', '2', '4', 'p1', 'p2') is what a
+    call of these sizes takes once that rule is loaded (a rule that does
+    not fit the call is skipped in favour of the built-in rule)."""
+    ep = epi.startswith("ep-")
+    vec = int(choice[-1])
+    pipelined = not ep and frn.launch_pipelined(R, k, T, H, EPI[epi])
+    return (frn.launch_shape(R, k, T, H, EPI[epi], ep=ep)[1] == vec and
+            pipelined == choice.startswith("p"))
+
+
 def tune_shape(H, R, k, epi, tokens, calls, dev, log=print):
-    """[(T, best_vec, {vec: us})] for one shape."""
+    """[(T, best_choice, {choice: us})] for one shape; a choice is a rule
+    value: '1', '2', '4' (one-row kernel) or 'p1', 'p2' (row-pipelined)."""
     rows = []
     for T in tokens:
         call = Call(H, R, k, epi, T, dev)
         times = {}
-        for vec in (1, 2, 4):
+        for vec in ("1", "2", "4", "p1", "p2"):
             frn.set_launch_table(f"{H} {R} {k} {epi} {T} {T} {vec}")
-            if frn.launch_shape(R, k, T, H, EPI[epi], ep=epi.startswith("ep-"))[1] != vec:
+            if not fits(H, R, k, epi, T, vec):
                 continue  # does not fit this call
             times[vec] = graph_us(call, calls)
         frn.set_launch_table(None)
