@@ -615,22 +615,26 @@ def test_auto_workspace_graphs_survive_a_larger_capture():
 
 SHAPE_CASES = [(4, 300, 5120, "sandwich", 0, False), (3, 7, 5128, "rmsnorm", 0, False),
                (8, 40, 8192, "sandwich", 0, False), (2, 260, 7168, "rmsnorm", 8, True),
-               (16, 5, 16384, "rmsnorm", 0, False)]
+               (16, 5, 16384, "rmsnorm", 0, False),
+               (4, 40, 4096, "rmsnorm", 4, True)]   # split-row finalize, then a k = 0 pass
 
 
-@pytest.mark.parametrize("vec", [1, 2, 4])
+@pytest.mark.parametrize("vec", ["1", "2", "4", "p1", "p2"])
 def test_results_do_not_depend_on_launch_shape(vec):
-    """Force every vectors-per-lane choice through a launch table: fused and
-    split results stay equal to the oracle (rules that do not fit a call are
-    skipped, so the built-in rule takes over there)."""
+    """Force every launch choice through a launch table -- the one-row
+    kernel's vectors per lane, and the row-pipelined kernel (p1 / p2), which
+    then also runs the k = 0 passes of the split-row finalize and of the split
+    path: fused and split results stay equal to the oracle (rules that do not
+    fit a call are skipped, so the built-in rule takes over there)."""
     m = frn()
     try:
         m.set_launch_table(f"* * * * 0 * {vec}")
         for case in SHAPE_CASES:
             R, T, H, epi, k, sh = case
-            log(f"launch shape vec={vec} {mid_id(case)} -> {m.launch_shape(R, k, T, H)}")
+            log(f"launch shape vec={vec} {mid_id(case)} -> {m.launch_shape(R, k, T, H)}, "
+                f"pipelined {m.launch_pipelined(R, k, T, H)}")
             inp = workloads.make(R, T, H, epilogue=epi, sigma=0.5, k=k, shared=sh,
-                                 seed=3000 + vec * 11 + T)
+                                 seed=3000 + int(vec[-1]) * 11 + T)
             d = to_dev(inp)
             y, x = gpu_fused(d)
             check(f"vec={vec} fused {mid_id(case)}", y, x, oracle_ref(inp))
