@@ -89,7 +89,9 @@ def build_probe() -> str:
 def pattern_probe(dev, cid=2, Ts=(1024, 4096)):
     """A workload's access pattern alone (bench_probe.hip: the same rows read
     and written, the same lanes, no arithmetic, no row-wide sums), graph-timed
-    beside the fused call.  Reduction workloads: on the call's own rotating
+    beside the fused call.  Where the call takes the row-pipelined kernel, its
+    pattern (one workgroup per CU walking the rows, the next row's loads before
+    the current row's stores) is timed as well.  Reduction workloads: on the call's own rotating
     buffers.  Expert-parallel workload: its k routed rows, the shared row and
     the residual of each token read as k + 2 contiguous [T,H] streams of
     their own (the same bytes without the gather, indices or weights)."""
@@ -102,6 +104,11 @@ def pattern_probe(dev, cid=2, Ts=(1024, 4096)):
     lib.probe_rows.restype = ctypes.c_int
     lib.probe_rows.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
                                ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+    lib.probe_rows_pipelined.restype = ctypes.c_int
+    lib.probe_rows_pipelined.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                                         ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                         ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
     rows = []
     for T in Ts:
         r = Runner(cid, T, dev, cold=True)
@@ -133,18 +140,37 @@ def pattern_probe(dev, cid=2, Ts=(1024, 4096)):
             if st != 0:
                 raise RuntimeError(f"probe_rows failed ({st})")
 
+        def probe_pipelined(i, arrays=arrays, T=T, H=w.H, nsrc=nsrc, vec=vec):
+            srcs, dsts = arrays[i % len(arrays)]
+            st = lib.probe_rows_pipelined(ctypes.cast(srcs, ctypes.c_void_p), nsrc,
+                                          ctypes.cast(dsts, ctypes.c_void_p), 2, T, H, vec,
+                                          min(T, cus), torch.cuda.current_stream().cuda_stream)
+            if st != 0:
+                raise RuntimeError(f"probe_rows_pipelined failed ({st})")
+
+        pipelined = not w.ep and frn.launch_pipelined(w.R, 0, T, w.H, r.epi)
         kernel_us = r.graph_us()
         call = r.call
         r.call = probe
         probe_us = r.graph_us()
+        pipe_us = None
+        if pipelined:
+            r.call = probe_pipelined
+            pipe_us = r.graph_us()
         r.call = call
         pattern_bytes = T * w.H * 2 * (nsrc + 2)
         rows.append(dict(workload=w.name, T=T, vectors_per_lane=vec, rows_read=nsrc,
+                         kernel="rows_pipelined_kernel" if pipelined else "row_kernel",
                          kernel_us=round(kernel_us, 3), kernel_GBps=round(r.bytes / kernel_us / 1e3, 1),
                          pattern_us=round(probe_us, 3),
                          pattern_GBps=round(pattern_bytes / probe_us / 1e3, 1),
                          pattern_frac_of_peak=round(pattern_bytes / probe_us / 1e3 / PEAK_GBS, 4),
                          kernel_over_pattern=round(kernel_us / probe_us, 4)))
+        if pipelined:
+            rows[-1].update(
+                pipelined_pattern_us=round(pipe_us, 3),
+                pipelined_pattern_frac_of_peak=round(pattern_bytes / pipe_us / 1e3 / PEAK_GBS, 4),
+                kernel_over_pipelined_pattern=round(kernel_us / pipe_us, 4))
         print(json.dumps(dict(pattern_probe=rows[-1])), file=sys.stderr, flush=True)
         del r, keep, arrays
         torch.cuda.empty_cache()

@@ -6,7 +6,8 @@
 // one-row kernel (lane l owns vectors l, l + threads, ...), with no
 // arithmetic beyond an XOR that keeps every load live and no row-wide sums.
 // Its rate is what this GPU delivers to the access pattern itself, the
-// reference the fused kernel's rate is read against.  Measurement
+// reference the fused kernel's rate is read against.  probe_rows_pipelined
+// does the same for the row-pipelined kernel's pattern.  Measurement
 // infrastructure only; not part of the library.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -74,7 +75,95 @@ __global__ __launch_bounds__(1024) void probe_rows_kernel(const ProbeArgs a) {
             if (ok[j]) st_nt(a.dst[d] + row + vi[j], acc[j]);
 }
 
+// The row-pipelined kernel's pattern: one workgroup per CU walks rows b,
+// b + G, ...; the next row's NS loads are issued before the current row's
+// two stores.  Exact NS and two destinations, and rows that split into whole
+// waves, so no lane predicate or run-time count hides an access from the
+// compiler's wait counting (as in the library's kernel).
+template <int V, int NS>
+__global__ __launch_bounds__(V == 1 ? 1024 : 512) void probe_pipelined_kernel(const ProbeArgs a,
+                                                                               int64_t T) {
+    int vi[V];
+#pragma unroll
+    for (int j = 0; j < V; ++j) vi[j] = threadIdx.x + j * blockDim.x;
+    int64_t t = blockIdx.x;
+    uint4 q[NS][V];
+#pragma unroll
+    for (int c = 0; c < NS; ++c)
+#pragma unroll
+        for (int j = 0; j < V; ++j) q[c][j] = ld_nt(a.src[c] + t * a.nvec + vi[j]);
+    for (;;) {
+        uint4 acc[V];
+#pragma unroll
+        for (int j = 0; j < V; ++j) {
+            acc[j] = q[0][j];
+#pragma unroll
+            for (int c = 1; c < NS; ++c) {
+                acc[j].x ^= q[c][j].x;
+                acc[j].y ^= q[c][j].y;
+                acc[j].z ^= q[c][j].z;
+                acc[j].w ^= q[c][j].w;
+            }
+        }
+        const int64_t tn = t + gridDim.x;
+        if (tn < T) {
+#pragma unroll
+            for (int c = 0; c < NS; ++c)
+#pragma unroll
+                for (int j = 0; j < V; ++j) q[c][j] = ld_nt(a.src[c] + tn * a.nvec + vi[j]);
+        }
+#pragma unroll
+        for (int d = 0; d < 2; ++d)
+#pragma unroll
+            for (int j = 0; j < V; ++j) st_nt(a.dst[d] + t * a.nvec + vi[j], acc[j]);
+        if (tn >= T) break;
+        t = tn;
+    }
+}
+
+template <int V>
+void launch_pipelined(const ProbeArgs& a, int64_t T, int groups, int threads, hipStream_t s) {
+    switch (a.nsrc) {
+        case 2: hipLaunchKernelGGL((probe_pipelined_kernel<V, 2>), dim3(groups), dim3(threads), 0, s, a, T); break;
+        case 3: hipLaunchKernelGGL((probe_pipelined_kernel<V, 3>), dim3(groups), dim3(threads), 0, s, a, T); break;
+        case 4: hipLaunchKernelGGL((probe_pipelined_kernel<V, 4>), dim3(groups), dim3(threads), 0, s, a, T); break;
+        default: hipLaunchKernelGGL((probe_pipelined_kernel<V, 5>), dim3(groups), dim3(threads), 0, s, a, T); break;
+    }
+}
+
 }  // namespace
+
+// The row-pipelined pattern: src as below with 2 <= nsrc <= 5, exactly two
+// dst rows, vec 1 or 2 with H/8 a multiple of 64 * vec (at most 1024 lanes
+// with one vector, 512 with two), groups workgroups with 1 <= groups <= T.
+// Returns 0 on success, 1 on bad arguments, 2 if the launch failed.
+extern "C" __attribute__((visibility("default"))) int probe_rows_pipelined(
+    const void* const* src, int nsrc, void* const* dst, int ndst, int64_t T, int64_t H, int vec,
+    int groups, void* stream) {
+    if (nsrc < 2 || nsrc > 5 || ndst != 2 || T < 1 || H < 8 || H % 8 != 0 || H > 16384 ||
+        T > 4194303 || !(vec == 1 || vec == 2) || groups < 1 || groups > T)
+        return 1;
+    const int nvec = (int)(H / 8);
+    if (nvec % (64 * vec) != 0 || nvec / vec > (vec == 1 ? 1024 : 512)) return 1;
+    ProbeArgs a{};
+    for (int r = 0; r < nsrc; ++r) {
+        if (src[r] == nullptr) return 1;
+        a.src[r] = static_cast<const uint4*>(src[r]);
+    }
+    for (int d = 0; d < 2; ++d) {
+        if (dst[d] == nullptr) return 1;
+        a.dst[d] = static_cast<uint4*>(dst[d]);
+    }
+    a.nsrc = nsrc;
+    a.ndst = 2;
+    a.nvec = nvec;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (vec == 1)
+        launch_pipelined<1>(a, T, groups, nvec, s);
+    else
+        launch_pipelined<2>(a, T, groups, nvec / 2, s);
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+}
 
 // src: nsrc device pointers to [T,H] BF16; dst: ndst device pointers to
 // [T,H] BF16; vec: vectors per lane (1, 2 or 4).  Returns 0 on success, 1 on
