@@ -39,6 +39,8 @@ PIPE_CASES = [
     (2, 1, 512, "rmsnorm", 1),       # one row of one wave
     (1, 1600, 512, "sandwich", 1),   # six or seven rows per workgroup
     (2, 700, 1024, "sandwich", 2),   # 64 lanes, two vectors each
+    (4, 256, 6144, "rmsnorm", 2),    # T equal to the CU count: one row per workgroup, R = 4
+    (3, 1537, 6144, "sandwich", 1),  # the built-in rule's first T, one vector per lane
 ]
 
 
