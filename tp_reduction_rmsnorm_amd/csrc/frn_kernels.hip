@@ -666,9 +666,14 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) f32x4_t lds_f32x4_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-__device__ __forceinline__ void load_gamma(const lds_f32x4_t* g, int v, float (&out)[8]) {
-    const f32x4_t a = g[2 * v];
-    const f32x4_t b = g[2 * v + 1];
+// A gamma row in LDS is two planes of nvec FP32 vectors: plane 0 holds the
+// first four values of each 8-value vector, plane 1 the last four, so the
+// lanes of a wave read 16-byte words at a 16-byte stride (no bank
+// conflicts; one interleaved row would put them 32 bytes apart).
+__device__ __forceinline__ void load_gamma(const lds_f32x4_t* g, int nvec, int v,
+                                           float (&out)[8]) {
+    const f32x4_t a = g[v];
+    const f32x4_t b = g[nvec + v];
     out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
     out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
 }
@@ -716,7 +721,7 @@ __device__ __forceinline__ void epilogue_lds(const RowArgs& a, int64_t row, cons
 #pragma unroll
         for (int j = 0; j < V; ++j) {
             float g[8], x[8];
-            load_gamma(gamma1, L.vi[j], g);
+            load_gamma(gamma1, a.nvec, L.vi[j], g);
             widen(xr[j], x);
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
@@ -741,7 +746,7 @@ __device__ __forceinline__ void epilogue_lds(const RowArgs& a, int64_t row, cons
 #pragma unroll
     for (int j = 0; j < V; ++j) {
         float g[8], y[8];
-        load_gamma(g2, L.vi[j], g);
+        load_gamma(g2, a.nvec, L.vi[j], g);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const float n = s[j][i] * r2;
@@ -765,19 +770,25 @@ __global__ __launch_bounds__(V == 1 ? 1024 : 512) void rows_pipelined_kernel(con
     __shared__ double slots[2][16];
     lds_f32x4_t* gamma_lds = (lds_f32x4_t*)gamma_lds_raw;
     const int nvec = a.nvec;
-    const int n4 = 2 * nvec;  // FP32 vectors per gamma row (a multiple of 64)
+    const int n4 = 2 * nvec;  // FP32 vectors per gamma row (two planes of nvec, a multiple of 64)
     Lanes<V> L(nvec);
 #pragma unroll
     for (int j = 0; j < V; ++j) L.ok[j] = true;  // no tail lanes (see above)
     {
+        // lane l of an instruction copies word (base + l) of one plane: the
+        // global FP32 vector 2 (base + l) (plane 0) or 2 (base + l) + 1 (plane 1)
         const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, nw = blockDim.x >> 6;
-        for (int base = w * 64; base < n4; base += nw * 64) {
-            __builtin_amdgcn_global_load_lds((const void*)(a.gamma1 + base + lane),
-                                             (lds_void_t*)(gamma_lds + base), 16, 0, 0);
-            if constexpr (EPI == kSandwich)
-                __builtin_amdgcn_global_load_lds((const void*)(a.gamma2 + base + lane),
-                                                 (lds_void_t*)(gamma_lds + n4 + base), 16, 0,
-                                                 0);
+        for (int base = w * 64; base < nvec; base += nw * 64) {
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                __builtin_amdgcn_global_load_lds(
+                    (const void*)(a.gamma1 + 2 * (base + lane) + half),
+                    (lds_void_t*)(gamma_lds + half * nvec + base), 16, 0, 0);
+                if constexpr (EPI == kSandwich)
+                    __builtin_amdgcn_global_load_lds(
+                        (const void*)(a.gamma2 + 2 * (base + lane) + half),
+                        (lds_void_t*)(gamma_lds + n4 + half * nvec + base), 16, 0, 0);
+            }
         }
     }
     int64_t t = blockIdx.x;
