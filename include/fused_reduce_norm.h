@@ -352,9 +352,9 @@ int32_t frn_split_rows(int32_t R, int32_t k, int64_t T, int64_t H, int32_t epilo
  * after).  It serves 1 <= R <= 4, H/8 a multiple of 64 * vec (at most 1024
  * lanes with one vector per lane, 512 with two) and gamma rows of at most
  * 64 KiB.  The built-in rule, measured on MI355X, takes it with two
- * vectors per lane from T = 1536 for 4096 < H < 8192 (where it measured
- * faster or even); launch-table p1 / p2 rules and numeric vec rules
- * override it.  Results are bit-identical either
+ * vectors per lane from T = 1536 for 4096 < H < 8192, for the sandwich
+ * epilogue and for residual + RMSNorm at R = 1 (where it measured faster or
+ * even); launch-table p1 / p2 rules and numeric vec rules override it.  Results are bit-identical either
  * way: the same arithmetic in the same order, row by row.
  */
 int32_t frn_launch_pipelined(int32_t R, int32_t k, int64_t T, int64_t H, int32_t epilogue);

@@ -503,6 +503,8 @@ def test_pipelined_builtin_rule():
     assert frn.launch_shape(4, 0, 1535, 5120, S) == (320, 2)   # one-row kernel, two vectors
     assert frn.launch_pipelined(1, 0, 16384, 7168, N)          # split pass 2
     assert frn.launch_shape(1, 0, 16384, 7168, N) == (448, 2)
+    assert not frn.launch_pipelined(2, 0, 16384, 7168, N)      # residual + RMSNorm: R = 1 only
+    assert frn.launch_pipelined(2, 0, 2048, 6144, S)           # the sandwich at R = 2
     assert frn.launch_pipelined(3, 0, 2048, 6144, S)           # 768 vectors, R = 3
     assert frn.launch_shape(3, 0, 2048, 6144, S) == (384, 2)
     assert not frn.launch_pipelined(4, 0, 4096, 8192, S)       # 1024 vectors: one row per group

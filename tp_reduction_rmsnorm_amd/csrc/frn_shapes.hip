@@ -225,20 +225,25 @@ bool pipe_fits(int vec, int nvec, int fin, int epilogue, int R) {
 // MI355X with inputs rotated over 1 GiB, each graph replayed for a warm-up
 // first (bit-identical outputs either way).  With two vectors per lane and
 // one workgroup per CU it beat one row per workgroup from T = 1536 on rows
-// of 640 and 896 vectors -- sandwich H=5120 R=4 (A/B/B/A): T=1536 22.1
-// against 23.6 us, T=2048 27.7 against 29.0, T=4096 49.7-50.5 against
-// 51.5-51.9, T=8192 94.7 against 97.2; residual + RMSNorm H=7168: R=1
-// T=4096 40.2 against 41.0, T=16384 153.6 against 156.4, R=2 T=4096 49.3
-// against 50.4 -- and came out even at 768 vectors (H=6144 R=4, within 1%
-// either way from T=1536).  It lost at T <= 1024 (H=5120: 15.6 against
-// 14.7 us; every row is resident at once there already), with two or three
-// workgroups per CU (up to 1.06x slower), at R=8 (H=8192 T=4096: 125-128
-// against 119 us), and on rows of 512 and 1024 vectors, where the one-row
-// kernel's four vectors per lane fit the row in few waves (H=4096 R=2
-// T=1536-2048: 3-7% behind; H=8192 R=4: 1-3% behind).  Returns the vec,
-// or 0 for the one-row kernel.
+// of 640 to 896 vectors with the sandwich epilogue, whose two row sums and
+// two gamma rows it overlaps with the next row's loads -- H=5120 R=4
+// (A/B/B/A): T=1536 22.1 against 23.6 us, T=2048 27.1-27.7 against
+// 28.8-29.0, T=4096 49.7-50.5 against 51.5-51.9, T=8192 94.4 against 97.7,
+// T=16384 185.9 against 191.2; H=6144 R=2 T=2048 24.7 against 26.6 -- and
+// with the residual + RMSNorm epilogue at R = 1 (the split path's pass 2,
+// H=7168: T=4096 40.2 against 41.0 us, T=16384 154.1 either way).  With
+// that lighter epilogue at R >= 2 it came out even or behind (H=7168 R=2:
+// T=8192 even, T=16384 195.7 against 187.4 us; H=6144 R=4 T=4096 60.3
+// against 59.0).  It lost at T <= 1024 (H=5120: 15.6 against 14.7 us; every
+// row is resident at once there already), with two or three workgroups per
+// CU (up to 1.06x slower), at R=8 (H=8192 T=4096: 125-128 against 119 us),
+// and on rows of 512 and 1024 vectors, where the one-row kernel's four
+// vectors per lane fit the row in few waves (H=4096 R=2 T=1536-2048: 3-7%
+// behind; H=8192 R=4: 1-3% behind).  Returns the vec, or 0 for the one-row
+// kernel.
 int builtin_pipe_vec(int nvec, int fin, int64_t T, int epilogue, int R) {
     if (T < 1536 || nvec <= 512 || nvec >= 1024) return 0;
+    if (epilogue == kRmsNorm && R != 1) return 0;
     if (pipe_fits(2, nvec, fin, epilogue, R)) return 2;
     if (pipe_fits(1, nvec, fin, epilogue, R)) return 1;
     return 0;
