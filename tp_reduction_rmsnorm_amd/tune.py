@@ -8,7 +8,7 @@ through ``set_launch_table`` -- the one-row kernel with 1, 2 or 4 vectors
 per lane, and for calls without finalize the row-pipelined kernel with 1 or
 2 (``p1``, ``p2``) -- and timed the way the pages time this
 operation (vLLM PR #62366, kernel microbenchmark table): a HIP graph holding
-``--calls`` calls, median of 5 replays.  Inputs rotate over up to 64 sets,
+``--calls`` calls, median of 5 replays after at least 100 ms of replays.  Inputs rotate over up to 64 sets,
 at least 1 GiB where that many sets reach it, so large calls are not served
 from the Infinity Cache.  The fastest choice per T becomes a rule covering
 the T range up to it; neighbouring ranges with the same choice merge.  Load
@@ -29,6 +29,7 @@ from __future__ import annotations
 import argparse
 import os
 import sys
+import time
 
 import torch
 
@@ -114,6 +115,12 @@ class Call:
                                            residual_out=d["rout"])
 
 
+# Each graph is replayed for this long before it is timed: after idle time
+# (input generation) MI355X runs the first ~10 ms of sustained traffic
+# slow, which would penalise whichever choice is timed first.
+SETTLE_S = 0.1
+
+
 def graph_us(call: Call, calls: int) -> float:
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -129,6 +136,11 @@ def graph_us(call: Call, calls: int) -> float:
     for _ in range(3):
         g.replay()
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < SETTLE_S:
+        for _ in range(10):
+            g.replay()
+        torch.cuda.synchronize()
     ts = []
     for _ in range(5):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
