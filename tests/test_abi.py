@@ -708,15 +708,29 @@ def test_builtin_launch_shapes_always_fit():
 
 def test_shipped_launch_table_parses_and_routes():
     """The measured table shipped with the package loads, and its split /
-    fused rules route the finalize workloads as measured."""
+    fused rules and its row-pipelined rules route calls as the table says
+    (the edges are read from the table, which a re-tune may move)."""
     import tp_reduction_rmsnorm_amd as frn
     path = os.path.join(ROOT, "tp_reduction_rmsnorm_amd", "launch_table_mi355x.txt")
+    text = open(path).read()
+    rules = [l.split() for l in text.splitlines() if l.strip() and not l.startswith("#")]
+    epis = {"rmsnorm": frn.EPI_RMSNORM, "sandwich": frn.EPI_SANDWICH}
     try:
-        frn.set_launch_table(open(path).read())
-        assert frn.split_rows(8, 10, 96, 6144) and not frn.split_rows(8, 10, 97, 6144)
-        assert frn.split_rows(2, 8, 32, 7168) and not frn.split_rows(2, 8, 33, 7168)
-        assert frn.split_rows(8, 10, 1, 6144, ep=True)
-        assert not frn.split_rows(8, 10, 64, 6144, ep=True)
-        assert frn.launch_shape(4, 0, 4096, 5120, frn.EPI_SANDWICH)[1] in (2, 4)
+        frn.set_launch_table(text)
+        splits = [r for r in rules if r[6] == "split"]
+        assert splits, "the table has split rules"
+        for H, R, k, epi, lo, hi, _ in splits:
+            ep = epi.startswith("ep-")
+            H, R, k, hi = int(H), int(R), int(k), int(hi)
+            assert frn.split_rows(R, k, hi, H, epis[epi.replace("ep-", "")], ep=ep)
+            assert not frn.split_rows(R, k, hi + 1, H, epis[epi.replace("ep-", "")], ep=ep)
+        piped = [r for r in rules if r[6] in ("p1", "p2")]
+        assert piped, "the table has row-pipelined rules"
+        for H, R, k, epi, lo, hi, v in piped:
+            H, R, k, lo = int(H), int(R), int(k), max(int(lo), 1)
+            assert frn.launch_pipelined(R, k, lo, H, epis[epi])
+            assert frn.launch_shape(R, k, lo, H, epis[epi])[1] == int(v[1])
     finally:
         frn.set_launch_table(None)
+
+
