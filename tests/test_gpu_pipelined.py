@@ -136,3 +136,30 @@ def test_pipelined_graph_replay():
             assert torch.equal(ex.view(torch.int16), r.view(torch.int16)), f"replay {rep}"
         gpu_fused(sets[0])  # eager work between replays
     del g
+
+
+def test_pipelined_calls_on_two_streams_at_once():
+    """Row-pipelined calls queued on two streams together (each launch has its
+    own LDS and no state outside its arguments) match the oracle."""
+    m = frn()
+    try:
+        m.set_launch_table("5120 4 0 sandwich 0 * p2\n5120 2 0 rmsnorm 0 * p1")
+        cases = [workloads.make(4, 600, 5120, epilogue="sandwich", sigma=0.5, seed=5301),
+                 workloads.make(2, 777, 5120, epilogue="rmsnorm", sigma=0.5, seed=5302)]
+        devs = [to_dev(c) for c in cases]
+        streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+        for s in streams:
+            s.wait_stream(torch.cuda.current_stream())
+        outs = []
+        for d, s in zip(devs, streams):
+            with torch.cuda.stream(s):
+                for _ in range(3):          # several launches in flight on each stream
+                    y, x = gpu_fused(d)
+                outs.append((y, x))
+        for s in streams:
+            torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        for c, (y, x) in zip(cases, outs):
+            check(f"two streams R{c.R} T{c.T} {c.epilogue}", y, x, oracle_ref(c))
+    finally:
+        m.set_launch_table(None)
