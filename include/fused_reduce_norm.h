@@ -320,10 +320,12 @@ frn_status frn_launch_shape(int32_t R, int32_t k, int64_t T, int64_t H, int32_t 
  * BF16 values, summed in the same order).  Layout: R x T x H BF16.  The
  * caller allocates it (256-byte aligned); it needs no initialisation and
  * holds nothing between calls.  Calls that share one workspace must not run
- * concurrently.  A workspace that is NULL, smaller than needed for a call,
- * or given to a call that does not take the split-row finalize is ignored
- * (the call then uses the one-row-per-workgroup kernel); one that is used
- * must not overlap any other argument (FRN_ERR_INVALID).
+ * concurrently.  A workspace that is NULL, or given to a call that does not
+ * take the split-row finalize, is ignored (the call then uses the
+ * one-row-per-workgroup kernel).  A workspace given to a call that takes it
+ * must cover that call (R * T * H * 2 bytes) and be 256-byte aligned, else
+ * the call returns FRN_ERR_UNSUPPORTED without launching; it must not
+ * overlap any other argument (FRN_ERR_INVALID).
  */
 size_t frn_workspace_bytes(int64_t max_T, int64_t H, int32_t R, int32_t k);
 

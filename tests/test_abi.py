@@ -376,6 +376,8 @@ def test_misaligned_or_overlapping_workspace_rejected(lib):
         assert lib.frn_set_launch_table(b"* * * * 0 * split\n") == OK
         assert frn.split_rows(2, 3, 4, 64)
         assert moe(addr(40, 16), need) == UNSUPPORTED   # not 256-byte aligned
+        assert moe(addr(40), need - 1) == UNSUPPORTED   # too small for the split-row mode
+        assert b"smaller than" in lib.frn_last_error()
         assert moe(addr(10), need) == INVALID           # overlaps expert rows of rank 0
         assert moe(addr(3), need) == INVALID            # overlaps out
     finally:

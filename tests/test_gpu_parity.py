@@ -502,9 +502,15 @@ def test_split_row_small_or_misaligned_workspace():
     inp = workloads.make(4, 8, 2048, k=3, shared=True, seed=55)
     ref = oracle_ref(inp)
     d = to_dev(inp)
-    small = torch.zeros(64, dtype=torch.uint8, device=DEV)   # too small: ignored
-    y, x = gpu_fused(d, workspace=small)
-    check("too-small workspace ignored", y, x, ref)
+    out = torch.full((8, 2048), 3.0, dtype=torch.bfloat16, device=DEV)
+    rout = torch.full((8, 2048), 5.0, dtype=torch.bfloat16, device=DEV)
+    small = torch.zeros(64, dtype=torch.uint8, device=DEV)   # too small: declined
+    with pytest.raises(m.FusedReduceNormUnsupported, match="smaller than"):
+        gpu_fused(d, workspace=small, out=out, residual_out=rout)
+    torch.cuda.synchronize()
+    assert bool((out == 3.0).all()) and bool((rout == 5.0).all())   # untouched
+    y, x = gpu_fused(d, workspace=None)                        # none: the one-row kernel
+    check("no workspace", y, x, ref)
     big = torch.zeros(m.workspace_bytes(8, 2048, 4, 3) + 512, dtype=torch.uint8, device=DEV)
     with pytest.raises(m.FusedReduceNormUnsupported):
         gpu_fused(d, workspace=big[16:])                      # 16-byte, not 256-byte aligned

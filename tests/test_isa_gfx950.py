@@ -110,3 +110,48 @@ def test_pipelined_kernel_keeps_the_next_row_in_flight():
     assert re.search(r"s_waitcnt vmcnt\(4\)", f)
     first_barrier = f.index("s_barrier")
     assert f.index("vmcnt(0)") < first_barrier
+
+
+def _pipelined_instances():
+    """(epilogue, vectors per lane, ranks) of every rows_pipelined_kernel."""
+    return [(e, v, r) for e in (0, 1) for v in (1, 2) for r in (1, 2, 3, 4)]
+
+
+def _pipelined_symbol(e, v, r):
+    return f"_ZN3frn12_GLOBAL__N_121rows_pipelined_kernelILi{e}ELi{v}ELi{r}EEEvNS_7RowArgsE"
+
+
+@pytest.mark.parametrize("epi,vec,ranks", _pipelined_instances())
+def test_pipelined_row_sums_alternate_slot_arrays(epi, vec, ranks):
+    """A row sum writes one FP64 per wave into an LDS slot array, then one
+    barrier, then every lane reads all of them; nothing follows the reads.
+    So the next write into the same array must sit behind another barrier,
+    or a fast wave could overwrite a slot a slow wave has not read yet.  In
+    the row loop the slot writes (ds_write_b64 at offset 0 = slots[0] and
+    128 = slots[1]) alternate between the two arrays, each followed by a
+    barrier before the next write: two per loop, for the sandwich (two sums
+    per row) and for residual + RMSNorm (one sum per row, rows unrolled by
+    two)."""
+    f = _function(_disassembly(), _pipelined_symbol(epi, vec, ranks))
+    events = [m.group(0) for m in re.finditer(
+        r"s_barrier|ds_write_b64 v\d+, v\[\d+:\d+\]( offset:\d+)?", f)]
+    writes = [e for e in events if e.startswith("ds_write_b64")]
+    offsets = [int(e.split("offset:")[1]) if "offset:" in e else 0 for e in writes]
+    assert offsets == [0, 128], f"slot writes at offsets {offsets}"
+    # every slot write is followed by a barrier before the next slot write
+    seq = ["W" if e.startswith("ds_write") else "B" for e in events]
+    first = seq.index("W")
+    assert seq[first:] == ["W", "B", "W", "B"], seq
+
+
+@pytest.mark.parametrize("epi,vec,ranks", _pipelined_instances())
+def test_pipelined_loop_never_waits_for_everything(epi, vec, ranks):
+    """One full wait on the vector memory counter (the gamma copies before
+    the first barrier); every other wait leaves the row's 2 x vec output
+    stores in flight, so none of them waits for the stores."""
+    f = _function(_disassembly(), _pipelined_symbol(epi, vec, ranks))
+    waits = [int(n) for n in re.findall(r"s_waitcnt vmcnt\((\d+)\)", f)]
+    assert waits.count(0) == 1, waits
+    assert f.index("vmcnt(0)") < f.index("s_barrier")
+    assert min(w for w in waits if w) >= 2 * vec, waits
+

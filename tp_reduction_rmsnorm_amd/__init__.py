@@ -371,6 +371,19 @@ def reduce_sandwich_norm(partials: TensorList, residual: torch.Tensor, gamma1: t
     return out, residual_out
 
 
+def _check_moe_epilogue(residual, gamma1, gamma2, epilogue, T, H, device):
+    if residual is None:
+        raise ValueError("residual is required: this boundary always adds the residual")
+    _need(residual, "residual", torch.bfloat16, 2, device)
+    if tuple(residual.shape) != (T, H):
+        raise ValueError("residual must be [T, H]")
+    _check_gamma(gamma1, H, device, "gamma1")
+    if epilogue == EPI_SANDWICH:
+        if gamma2 is None:
+            raise ValueError("the sandwich epilogue needs gamma2")
+        _check_gamma(gamma2, H, device, "gamma2")
+
+
 def moe_finalize_reduce_norm(expert_rows: TensorList, topk_weights: torch.Tensor,
                              topk_rows: torch.Tensor, residual: torch.Tensor,
                              gamma1: torch.Tensor, gamma2: Optional[torch.Tensor] = None,
@@ -386,14 +399,7 @@ def moe_finalize_reduce_norm(expert_rows: TensorList, topk_weights: torch.Tensor
         raise ValueError("residual is required: this boundary always adds the residual")
     es, sh, T, H, k, num_rows, device = _check_finalize(expert_rows, topk_weights, topk_rows,
                                                         shared)
-    _need(residual, "residual", torch.bfloat16, 2, device)
-    if tuple(residual.shape) != (T, H):
-        raise ValueError("residual must be [T, H]")
-    _check_gamma(gamma1, H, device, "gamma1")
-    if epilogue == EPI_SANDWICH:
-        if gamma2 is None:
-            raise ValueError("the sandwich epilogue needs gamma2")
-        _check_gamma(gamma2, H, device, "gamma2")
+    _check_moe_epilogue(residual, gamma1, gamma2, epilogue, T, H, device)
     out, residual_out = _outputs(T, H, device, out, residual_out)
     st = _stream(stream, device)
     ws, wsb = _workspace(workspace, T, H, len(es), k, device, st, epilogue)

@@ -244,15 +244,20 @@ frn_status run(const Call& c, int32_t epilogue, int64_t T, void* stream) {
 }
 
 // The optional workspace serves the split-row finalize where that is the
-// chosen path for this call and the workspace is large enough for its T;
-// otherwise it is ignored (the one-row kernel needs none).
+// chosen path for this call; a call that does not take it ignores the
+// workspace (the one-row kernel needs none).  A workspace too small for the
+// chosen mode declines the call, as a misaligned one does.
 frn_status set_workspace(Call& c, void* workspace, size_t workspace_bytes, int32_t k, int64_t T,
                          int64_t H, int32_t R, int32_t epilogue) {
     c.a.ws_p = nullptr;
     if (k == 0 || workspace == nullptr) return FRN_OK;
     if (!frn::use_split_rows(R, H, k, c.a.ep != 0, epilogue, T)) return FRN_OK;
     const size_t need = frn::split_workspace_bytes(T, H, R);
-    if (workspace_bytes < need) return FRN_OK;
+    if (workspace_bytes < need)
+        return fail(FRN_ERR_UNSUPPORTED,
+                    "workspace of %zu bytes is smaller than the %zu bytes the split-row "
+                    "finalize needs at T=%lld (frn_workspace_bytes)",
+                    workspace_bytes, need, (long long)T);
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
         return fail(FRN_ERR_UNSUPPORTED, "workspace is not 256-byte aligned");
     frn_status st = add_out(c, "workspace", workspace, need);
@@ -277,6 +282,14 @@ frn_status fused(const void* const* src, const void* const* shared, int32_t R,
         return st;
     if ((st = check_alias(c)) != FRN_OK) return st;
     return run(c, epilogue, T, stream);
+}
+
+// Checks of a finalize call's k and epilogue that come before the sizes.
+frn_status check_finalize_call(int32_t k, int32_t epilogue) {
+    if (k < 1) return fail(FRN_ERR_INVALID, "k must be >= 1 for the finalize (got %d)", k);
+    if (epilogue != FRN_EPI_RMSNORM && epilogue != FRN_EPI_SANDWICH)
+        return fail(FRN_ERR_INVALID, "unknown epilogue %d", epilogue);
+    return FRN_OK;
 }
 
 frn_status pass1(const void* const* src, const void* const* shared, int32_t R,
@@ -322,14 +335,9 @@ FRN_API frn_status frn_moe_finalize_reduce_norm(
     const void* residual_in, const float* gamma1, const float* gamma2, float eps, int64_t T,
     int64_t H, void* out, void* residual_out, void* workspace, size_t workspace_bytes,
     void* stream) {
-    if (k < 1) {
-        g_last_error[0] = '\0';
-        return fail(FRN_ERR_INVALID, "k must be >= 1 for the finalize (got %d)", k);
-    }
-    if (epilogue != FRN_EPI_RMSNORM && epilogue != FRN_EPI_SANDWICH) {
-        g_last_error[0] = '\0';
-        return fail(FRN_ERR_INVALID, "unknown epilogue %d", epilogue);
-    }
+    g_last_error[0] = '\0';
+    const frn_status st = check_finalize_call(k, epilogue);
+    if (st != FRN_OK) return st;
     return fused(expert_rows, shared, R, tp_routing(R, topk_w, topk_row, num_rows), k, epilogue,
                  residual_in, gamma1, gamma2, eps, T, H, out, residual_out, workspace,
                  workspace_bytes, stream);

@@ -44,6 +44,8 @@
 //   rmsnorm    h = s + x; y = (h * rinv(h)) * gamma
 //   sandwich   a = (s * rinv(s)) * gamma1; h = a + x; y = (h * rinv(h)) * gamma2
 // No MFMA: nothing here is a dense contraction; the kernels are bound by HBM.
+#include <type_traits>
+
 #include "frn_internal.h"
 
 namespace frn {
@@ -130,7 +132,8 @@ __device__ __forceinline__ double readlane_f64(double v, int lane) {
 // mirrors), each step adding two equal partial sums in either order, so all
 // 16 lanes hold identical bits; the four row sums are then read out and
 // added in row order; the waves' sums meet in LDS and are added in wave order.
-__device__ __forceinline__ double block_sum(double v, double* slots) {
+// nw: waves in the workgroup.
+__device__ __forceinline__ double block_sum(double v, double* slots, int nw) {
     v = v + dpp_f64<0xB1>(v);   // quad_perm [1,0,3,2]
     v = v + dpp_f64<0x4E>(v);   // quad_perm [2,3,0,1]
     v = v + dpp_f64<0x141>(v);  // row_half_mirror
@@ -140,7 +143,6 @@ __device__ __forceinline__ double block_sum(double v, double* slots) {
     const int wave = threadIdx.x >> 6;
     if (lane == 0) slots[wave] = v;
     __syncthreads();
-    const int nw = blockDim.x >> 6;
     double t = slots[0];
     for (int w = 1; w < nw; ++w) t += slots[w];
     return t;
@@ -553,8 +555,9 @@ __device__ __forceinline__ void epilogue(const RowArgs& a, int64_t row, const La
         const float eps = a.eps;
         const int H = a.H;
         // h overwrites s in place
+        const int nw = blockDim.x >> 6;
         if constexpr (EPI == kSandwich) {
-            const float r1 = inv_rms(block_sum(sum_squares<V>(s, L), slots[0]), H, eps);
+            const float r1 = inv_rms(block_sum(sum_squares<V>(s, L), slots[0], nw), H, eps);
 #pragma unroll
             for (int j = 0; j < V; ++j) {
                 float g[8], x[8];
@@ -582,7 +585,7 @@ __device__ __forceinline__ void epilogue(const RowArgs& a, int64_t row, const La
         for (int j = 0; j < V; ++j)
             if (L.ok[j]) st_stream(a.residual_out + row + L.vi[j], narrow(s[j]));
 
-        const float r2 = inv_rms(block_sum(sum_squares<V>(s, L), slots[1]), H, eps);
+        const float r2 = inv_rms(block_sum(sum_squares<V>(s, L), slots[1], nw), H, eps);
         const float4* g2 = (EPI == kSandwich) ? gamma2 : gamma1;
 #pragma unroll
         for (int j = 0; j < V; ++j) {
@@ -708,16 +711,21 @@ __device__ __forceinline__ void sum_ranks(const uint4 (&q)[R][V], float (&s)[V][
 }
 
 // The epilogue of `epilogue` with the gamma rows read from LDS.  Same
-// arithmetic, in the same order.
-template <int EPI, int V>
+// arithmetic, in the same order.  Slot arrays: the sandwich's two row sums
+// take slots[0] and slots[1]; residual + RMSNorm's one row sum takes
+// slots[P], so that the caller can alternate them from row to row.
+template <int EPI, int V, int P>
 __device__ __forceinline__ void epilogue_lds(const RowArgs& a, int64_t row, const Lanes<V>& L,
                                              float (&s)[V][8], const uint4 (&xr)[V],
                                              double (&slots)[2][16], const lds_f32x4_t* gamma1,
                                              const lds_f32x4_t* gamma2) {
     const float eps = a.eps;
     const int H = a.H;
+    // waves per workgroup, from the kernel arguments (a scalar load): the
+    // launch sizes the workgroup to the row, blockDim.x * V == nvec
+    const int nw = a.nvec / (64 * V);
     if constexpr (EPI == kSandwich) {
-        const float r1 = inv_rms(block_sum(sum_squares<V>(s, L), slots[0]), H, eps);
+        const float r1 = inv_rms(block_sum(sum_squares<V>(s, L), slots[0], nw), H, eps);
 #pragma unroll
         for (int j = 0; j < V; ++j) {
             float g[8], x[8];
@@ -741,7 +749,8 @@ __device__ __forceinline__ void epilogue_lds(const RowArgs& a, int64_t row, cons
     }
 #pragma unroll
     for (int j = 0; j < V; ++j) st_stream(a.residual_out + row + L.vi[j], narrow(s[j]));
-    const float r2 = inv_rms(block_sum(sum_squares<V>(s, L), slots[1]), H, eps);
+    const float r2 =
+        inv_rms(block_sum(sum_squares<V>(s, L), slots[EPI == kSandwich ? 1 : P], nw), H, eps);
     const lds_f32x4_t* g2 = (EPI == kSandwich) ? gamma2 : gamma1;
 #pragma unroll
     for (int j = 0; j < V; ++j) {
@@ -803,16 +812,33 @@ __global__ __launch_bounds__(V == 1 ? 1024 : 512) void rows_pipelined_kernel(con
     for (int j = 0; j < V; ++j)
         asm volatile("" ::"v"(xr[j].x), "v"(xr[j].y), "v"(xr[j].z), "v"(xr[j].w));
     __syncthreads();  // the gamma rows are in LDS (the compiler waits for the copies here)
-    for (;;) {
+    // One row: the next row's loads go out, then this row's epilogue runs;
+    // false once this was the workgroup's last row.
+    auto step = [&](auto parity) -> bool {
         const int64_t tn = t + gridDim.x;
         const bool more = tn < a.T;
         uint4 xn[V];
         if (more) issue_row<V, R>(a, tn * nvec, L, xn, q);
-        epilogue_lds<EPI, V>(a, t * nvec, L, s, xr, slots, gamma_lds, gamma_lds + n4);
-        if (!more) break;
+        epilogue_lds<EPI, V, decltype(parity)::value>(a, t * nvec, L, s, xr, slots, gamma_lds,
+                                                      gamma_lds + n4);
+        if (!more) return false;
         sum_ranks<V, R>(q, s);
         for (int j = 0; j < V; ++j) xr[j] = xn[j];
         t = tn;
+        return true;
+    };
+    // A row sum's slot array is written by one lane per wave before a
+    // barrier and read by every lane after it, with no second barrier: the
+    // next write to the same array must come after a later barrier, which no
+    // wave passes before every wave has read it.  The sandwich's two sums per
+    // row alternate the two arrays; residual + RMSNorm has one sum per row, so
+    // consecutive rows alternate them (two rows per iteration).
+    if constexpr (EPI == kSandwich) {
+        while (step(std::integral_constant<int, 0>{})) {
+        }
+    } else {
+        while (step(std::integral_constant<int, 0>{}) && step(std::integral_constant<int, 1>{})) {
+        }
     }
 }
 
