@@ -67,6 +67,8 @@ extern "C" {
 #define FRN_MAX_H 16384  /* hidden size */
 #define FRN_MAX_T 4194303 /* token rows per call (a row's workgroup has up to
                              1024 lanes, and a dispatch holds < 2^32 lanes) */
+#define FRN_NOALLOC_SCRATCH_BYTES (16u << 20) /* scratch per GPU of
+                             frn_moe_finalize_reduce_norm_noalloc (16 MiB) */
 
 typedef enum frn_status {
     FRN_OK = 0,
@@ -142,6 +144,36 @@ frn_status frn_moe_finalize_reduce_norm(const void* const* expert_rows,
                                         int64_t H, void* out, void* residual_out,
                                         void* workspace, size_t workspace_bytes,
                                         void* stream);
+
+/*
+ * frn_moe_finalize_reduce_norm for callers that cannot allocate device
+ * memory or hand in a workspace: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  Same arguments, results
+ * and checks as frn_moe_finalize_reduce_norm, without workspace and
+ * workspace_bytes: where that call would take the split-row finalize (see
+ * frn_split_rows), this one writes its R x T x H BF16 partials to a scratch
+ * array that the library holds in device memory, FRN_NOALLOC_SCRATCH_BYTES
+ * per GPU, kept until the process ends; elsewhere it runs the one-row kernel
+ * and uses no scratch.  It calls no allocation routine.  A call whose
+ * split-row finalize needs more than FRN_NOALLOC_SCRATCH_BYTES (R * T * H *
+ * 2 bytes; e.g. R = 8, H = 6144 fits up to T = 170) returns
+ * FRN_ERR_UNSUPPORTED without launching, and frn_last_error() states both
+ * sizes.  The scratch needs no initialisation and its contents from the
+ * previous call are never read.  Every call on one GPU shares that GPU's
+ * array: calls that may overlap in time on one GPU (different streams,
+ * concurrent graph replays) race and give wrong results; serialise them.
+ * The first call on each GPU looks up the array's device address
+ * (hipGetSymbolAddress, with that GPU current); make it once before any
+ * graph capture.  The kernels run on the device of `stream`.
+ */
+frn_status frn_moe_finalize_reduce_norm_noalloc(const void* const* expert_rows,
+                                                const void* const* shared, int32_t R,
+                                                const float* topk_w, const int32_t* topk_row,
+                                                int32_t k, int64_t num_rows, int32_t epilogue,
+                                                const void* residual_in, const float* gamma1,
+                                                const float* gamma2, float eps, int64_t T,
+                                                int64_t H, void* out, void* residual_out,
+                                                void* stream);
 
 /*
  * Split path, pass 1 (vLLM PR #62366 "Claims": for large batches the

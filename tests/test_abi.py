@@ -190,6 +190,63 @@ def test_moe_zero_tokens_is_a_no_op(lib):
     assert call_moe(lib, T=0) == OK
 
 
+def call_moe_noalloc(lib, R=2, k=3, T=4, H=64, num_rows=12, epilogue=0, shared=True, w=None,
+                     rows=None):
+    lib.frn_moe_finalize_reduce_norm_noalloc.argtypes = [
+        P, P, ctypes.c_int32, P, P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, P, P, P,
+        ctypes.c_float, ctypes.c_int64, ctypes.c_int64, P, P, P]
+    src = ptrs(*[addr(10 + r) for r in range(R)])
+    sh = ptrs(*[addr(30 + r) for r in range(R)]) if shared else None
+    return lib.frn_moe_finalize_reduce_norm_noalloc(
+        src, sh, R, addr(5) if w is None else w, addr(6) if rows is None else rows, k, num_rows,
+        epilogue, addr(1), addr(2), addr(7), 1e-6, T, H, addr(3), addr(4), None)
+
+
+def noalloc_scratch_bytes():
+    m = re.search(r"#define FRN_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", open(HEADER).read())
+    return int(m.group(1)) << int(m.group(2))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=0), INVALID),
+    (dict(k=17), UNSUPPORTED),
+    (dict(T=4194304), UNSUPPORTED),
+    (dict(num_rows=0), INVALID),
+    (dict(epilogue=7), INVALID),
+    (dict(w=0), INVALID),
+    (dict(rows=0), INVALID),
+    (dict(rows=addr(6, 2)), UNSUPPORTED),
+    (dict(w=addr(3)), INVALID),   # out overlaps the weights
+    (dict(H=68), UNSUPPORTED),
+])
+def test_noalloc_rejects_like_the_workspace_call(lib, kw, status):
+    assert call_moe_noalloc(lib, **kw) == status
+    assert call_moe(lib, **kw) == status
+
+
+def test_noalloc_zero_tokens_is_a_no_op(lib):
+    assert call_moe_noalloc(lib, T=0) == OK
+
+
+def test_noalloc_declines_beyond_its_scratch(lib):
+    """Where the split-row finalize is chosen and its partials (R*T*H*2
+    bytes) exceed the library's scratch array, the call is declined before
+    any HIP call, and the message gives both sizes."""
+    import tp_reduction_rmsnorm_amd as frn
+    cap = noalloc_scratch_bytes()
+    assert cap == frn.NOALLOC_SCRATCH_BYTES == 16 << 20
+    R, k, H, T = 16, 16, 16384, 64
+    assert frn.split_rows(R, k, T, H)
+    need = R * T * H * 2
+    assert need > cap
+    assert call_moe_noalloc(lib, R=R, k=k, T=T, H=H, num_rows=T * k) == UNSUPPORTED
+    msg = lib.frn_last_error().decode()
+    assert "scratch" in msg and str(need) in msg and str(cap) in msg
+    # R = 8, H = 6144 fits up to 170 tokens, which the built-in rule never splits at
+    assert 8 * 170 * 6144 * 2 <= cap < 8 * 171 * 6144 * 2
+    assert lib.frn_workspace_bytes(100000, 6144, 8, 10) <= cap
+
+
 def call_ep(lib, R=2, k=3, T=4, H=64, num_rows=(12, 12), epilogue=0, src=None, shared=None,
             rows=None, w=None, nr_ptr=True, outs=None):
     lib.frn_ep_moe_finalize_reduce_norm.argtypes = [

@@ -35,6 +35,10 @@ int main(void) {
     EXPECT(frn_reduce_residual_rmsnorm(parts, 2, NULL, NULL, 1e-6f, 4, 64, NULL, NULL, NULL, 0,
                                        NULL) == FRN_ERR_INVALID);
     EXPECT(strlen(frn_last_error()) > 0);
+    EXPECT(frn_moe_finalize_reduce_norm_noalloc(parts, NULL, 2, NULL, NULL, 3, 12, FRN_EPI_RMSNORM,
+                                                NULL, NULL, NULL, 1e-6f, 0, 64, NULL, NULL,
+                                                NULL) == FRN_OK);
+    EXPECT(FRN_NOALLOC_SCRATCH_BYTES == 16777216u);
     EXPECT(strcmp(frn_status_string(FRN_OK), "") != 0);
     /* T == 0 is a no-op once the sizes are valid */
     EXPECT(frn_reduce_sandwich_norm(parts, 2, NULL, NULL, NULL, 1e-6f, 0, 64, NULL, NULL, NULL, 0,

@@ -1,0 +1,104 @@
+"""GPU test of frn_moe_finalize_reduce_norm_noalloc, called through the C ABI
+(via the binding): the MoE finalize + reduce + norm call whose split-row
+scratch is the library's own device array instead of a caller workspace.
+
+Two calls in a row, the second with a smaller input, both taking the
+split-row finalize (so both use the array, and the second runs on what the
+first left there): each output equals, bit for bit, that of the workspace
+entry point frn_moe_finalize_reduce_norm on the same inputs, and both equal
+the oracle.  A call above the split-row range (no scratch used) and a call
+whose scratch need exceeds the array (declined, outputs untouched) are
+checked too.
+"""
+import pytest
+import torch
+
+import workloads
+from tests import parity
+from tests.test_gpu_parity import DEV, frn, log, oracle_ref, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _epi(m, d):
+    return m.EPI_SANDWICH if d.epilogue == "sandwich" else m.EPI_RMSNORM
+
+
+def _noalloc(d):
+    m = frn()
+    out = torch.full((d.T, d.H), 7.0, dtype=torch.bfloat16, device=DEV)
+    rout = torch.full((d.T, d.H), 7.0, dtype=torch.bfloat16, device=DEV)
+    m.moe_finalize_reduce_norm_noalloc(d.expert_rows, d.topk_w, d.topk_idx, d.residual,
+                                       d.gamma1, d.gamma2, d.eps, out=out, residual_out=rout,
+                                       shared=d.shared, epilogue=_epi(m, d))
+    return out, rout
+
+
+def _with_workspace(d):
+    m = frn()
+    ws = torch.empty(m.workspace_bytes(d.T, d.H, d.R, d.k), dtype=torch.uint8, device=DEV)
+    return m.moe_finalize_reduce_norm(d.expert_rows, d.topk_w, d.topk_idx, d.residual,
+                                      d.gamma1, d.gamma2, d.eps, shared=d.shared,
+                                      epilogue=_epi(m, d), workspace=ws)
+
+
+def _same(name, got, want):
+    torch.cuda.synchronize()
+    parity.compare(name, workloads.bits(got), workloads.bits(want), min_exact=1.0)
+
+
+# (R, T, H, k, epilogue): the MoE finalize workload at T=64, then the same
+# shape at T=8; a sandwich pair at another shape; each pair large then small.
+PAIRS = [
+    ((8, 64, 6144, 10, "rmsnorm"), (8, 8, 6144, 10, "rmsnorm")),
+    ((4, 40, 2048, 3, "sandwich"), (4, 5, 2048, 3, "sandwich")),
+]
+
+
+@pytest.mark.parametrize("pair", PAIRS, ids=["moe_h6144_r8_k10", "sandwich_h2048_r4_k3"])
+def test_noalloc_matches_workspace_call_twice(pair):
+    m = frn()
+    for i, (R, T, H, k, epi) in enumerate(pair):
+        assert m.split_rows(R, k, T, H, m.EPI_SANDWICH if epi == "sandwich" else m.EPI_RMSNORM)
+        assert R * T * H * 2 <= m.NOALLOC_SCRATCH_BYTES
+        log(f"noalloc call {i}: R={R} T={T} H={H} k={k} {epi}")
+        inp = workloads.make(R, T, H, k=k, shared=True, epilogue=epi, seed=900 + 10 * i + R)
+        d = to_dev(inp)
+        y, x = _noalloc(d)
+        yw, xw = _with_workspace(d)
+        _same(f"noalloc call {i} T={T} out vs workspace call", y, yw)
+        _same(f"noalloc call {i} T={T} residual_out vs workspace call", x, xw)
+        ref = oracle_ref(inp)
+        parity.compare(f"noalloc call {i} T={T} out vs oracle", workloads.bits(y), ref.y)
+        parity.compare(f"noalloc call {i} T={T} residual_out vs oracle", workloads.bits(x),
+                       ref.xout)
+
+
+def test_noalloc_without_split_rows_and_beyond_its_scratch():
+    m = frn()
+    # above the split-row range: the one-row kernel, no scratch
+    R, T, H, k = 2, 300, 520, 2
+    assert not m.split_rows(R, k, T, H)
+    inp = workloads.make(R, T, H, k=k, shared=True, seed=977)
+    d = to_dev(inp)
+    log(f"noalloc call without scratch: R={R} T={T} H={H} k={k}")
+    y, x = _noalloc(d)
+    yw, xw = _with_workspace(d)
+    _same("noalloc one-row out vs workspace call", y, yw)
+    _same("noalloc one-row residual_out vs workspace call", x, xw)
+    # a split-row call needing more than the array holds is declined before
+    # any launch: the outputs keep their contents
+    R, T, H, k = 16, 64, 16384, 2
+    assert m.split_rows(R, k, T, H) and R * T * H * 2 > m.NOALLOC_SCRATCH_BYTES
+    e = [torch.zeros(T * k, H, dtype=torch.bfloat16, device=DEV) for _ in range(R)]
+    w = torch.ones(T, k, dtype=torch.float32, device=DEV)
+    idx = torch.arange(T * k, dtype=torch.int32, device=DEV).reshape(T, k)
+    res = torch.zeros(T, H, dtype=torch.bfloat16, device=DEV)
+    g = torch.ones(H, dtype=torch.float32, device=DEV)
+    out = torch.full((T, H), 3.0, dtype=torch.bfloat16, device=DEV)
+    rout = torch.full((T, H), 5.0, dtype=torch.bfloat16, device=DEV)
+    log("noalloc call beyond the scratch: declined")
+    with pytest.raises(m.FusedReduceNormUnsupported, match="scratch"):
+        m.moe_finalize_reduce_norm_noalloc(e, w, idx, res, g, out=out, residual_out=rout)
+    torch.cuda.synchronize()
+    assert bool((out == 3.0).all()) and bool((rout == 5.0).all())

@@ -13,6 +13,9 @@ Function names are the C entry points without their ``frn_`` prefix:
 * ``reduce_sandwich_norm``       FP32 sum + norm(gamma1) + residual + norm(gamma2)
 * ``moe_finalize_reduce_norm``   top-k finalize (+ shared expert) per rank,
                                  rounded to BF16, then either epilogue
+* ``moe_finalize_reduce_norm_noalloc``  the same for callers that cannot
+                                 allocate: no workspace argument, scratch
+                                 from the library's own device array
 * ``reduce_bf16``, ``moe_finalize_reduce_bf16``  split path, pass 1
 * ``split_reduce_norm``          both passes of the split path
 * ``moe_finalize``               the per-rank finalize alone (materialized)
@@ -54,6 +57,7 @@ EPI_SANDWICH = 1
 MAX_R = 16
 MAX_K = 16
 MAX_H = 16384
+NOALLOC_SCRATCH_BYTES = 16 << 20  # FRN_NOALLOC_SCRATCH_BYTES
 
 
 class FusedReduceNormError(RuntimeError):
@@ -92,6 +96,9 @@ _c_sandwich = _sig("frn_reduce_sandwich_norm", ctypes.c_int,
 _c_moe = _sig("frn_moe_finalize_reduce_norm", ctypes.c_int,
               [_P, _P, _I32, _P, _P, _I32, _I64, _I32, _P, _P, _P, _F32, _I64, _I64,
                _P, _P, _P, _SZ, _P])
+_c_moe_noalloc = _sig("frn_moe_finalize_reduce_norm_noalloc", ctypes.c_int,
+                      [_P, _P, _I32, _P, _P, _I32, _I64, _I32, _P, _P, _P, _F32, _I64, _I64,
+                       _P, _P, _P])
 _c_reduce_bf16 = _sig("frn_reduce_bf16", ctypes.c_int, [_P, _I32, _I64, _I64, _P, _P])
 _c_moe_bf16 = _sig("frn_moe_finalize_reduce_bf16", ctypes.c_int,
                    [_P, _P, _I32, _P, _P, _I32, _I64, _I64, _I64, _P, _P])
@@ -117,7 +124,8 @@ _c_last = _sig("frn_last_error", ctypes.c_char_p, [])
 _c_version = _sig("frn_version", ctypes.c_char_p, [])
 
 C_FUNCTIONS = ("frn_reduce_residual_rmsnorm", "frn_reduce_sandwich_norm",
-               "frn_moe_finalize_reduce_norm", "frn_reduce_bf16",
+               "frn_moe_finalize_reduce_norm", "frn_moe_finalize_reduce_norm_noalloc",
+               "frn_reduce_bf16",
                "frn_moe_finalize_reduce_bf16", "frn_split_reduce_norm", "frn_moe_finalize",
                "frn_ep_moe_finalize_reduce_norm", "frn_ep_moe_finalize",
                "frn_query", "frn_set_launch_table", "frn_launch_shape",
@@ -410,6 +418,38 @@ def moe_finalize_reduce_norm(expert_rows: TensorList, topk_weights: torch.Tensor
                   residual.data_ptr(), gamma1.data_ptr(),
                   gamma2.data_ptr() if gamma2 is not None else None, eps, T, H,
                   out.data_ptr(), residual_out.data_ptr(), ws, wsb, st))
+    return out, residual_out
+
+
+def moe_finalize_reduce_norm_noalloc(expert_rows: TensorList, topk_weights: torch.Tensor,
+                                     topk_rows: torch.Tensor, residual: torch.Tensor,
+                                     gamma1: torch.Tensor,
+                                     gamma2: Optional[torch.Tensor] = None, eps: float = 1e-6,
+                                     *, out: torch.Tensor, residual_out: torch.Tensor,
+                                     shared: Optional[TensorList] = None,
+                                     epilogue: int = EPI_RMSNORM,
+                                     stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """``moe_finalize_reduce_norm`` for callers that cannot allocate: the
+    outputs are the caller's (``out`` and ``residual_out`` are required) and
+    the split-row finalize's partials go to the library's own scratch array
+    on the GPU (``NOALLOC_SCRATCH_BYTES``), so neither this function nor the
+    C call allocates.  A call whose split-row finalize needs more scratch
+    raises ``FusedReduceNormUnsupported``.  Calls that may overlap in time
+    on one GPU share that array and race: serialise them."""
+    es, sh, T, H, k, num_rows, device = _check_finalize(expert_rows, topk_weights, topk_rows,
+                                                        shared)
+    _check_moe_epilogue(residual, gamma1, gamma2, epilogue, T, H, device)
+    if out is None or residual_out is None:
+        raise ValueError("out and residual_out are required: this call allocates nothing")
+    out, residual_out = _outputs(T, H, device, out, residual_out)
+    earr = _ptr_array(es)
+    sarr = _ptr_array(sh) if sh is not None else None
+    _check(_c_moe_noalloc(ctypes.cast(earr, _P),
+                          ctypes.cast(sarr, _P) if sarr is not None else None, len(es),
+                          topk_weights.data_ptr(), topk_rows.data_ptr(), k, num_rows, epilogue,
+                          residual.data_ptr(), gamma1.data_ptr(),
+                          gamma2.data_ptr() if gamma2 is not None else None, eps, T, H,
+                          out.data_ptr(), residual_out.data_ptr(), _stream(stream, device)))
     return out, residual_out
 
 

@@ -9,6 +9,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "frn_internal.h"
 
 #define FRN_API extern "C" __attribute__((visibility("default")))
@@ -341,6 +343,87 @@ FRN_API frn_status frn_moe_finalize_reduce_norm(
     return fused(expert_rows, shared, R, tp_routing(R, topk_w, topk_row, num_rows), k, epilogue,
                  residual_in, gamma1, gamma2, eps, T, H, out, residual_out, workspace,
                  workspace_bytes, stream);
+}
+
+// ------------------------------------------- the no-allocation entry point --- //
+
+// Scratch memory of frn_moe_finalize_reduce_norm_noalloc: the split-row
+// finalize's R x T x H BF16 partials, for callers that cannot allocate.
+// Each GPU the library runs on holds its own copy of this array until the
+// process ends.  Host code never uses the array's name as an address (on
+// the host it is a stand-in, not device memory): it uses the address that
+// hipGetSymbolAddress returns for the device, kept per device below.
+static __device__ __align__(256) uint8_t scratch[FRN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device, under the mutex
+
+// The device address of `scratch` on the device that runs `stream`, looked
+// up once per device with that device current.
+frn_status scratch_address(void* stream, void** out) {
+    int dev = -1;
+    hipError_t e = hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev);
+    if (e != hipSuccess)
+        return fail(FRN_ERR_HIP, "hipStreamGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(FRN_ERR_UNSUPPORTED, "device %d: the scratch table holds %d devices", dev,
+                    kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        int cur = -1;
+        if ((e = hipGetDevice(&cur)) != hipSuccess)
+            return fail(FRN_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess)
+            return fail(FRN_ERR_HIP, "hipSetDevice(%d) failed: %s", dev, hipGetErrorString(e));
+        void* ptr = nullptr;
+        const hipError_t es = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (cur != dev && (e = hipSetDevice(cur)) != hipSuccess)
+            return fail(FRN_ERR_HIP, "hipSetDevice(%d) failed: %s", cur, hipGetErrorString(e));
+        if (es != hipSuccess || ptr == nullptr)
+            return fail(FRN_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                        hipGetErrorString(es));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return FRN_OK;
+}
+
+}  // namespace
+
+FRN_API frn_status frn_moe_finalize_reduce_norm_noalloc(
+    const void* const* expert_rows, const void* const* shared, int32_t R, const float* topk_w,
+    const int32_t* topk_row, int32_t k, int64_t num_rows, int32_t epilogue,
+    const void* residual_in, const float* gamma1, const float* gamma2, float eps, int64_t T,
+    int64_t H, void* out, void* residual_out, void* stream) {
+    g_last_error[0] = '\0';
+    frn_status st = check_finalize_call(k, epilogue);
+    if (st != FRN_OK) return st;
+    if ((st = check_sizes(R, k, T, H, epilogue)) != FRN_OK || T == 0) return st;
+    Call c{};
+    if ((st = set_sources(c, expert_rows, shared, R, tp_routing(R, topk_w, topk_row, num_rows), k,
+                          T, H)) != FRN_OK)
+        return st;
+    if ((st = set_epilogue(c, epilogue, residual_in, gamma1, gamma2, eps, T, H, out,
+                           residual_out)) != FRN_OK)
+        return st;
+    if ((st = check_alias(c)) != FRN_OK) return st;
+    c.a.ws_p = nullptr;
+    if (frn::use_split_rows(R, H, k, false, epilogue, T)) {
+        const size_t need = frn::split_workspace_bytes(T, H, R);
+        if (need > (size_t)FRN_NOALLOC_SCRATCH_BYTES)
+            return fail(FRN_ERR_UNSUPPORTED,
+                        "the split-row finalize needs %zu bytes of scratch at R=%d T=%lld "
+                        "H=%lld; this entry point holds %zu (FRN_NOALLOC_SCRATCH_BYTES)",
+                        need, R, (long long)T, (long long)H,
+                        (size_t)FRN_NOALLOC_SCRATCH_BYTES);
+        void* p = nullptr;
+        if ((st = scratch_address(stream, &p)) != FRN_OK) return st;
+        c.a.ws_p = static_cast<uint4*>(p);
+    }
+    return run(c, epilogue, T, stream);
 }
 
 FRN_API frn_status frn_reduce_bf16(const void* const* partials, int32_t R, int64_t T, int64_t H,
