@@ -101,9 +101,10 @@ def pattern_probe(dev, cid=2, Ts=(1024, 4096)):
     if not os.path.exists(PROBE_LIB):
         build_probe()
     lib = ctypes.CDLL(PROBE_LIB)
-    lib.probe_rows.restype = ctypes.c_int
-    lib.probe_rows.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
-                               ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+    lib.probe_rows_mode.restype = ctypes.c_int
+    lib.probe_rows_mode.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+                                    ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_void_p]
     lib.probe_rows_pipelined.restype = ctypes.c_int
     lib.probe_rows_pipelined.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
                                          ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
@@ -132,13 +133,19 @@ def pattern_probe(dev, cid=2, Ts=(1024, 4096)):
                                                 d.residual.data_ptr())
                 arrays.append((srcs, (ctypes.c_void_p * 2)(o.data_ptr(), ro.data_ptr())))
 
-        def probe(i, arrays=arrays, T=T, H=w.H, nsrc=nsrc, vec=vec):
+        def probe(i, arrays=arrays, T=T, H=w.H, nsrc=nsrc, vec=vec, mode=0):
             srcs, dsts = arrays[i % len(arrays)]
-            st = lib.probe_rows(ctypes.cast(srcs, ctypes.c_void_p), nsrc,
-                                ctypes.cast(dsts, ctypes.c_void_p), 2, T, H, vec,
-                                torch.cuda.current_stream().cuda_stream)
+            st = lib.probe_rows_mode(ctypes.cast(srcs, ctypes.c_void_p), nsrc,
+                                     ctypes.cast(dsts, ctypes.c_void_p), 2, T, H, vec, mode,
+                                     torch.cuda.current_stream().cuda_stream)
             if st != 0:
-                raise RuntimeError(f"probe_rows failed ({st})")
+                raise RuntimeError(f"probe_rows_mode failed ({st})")
+
+        def probe_reads(i):
+            probe(i, mode=1)
+
+        def probe_writes(i):
+            probe(i, mode=2)
 
         def probe_pipelined(i, arrays=arrays, T=T, H=w.H, nsrc=nsrc, vec=vec):
             srcs, dsts = arrays[i % len(arrays)]
@@ -153,19 +160,30 @@ def pattern_probe(dev, cid=2, Ts=(1024, 4096)):
         call = r.call
         r.call = probe
         probe_us = r.graph_us()
+        r.call = probe_reads
+        reads_us = r.graph_us()
+        r.call = probe_writes
+        writes_us = r.graph_us()
         pipe_us = None
         if pipelined:
             r.call = probe_pipelined
             pipe_us = r.graph_us()
         r.call = call
         pattern_bytes = T * w.H * 2 * (nsrc + 2)
+        read_bytes, write_bytes = T * w.H * 2 * nsrc, T * w.H * 2 * 2
         rows.append(dict(workload=w.name, T=T, vectors_per_lane=vec, rows_read=nsrc,
                          kernel="rows_pipelined_kernel" if pipelined else "row_kernel",
                          kernel_us=round(kernel_us, 3), kernel_GBps=round(r.bytes / kernel_us / 1e3, 1),
                          pattern_us=round(probe_us, 3),
                          pattern_GBps=round(pattern_bytes / probe_us / 1e3, 1),
                          pattern_frac_of_peak=round(pattern_bytes / probe_us / 1e3 / PEAK_GBS, 4),
-                         kernel_over_pattern=round(kernel_us / probe_us, 4)))
+                         kernel_over_pattern=round(kernel_us / probe_us, 4),
+                         reads_only_us=round(reads_us, 3),
+                         reads_only_GBps=round(read_bytes / reads_us / 1e3, 1),
+                         writes_only_us=round(writes_us, 3),
+                         writes_only_GBps=round(write_bytes / writes_us / 1e3, 1),
+                         reads_plus_writes_over_pattern=round((reads_us + writes_us) / probe_us,
+                                                              4)))
         if pipelined:
             rows[-1].update(
                 pipelined_pattern_us=round(pipe_us, 3),

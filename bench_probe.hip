@@ -35,7 +35,11 @@ __device__ __forceinline__ void st_nt(uint4* p, const uint4& q) {
     __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(p));
 }
 
-template <int V>
+// MODE 0: read the source rows, write the destination rows.  MODE 1: read
+// only -- the destination rows are written only where the XOR of a lane's
+// loads equals a sentinel (which keeps every load live and on these inputs
+// writes nothing).  MODE 2: write only, no loads.
+template <int V, int MODE>
 __global__ __launch_bounds__(1024) void probe_rows_kernel(const ProbeArgs a) {
     const int64_t row = (int64_t)blockIdx.x * a.nvec;
     int vi[V];
@@ -50,7 +54,7 @@ __global__ __launch_bounds__(1024) void probe_rows_kernel(const ProbeArgs a) {
     // every load of a chunk issued before any is consumed, as in the kernel
     // (5 rows -- partials and residual of the headline call -- in one chunk)
     constexpr int CH = V == 4 ? 5 : 8;
-    for (int r0 = 0; r0 < a.nsrc; r0 += CH) {
+    for (int r0 = 0; MODE != 2 && r0 < a.nsrc; r0 += CH) {
         uint4 q[CH][V];
 #pragma unroll
         for (int c = 0; c < CH; ++c)
@@ -71,8 +75,20 @@ __global__ __launch_bounds__(1024) void probe_rows_kernel(const ProbeArgs a) {
     }
     for (int d = 0; d < a.ndst; ++d)
 #pragma unroll
-        for (int j = 0; j < V; ++j)
-            if (ok[j]) st_nt(a.dst[d] + row + vi[j], acc[j]);
+        for (int j = 0; j < V; ++j) {
+            const bool write = MODE != 1 || (acc[j].x == 0x9E3779B9u && acc[j].y == 0x7F4A7C15u);
+            if (ok[j] && write) st_nt(a.dst[d] + row + vi[j], acc[j]);
+        }
+}
+
+template <int MODE>
+void launch_rows(const ProbeArgs& a, int64_t T, int threads, int vec, hipStream_t s) {
+    if (vec == 1)
+        hipLaunchKernelGGL((probe_rows_kernel<1, MODE>), dim3((unsigned)T), dim3(threads), 0, s, a);
+    else if (vec == 2)
+        hipLaunchKernelGGL((probe_rows_kernel<2, MODE>), dim3((unsigned)T), dim3(threads), 0, s, a);
+    else
+        hipLaunchKernelGGL((probe_rows_kernel<4, MODE>), dim3((unsigned)T), dim3(threads), 0, s, a);
 }
 
 // The row-pipelined kernel's pattern: one workgroup per CU walks rows b,
@@ -166,13 +182,15 @@ extern "C" __attribute__((visibility("default"))) int probe_rows_pipelined(
 }
 
 // src: nsrc device pointers to [T,H] BF16; dst: ndst device pointers to
-// [T,H] BF16; vec: vectors per lane (1, 2 or 4).  Returns 0 on success, 1 on
-// bad arguments, 2 if the launch failed.
-extern "C" __attribute__((visibility("default"))) int probe_rows(
+// [T,H] BF16; vec: vectors per lane (1, 2 or 4); mode: 0 read and write, 1
+// read only, 2 write only (see probe_rows_kernel).  Returns 0 on success, 1
+// on bad arguments, 2 if the launch failed.
+extern "C" __attribute__((visibility("default"))) int probe_rows_mode(
     const void* const* src, int nsrc, void* const* dst, int ndst, int64_t T, int64_t H, int vec,
-    void* stream) {
-    if (nsrc < 1 || nsrc > kMaxSrc || ndst < 0 || ndst > kMaxDst || T < 1 || H < 8 ||
-        H % 8 != 0 || H > 16384 || T > 4194303 || !(vec == 1 || vec == 2 || vec == 4))
+    int mode, void* stream) {
+    if (nsrc < 1 || nsrc > kMaxSrc || ndst < 1 || ndst > kMaxDst || T < 1 || H < 8 ||
+        H % 8 != 0 || H > 16384 || T > 4194303 || !(vec == 1 || vec == 2 || vec == 4) ||
+        mode < 0 || mode > 2)
         return 1;
     ProbeArgs a{};
     for (int r = 0; r < nsrc; ++r) {
@@ -190,11 +208,18 @@ extern "C" __attribute__((visibility("default"))) int probe_rows(
     const int threads = ((lanes + 63) / 64) * 64;
     if (threads > 1024) return 1;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (vec == 1)
-        hipLaunchKernelGGL(probe_rows_kernel<1>, dim3((unsigned)T), dim3(threads), 0, s, a);
-    else if (vec == 2)
-        hipLaunchKernelGGL(probe_rows_kernel<2>, dim3((unsigned)T), dim3(threads), 0, s, a);
+    if (mode == 0)
+        launch_rows<0>(a, T, threads, vec, s);
+    else if (mode == 1)
+        launch_rows<1>(a, T, threads, vec, s);
     else
-        hipLaunchKernelGGL(probe_rows_kernel<4>, dim3((unsigned)T), dim3(threads), 0, s, a);
+        launch_rows<2>(a, T, threads, vec, s);
     return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+// probe_rows_mode with mode 0.
+extern "C" __attribute__((visibility("default"))) int probe_rows(
+    const void* const* src, int nsrc, void* const* dst, int ndst, int64_t T, int64_t H, int vec,
+    void* stream) {
+    return probe_rows_mode(src, nsrc, dst, ndst, T, H, vec, 0, stream);
 }

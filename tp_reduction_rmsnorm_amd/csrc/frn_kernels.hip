@@ -647,8 +647,10 @@ __global__ __launch_bounds__(1024) void row_kernel(const RowArgs a) {
 
 // Per-rank MoE finalize of T rows, one row slice of one rank per workgroup:
 // workgroup (t, r, c) writes bf16(finalize) of vectors [c * kSplitThreads,
-// (c + 1) * kSplitThreads) of rank r, token t to row t of part_out[r].
-template <bool EARLY_SHARED>
+// (c + 1) * kSplitThreads) of rank r, token t to row t of part_out[r].  C:
+// top-k slots loaded per chunk (the launch takes C >= k, so all of a rank's
+// rows go out in one memory round trip).
+template <bool EARLY_SHARED, int C>
 __global__ __launch_bounds__(kSplitThreads) void finalize_slices_kernel(const RowArgs a, int S,
                                                                         int64_t t0) {
     const int c = blockIdx.x % S;
@@ -658,8 +660,21 @@ __global__ __launch_bounds__(kSplitThreads) void finalize_slices_kernel(const Ro
     L.vi[0] = c * kSplitThreads + threadIdx.x;
     L.ok[0] = L.vi[0] < a.nvec;
     float acc[1][8];
-    finalize_rank<1, 16, EARLY_SHARED>(a, r, t, L, acc);
+    finalize_rank<1, C, EARLY_SHARED>(a, r, t, L, acc);
     if (L.ok[0]) a.part_out[r][t * a.nvec + L.vi[0]] = narrow(acc[0]);
+}
+
+// Calls f(std::integral_constant<int, C>) with the top-k chunk for k slots:
+// the smallest of 4, 8, 12, 16 that holds all k.  A chunk's loads are
+// registers whether or not a slot is used, so a chunk sized to k keeps the
+// register count, and with it the workgroups resident per CU, as high as
+// one round trip for all of a rank's rows allows.
+template <class F>
+__device__ __host__ auto with_topk_chunk(int k, F f) {
+    if (k <= 4) return f(std::integral_constant<int, 4>{});
+    if (k <= 8) return f(std::integral_constant<int, 8>{});
+    if (k <= 12) return f(std::integral_constant<int, 12>{});
+    return f(std::integral_constant<int, 16>{});
 }
 
 // Gamma rows staged in LDS (rows_pipelined_kernel): FP32 vectors in the
@@ -885,7 +900,16 @@ template <int EPI, int FIN, int V>
 hipError_t launch_c(const RowArgs& a, int64_t T, int threads, hipStream_t stream) {
     constexpr int CMAX = 16 / V;
     if constexpr (FIN == kFinTp) {
-        return launch<EPI, FIN, V, (V == 1 ? 16 : 4)>(a, T, threads, stream);
+        // Split pass 1 keeps the 16-slot chunk: sized to k (more tokens per
+        // CU) it measured 4% slower (H=7168 R=2 k=8 T=4096), the fused
+        // calls 0-2% faster.
+        if constexpr (V == 1 && EPI != kStoreSum) {
+            return with_topk_chunk(a.k, [&](auto c) {
+                return launch<EPI, FIN, V, decltype(c)::value>(a, T, threads, stream);
+            });
+        } else {
+            return launch<EPI, FIN, V, (V == 1 ? 16 : 4)>(a, T, threads, stream);
+        }
     } else if constexpr (FIN == kFinEp) {
         return launch<EPI, FIN, V, (V == 1 ? 8 : 4)>(a, T, threads, stream);
     } else {
@@ -926,12 +950,16 @@ hipError_t launch_finalize(const RowArgs& a, int64_t T, hipStream_t stream) {
         const int64_t n = (T - t0 < chunk ? T - t0 : chunk) * per_token;
         // Under expert-parallel routing most ranks hold no shared row, and the
         // registers of an early shared load would cost occupancy for nothing.
-        if (a.ep)
-            hipLaunchKernelGGL(finalize_slices_kernel<false>, dim3((unsigned)n),
-                               dim3(kSplitThreads), 0, stream, a, S, t0);
-        else
-            hipLaunchKernelGGL(finalize_slices_kernel<true>, dim3((unsigned)n),
-                               dim3(kSplitThreads), 0, stream, a, S, t0);
+        with_topk_chunk(a.k, [&](auto c) {
+            constexpr int C = decltype(c)::value;
+            if (a.ep)
+                hipLaunchKernelGGL((finalize_slices_kernel<false, C>), dim3((unsigned)n),
+                                   dim3(kSplitThreads), 0, stream, a, S, t0);
+            else
+                hipLaunchKernelGGL((finalize_slices_kernel<true, C>), dim3((unsigned)n),
+                                   dim3(kSplitThreads), 0, stream, a, S, t0);
+            return 0;
+        });
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
