@@ -301,15 +301,18 @@ frn_status frn_query(int32_t R, int32_t k, int64_t T, int64_t H, int32_t epilogu
  * vectors of 8 BF16 values ("vec").  The best choice depends on H, R, k,
  * the epilogue and T, and shapes tuned for one hidden size do not carry
  * over to another (SGLang PR #34134: the shipped H=8192 profiles misfit
- * H=6144).  A built-in rule, measured on MI355X, applies unless a table of
- * tuned rules overrides it.  Table text: one rule per line, '#' starts a
- * comment:
+ * H=6144).  Three layers of rules decide, the first with a rule for the
+ * call winning: the caller's table (this call, or FRN_LAUNCH_TABLE); the
+ * table measured on MI355X for the shapes of the pages' workloads, which
+ * the library carries compiled in; and a hand-fitted rule, also measured on
+ * MI355X, for every other shape.  Table text: one rule per line, '#'
+ * starts a comment:
  *     H  R  k  epilogue  Tmin  Tmax  vec
  * H, R, k, Tmin, Tmax: integers or '*' (any); k = 0 means no finalize;
  * epilogue: rmsnorm | sandwich | sum (split pass 1) for calls without
  * expert-parallel routing, ep-rmsnorm | ep-sandwich | ep-* for
  * frn_ep_moe_finalize_reduce_norm, or * (every call); vec: 1 | 2 | 4,
- * p1 | p2, or split | fused.  A numeric vec sets the one-row kernel's
+ * p1 | p2, split | fused, or builtin.  A numeric vec sets the one-row kernel's
  * shape, p1 / p2 the row-pipelined kernel with 1 / 2 vectors per lane: the
  * first such rule that matches a call and fits it decides (one-row kernel:
  * at most 1024 lanes, vec 4 only without finalize and outside split pass 1;
@@ -317,10 +320,15 @@ frn_status frn_query(int32_t R, int32_t k, int64_t T, int64_t H, int32_t epilogu
  * decide, for a finalize call (k >= 1) given a large enough workspace,
  * whether it takes the split-row finalize (see frn_workspace_bytes) or the
  * one-row kernel: the first such rule that matches decides, and T above 256
- * is never split.  Results are identical for every choice; only speed
- * changes.  tp_reduction_rmsnorm_amd/tune.py measures a table.  frn_set_launch_table(NULL) restores the
- * built-in rule; an unparsable text returns FRN_ERR_INVALID (the line is in
- * frn_last_error) and leaves the table as it was.  If no table was set
+ * is never split.  builtin: the calls the rule matches take the
+ * hand-fitted rule for both questions, whatever later rules and the
+ * compiled-in table say ("* * * * 0 * builtin" alone turns the measured
+ * table off).  Results are identical for every choice; only speed
+ * changes.  tp_reduction_rmsnorm_amd/tune.py measures a table.
+ * frn_set_launch_table(NULL) removes the caller's table (the compiled-in
+ * table and the hand-fitted rule then decide); an unparsable text returns
+ * FRN_ERR_INVALID (the line is in frn_last_error) and leaves the table as
+ * it was.  If no table was set
  * before the first launch, the file named by the environment variable
  * FRN_LAUNCH_TABLE (if any) is loaded.  Thread-safe; affects later launches
  * only.
@@ -368,9 +376,10 @@ size_t frn_workspace_bytes(int64_t max_T, int64_t H, int32_t R, int32_t k);
  * FRN_EPI_SANDWICH, OR'ed with FRN_SHAPE_EP for a call of
  * frn_ep_moe_finalize_reduce_norm.  The split-row finalize writes and
  * re-reads R partial rows per token, so it pays only while the one-row
- * kernel is bound by its memory round trips: the built-in rule, measured on
+ * kernel is bound by its memory round trips.  The compiled-in measured
+ * table decides the shapes it covers; the hand-fitted rule, measured on
  * MI355X, takes it up to 8 to 192 tokens depending on R, H and the routing;
- * launch-table split / fused rules override it.
+ * a caller's split / fused rules override both (see frn_set_launch_table).
  */
 int32_t frn_split_rows(int32_t R, int32_t k, int64_t T, int64_t H, int32_t epilogue);
 
@@ -385,11 +394,13 @@ int32_t frn_split_rows(int32_t R, int32_t k, int64_t T, int64_t H, int32_t epilo
  * workgroup, the reads of all resident rows come first and the writes
  * after).  It serves 1 <= R <= 4, H/8 a multiple of 64 * vec (at most 1024
  * lanes with one vector per lane, 512 with two) and gamma rows of at most
- * 64 KiB.  The built-in rule, measured on MI355X, takes it with two
- * vectors per lane from T = 1536 for 4096 < H < 8192, for the sandwich
- * epilogue and for residual + RMSNorm at R = 1 (where it measured faster or
- * even); launch-table p1 / p2 rules and numeric vec rules override it.  Results are bit-identical either
- * way: the same arithmetic in the same order, row by row.
+ * 64 KiB.  The compiled-in measured table decides the shapes it covers;
+ * the hand-fitted rule, measured on MI355X,
+ * takes it with two vectors per lane from T = 1536 for 4096 < H < 8192,
+ * for the sandwich epilogue and for residual + RMSNorm at R = 1 (where it
+ * measured faster or even); a caller's p1 / p2 and numeric vec rules
+ * override both.  Results are bit-identical either way: the same
+ * arithmetic in the same order, row by row.
  */
 int32_t frn_launch_pipelined(int32_t R, int32_t k, int64_t T, int64_t H, int32_t epilogue);
 

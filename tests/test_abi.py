@@ -108,6 +108,31 @@ def ptrs(*xs):
     return ctypes.cast((ctypes.c_void_p * len(xs))(*xs), P)
 
 
+TUNED_INC = os.path.join(ROOT, "tp_reduction_rmsnorm_amd", "csrc", "frn_tuned_mi355x.inc")
+HAND_FITTED = "* * * * 0 * builtin\n"   # every call: the hand-fitted rule
+
+
+@pytest.fixture
+def hand_fitted():
+    """Every call under the hand-fitted rule for the test's duration."""
+    import tp_reduction_rmsnorm_amd as frn
+    frn.set_launch_table(HAND_FITTED)
+    yield
+    frn.set_launch_table(None)
+
+
+def tuned_table_text():
+    """The launch table compiled into the library (the raw string in
+    frn_tuned_mi355x.inc)."""
+    text = open(TUNED_INC).read()
+    return text.split('R"FRN_TABLE(\n', 1)[1].split(')FRN_TABLE"', 1)[0]
+
+
+def tuned_rules():
+    return [l.split() for l in tuned_table_text().splitlines()
+            if l.strip() and not l.lstrip().startswith("#")]
+
+
 def call_rms(lib, R=2, T=4, H=64, eps=1e-6, parts=None, residual=None, gamma=None,
              out=None, rout=None):
     parts = ptrs(*[addr(10 + r) for r in range(R)]) if parts is None else parts
@@ -326,22 +351,31 @@ def test_pass1_rejects(lib):
 
 
 def test_workspace_bytes(lib):
-    assert lib.frn_workspace_bytes(8, 6144, 8, 10) == 8 * 8 * 6144 * 2
-    # covers the largest T either routing splits at: R=8 H=6144 -> 96 (TP)
-    assert lib.frn_workspace_bytes(5000, 6144, 8, 10) == 96 * 8 * 6144 * 2
-    assert lib.frn_workspace_bytes(5000, 7168, 2, 8) == 32 * 2 * 7168 * 2
-    assert lib.frn_workspace_bytes(5000, 4096, 2, 4) == 8 * 2 * 4096 * 2   # EP only
-    assert lib.frn_workspace_bytes(64, 5120, 4, 0) == 0      # no finalize: none used
-    assert lib.frn_workspace_bytes(64, 5124, 4, 2) == 0      # unsupported H
-    assert lib.frn_workspace_bytes(0, 5120, 4, 2) == 0
-    assert lib.frn_workspace_bytes(8, 5120, 4, 17) == 0      # k beyond FRN_MAX_K
+    lib.frn_set_launch_table.argtypes = [ctypes.c_char_p]
+    assert lib.frn_set_launch_table(HAND_FITTED.encode()) == OK
+    try:
+        assert lib.frn_workspace_bytes(8, 6144, 8, 10) == 8 * 8 * 6144 * 2
+        # covers the largest T either routing splits at: R=8 H=6144 -> 96 (TP)
+        assert lib.frn_workspace_bytes(5000, 6144, 8, 10) == 96 * 8 * 6144 * 2
+        assert lib.frn_workspace_bytes(5000, 4096, 2, 4) == 8 * 2 * 4096 * 2   # EP only
+        assert lib.frn_workspace_bytes(64, 5120, 4, 0) == 0      # no finalize: none used
+        assert lib.frn_workspace_bytes(64, 5124, 4, 2) == 0      # unsupported H
+        assert lib.frn_workspace_bytes(0, 5120, 4, 2) == 0
+        assert lib.frn_workspace_bytes(8, 5120, 4, 17) == 0      # k beyond FRN_MAX_K
+        # the size covers the compiled-in table's split rules too
+        assert lib.frn_workspace_bytes(5000, 7168, 2, 8) == max(
+            [32] + [int(r[5]) for r in tuned_rules()
+                    if r[:3] == ["7168", "2", "8"] and r[6] == "split"]) * 2 * 7168 * 2
+    finally:
+        lib.frn_set_launch_table(None)
 
 
 def test_split_rows_builtin_rule():
-    """The built-in choice of the split-row finalize at its measured edges."""
+    """The hand-fitted choice of the split-row finalize at its measured
+    edges (a 'builtin' rule turns the compiled-in table off)."""
     import tp_reduction_rmsnorm_amd as frn
     S, EP = frn.EPI_SANDWICH, True
-    frn.set_launch_table(None)
+    frn.set_launch_table(HAND_FITTED)
     cases = [  # R, k, H, ep, T, expected
         (8, 10, 6144, False, 1, True), (8, 10, 6144, False, 96, True),
         (8, 10, 6144, False, 97, False), (8, 10, 6144, False, 256, False),
@@ -357,13 +391,16 @@ def test_split_rows_builtin_rule():
         (8, 10, 5120, False, 96, True), (8, 10, 5120, False, 97, False),
         (16, 6, 3072, EP, 32, True), (16, 6, 3072, EP, 33, False),
     ]
-    for R, k, H, ep, T, want in cases:
-        assert frn.split_rows(R, k, T, H, ep=ep) is want, (R, k, H, ep, T)
-        assert frn.split_rows(R, k, T, H, S, ep=ep) is want, (R, k, H, ep, T)
-    assert not frn.split_rows(8, 0, 8, 6144)                 # no finalize
-    assert not frn.split_rows(8, 10, 0, 6144)                # empty call
-    assert not frn.split_rows(8, 10, 8, 6148)                # unsupported H
-    assert not frn.split_rows(8, 10, 8, 6144, frn.EPI_SUM)   # split pass 1 has no workspace
+    try:
+        for R, k, H, ep, T, want in cases:
+            assert frn.split_rows(R, k, T, H, ep=ep) is want, (R, k, H, ep, T)
+            assert frn.split_rows(R, k, T, H, S, ep=ep) is want, (R, k, H, ep, T)
+        assert not frn.split_rows(8, 0, 8, 6144)                 # no finalize
+        assert not frn.split_rows(8, 10, 0, 6144)                # empty call
+        assert not frn.split_rows(8, 10, 8, 6148)                # unsupported H
+        assert not frn.split_rows(8, 10, 8, 6144, frn.EPI_SUM)   # split pass 1: no workspace
+    finally:
+        frn.set_launch_table(None)
 
 
 def test_split_rows_is_covered_by_workspace_bytes(lib):
@@ -516,9 +553,8 @@ def test_python_layer_requires_gpu_tensors():
 
 # ------------------------------------------------------- launch tables --- #
 
-def test_launch_shape_builtin_rule():
+def test_launch_shape_builtin_rule(hand_fitted):
     import tp_reduction_rmsnorm_amd as frn
-    frn.set_launch_table(None)
     S = frn.EPI_SANDWICH
     assert frn.launch_shape(4, 0, 1, 5120, S) == (640, 1)      # small T: one vector ...
     assert frn.launch_shape(8, 0, 200, 6144, 0) == (768, 1)    # ... up to 896 lanes
@@ -549,11 +585,11 @@ def test_launch_shape_builtin_rule():
         frn.launch_shape(8, 10, 1024, 6144, frn.EPI_SUM, ep=True)
 
 
-def test_pipelined_builtin_rule():
-    """Calls without finalize take the row-pipelined kernel (one workgroup
-    per CU walking the rows) from T = 1536 where it serves them."""
+def test_pipelined_builtin_rule(hand_fitted):
+    """Under the hand-fitted rule, calls without finalize take the
+    row-pipelined kernel (one workgroup per CU walking the rows) from
+    T = 1536 where it serves them."""
     import tp_reduction_rmsnorm_amd as frn
-    frn.set_launch_table(None)
     S, N = frn.EPI_SANDWICH, frn.EPI_RMSNORM
     assert frn.launch_pipelined(4, 0, 4096, 5120, S)
     assert frn.launch_shape(4, 0, 4096, 5120, S) == (320, 2)
@@ -765,14 +801,77 @@ def test_builtin_launch_shapes_always_fit():
                                 assert v != 4, (H, R, k, epi, T)
 
 
-def test_shipped_launch_table_parses_and_routes():
-    """The measured table shipped with the package loads, and its split /
-    fused rules and its row-pipelined rules route calls as the table says
-    (the edges are read from the table, which a re-tune may move)."""
+def test_compiled_in_table_decides_its_shapes_by_default():
+    """With no caller table and no environment variable, every rule of the
+    table compiled into the library decides its shapes: at each range's
+    first and last T, launch_shape / launch_pipelined / split_rows give what
+    the table says (the edges are read from the table, which a re-tune may
+    move).  The text also loads as a caller table."""
     import tp_reduction_rmsnorm_amd as frn
-    path = os.path.join(ROOT, "tp_reduction_rmsnorm_amd", "launch_table_mi355x.txt")
-    text = open(path).read()
-    rules = [l.split() for l in text.splitlines() if l.strip() and not l.startswith("#")]
+    frn.set_launch_table(tuned_table_text())           # it parses
+    frn.set_launch_table(None)                         # the defaults
+    assert os.environ.get("FRN_LAUNCH_TABLE") is None
+    epis = {"rmsnorm": frn.EPI_RMSNORM, "sandwich": frn.EPI_SANDWICH, "sum": frn.EPI_SUM}
+    rules = tuned_rules()
+    assert len({tuple(r[:4]) for r in rules}) >= 9      # the nine tuned shapes
+    seen = set()
+    for H, R, k, epi, lo, hi, v in rules:
+        H, R, k = int(H), int(R), int(k)
+        ep = epi.startswith("ep-")
+        e = epis[epi.replace("ep-", "")]
+        ts = [max(int(lo), 1)] + ([int(hi)] if hi != "*" else [])
+        for T in ts:
+            if (H, R, k, epi, T, v in ("split", "fused")) in seen:
+                continue                            # an earlier rule decides this T
+            seen.add((H, R, k, epi, T, v in ("split", "fused")))
+            if v in ("split", "fused"):
+                assert frn.split_rows(R, k, T, H, e, ep=ep) == (v == "split"), (H, R, k, epi, T)
+            elif v in ("p1", "p2"):
+                assert frn.launch_pipelined(R, k, T, H, e), (H, R, k, epi, T)
+                assert frn.launch_shape(R, k, T, H, e)[1] == int(v[1])
+            else:
+                assert not ep and frn.launch_shape(R, k, T, H, e)[1] == int(v) or \
+                    ep and frn.launch_shape(R, k, T, H, e, ep=True)[1] == int(v), (H, R, k, epi, T)
+                if k == 0 and epi != "sum":
+                    assert not frn.launch_pipelined(R, k, T, H, e), (H, R, k, epi, T)
+
+
+def test_compiled_in_table_file_is_what_the_tuner_writes():
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "frn_tune", os.path.join(ROOT, "tp_reduction_rmsnorm_amd", "tune.py"))
+    tune = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(tune)
+    assert tune.as_inc(tuned_table_text()) == open(TUNED_INC).read()
+
+
+def test_caller_table_and_builtin_rule_override_the_compiled_in_table():
+    import tp_reduction_rmsnorm_amd as frn
+    S = frn.EPI_SANDWICH
+    rules = tuned_rules()
+    assert ["5120", "4", "0", "sandwich", "2049", "*", "p2"] in rules
+    try:
+        frn.set_launch_table(None)
+        assert frn.launch_pipelined(4, 0, 4096, 5120, S)
+        frn.set_launch_table("5120 4 0 sandwich 4000 5000 4\n")   # a caller rule wins
+        assert not frn.launch_pipelined(4, 0, 4096, 5120, S)
+        assert frn.launch_shape(4, 0, 4096, 5120, S) == (192, 4)
+        assert frn.launch_pipelined(4, 0, 8192, 5120, S)          # outside it: the table
+        frn.set_launch_table("5120 4 0 sandwich 0 1200 builtin\n")
+        assert not frn.launch_pipelined(4, 0, 1100, 5120, S)      # hand-fitted: not below 1536
+        assert frn.launch_pipelined(4, 0, 1300, 5120, S)          # the table again
+        frn.set_launch_table("6144 8 10 rmsnorm 0 256 builtin\n")
+        assert frn.split_rows(8, 10, 96, 6144) and not frn.split_rows(8, 10, 97, 6144)
+    finally:
+        frn.set_launch_table(None)
+
+
+def test_shipped_launch_table_parses_and_routes():
+    """The measured table, loaded as a caller table, routes its split /
+    fused rules and its row-pipelined rules as it says."""
+    import tp_reduction_rmsnorm_amd as frn
+    text = tuned_table_text()
+    rules = tuned_rules()
     epis = {"rmsnorm": frn.EPI_RMSNORM, "sandwich": frn.EPI_SANDWICH}
     try:
         frn.set_launch_table(text)

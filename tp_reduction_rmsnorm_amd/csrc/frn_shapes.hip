@@ -1,14 +1,18 @@
 // frn_shapes.hip -- launch shapes of row_kernel and the choice between the
-// split-row and the one-row finalize: built-in rules measured on MI355X,
-// and an optional table of tuned rules that overrides them.  Launch
-// profiles tuned for one hidden size do not carry over to another (SGLang PR
-// #34134: shipped profiles for H=8192 misfit H=6144), so a deployment can
-// measure its own shapes (tp_reduction_rmsnorm_amd/tune.py) and load them.
+// split-row and the one-row finalize.  Three layers of rules, the first
+// that has a rule for a call deciding it: a caller's table
+// (frn_set_launch_table, FRN_LAUNCH_TABLE), the table measured on MI355X
+// that is compiled in (frn_tuned_mi355x.inc), and the hand-fitted rules
+// below for every shape the measured table does not cover.  Launch profiles
+// tuned for one hidden size do not carry over to another (SGLang PR #34134:
+// shipped profiles for H=8192 misfit H=6144), so a deployment can measure
+// its own shapes (tp_reduction_rmsnorm_amd/tune.py) and load them.
 #include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
 
 #include <atomic>
+#include <initializer_list>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -22,7 +26,9 @@ namespace {
 // tmax].  ep: 1 for calls with expert-parallel routing, 0 for the others.
 // vec 1, 2 or 4: vectors per lane of row_kernel, or with pipe set, of
 // rows_pipelined_kernel (1 or 2); kSplitRule / kFusedRule: a finalize call
-// given a workspace takes the split-row / the one-row finalize.
+// given a workspace takes the split-row / the one-row finalize;
+// kBuiltinRule: the calls it matches take the hand-fitted rules for both
+// questions, whatever the later rules and the compiled-in table say.
 struct Rule {
     int64_t H, R, k, epilogue, ep;
     int64_t tmin, tmax;
@@ -32,11 +38,18 @@ struct Rule {
 
 constexpr int kSplitRule = -1;
 constexpr int kFusedRule = -2;
+constexpr int kBuiltinRule = -3;
 
 std::mutex g_mu;
-std::vector<Rule> g_rules;
+std::vector<Rule> g_rules;   // the caller's table
+std::vector<Rule> g_tuned;   // the compiled-in measured table
 bool g_env_checked = false;
+bool g_tuned_parsed = false;
 std::string g_parse_error;
+
+const char kTunedTable[] =
+#include "frn_tuned_mi355x.inc"
+    ;
 
 bool parse_field(const char* tok, int64_t* out) {
     if (strcmp(tok, "*") == 0) {
@@ -101,8 +114,9 @@ bool parse(const char* text, std::vector<Rule>& out, std::string& err) {
         int64_t vec = 0;
         const bool last_ok =
             tok.size() == 7 &&
-            (tok[6] == "split"   ? (vec = kSplitRule, true)
-             : tok[6] == "fused" ? (vec = kFusedRule, true)
+            (tok[6] == "split"     ? (vec = kSplitRule, true)
+             : tok[6] == "fused"   ? (vec = kFusedRule, true)
+             : tok[6] == "builtin" ? (vec = kBuiltinRule, true)
              : tok[6] == "p1"    ? (vec = 1, r.pipe = true, true)
              : tok[6] == "p2"    ? (vec = 2, r.pipe = true, true)
                                  : parse_field(tok[6].c_str(), &vec) &&
@@ -113,7 +127,8 @@ bool parse(const char* text, std::vector<Rule>& out, std::string& err) {
             !parse_field(tok[4].c_str(), &r.tmin) || !parse_field(tok[5].c_str(), &r.tmax)) {
             err = "launch table line " + std::to_string(lineno) +
                   ": expected 'H R k epilogue Tmin Tmax vec' (numbers or *, epilogue "
-                  "rmsnorm|sandwich|sum|ep-rmsnorm|ep-sandwich|ep-*|*, vec 1|2|4|p1|p2|split|fused)";
+                  "rmsnorm|sandwich|sum|ep-rmsnorm|ep-sandwich|ep-*|*, vec "
+                  "1|2|4|p1|p2|split|fused|builtin)";
             return false;
         }
         if (r.tmin < 0) r.tmin = 0;
@@ -153,7 +168,25 @@ void load_env_table_locked() {
     g_rules.swap(rules);
 }
 
-// The built-in rule, from graph-replay sweeps on MI355X (the sandwich
+// The compiled-in measured table, parsed at the first use (it is checked by
+// a test; a table that failed to parse would leave the hand-fitted rules).
+void load_tuned_locked() {
+    if (g_tuned_parsed) return;
+    g_tuned_parsed = true;
+    std::string err;
+    if (!parse(kTunedTable, g_tuned, err)) {
+        fprintf(stderr, "fused_reduce_norm: compiled-in launch table: %s\n", err.c_str());
+        g_tuned.clear();
+    }
+}
+
+// Both tables, caller's first, ready under g_mu.
+void load_tables_locked() {
+    load_env_table_locked();
+    load_tuned_locked();
+}
+
+// The hand-fitted rule, from graph-replay sweeps on MI355X (the sandwich
 // workloads by hand, then tune.py over nine shapes with inputs rotated over
 // 1 GiB, the disputed cells A/B/B/A-interleaved):
 //  - small T (T <= 256, latency-bound): one vector per lane up to 896
@@ -296,10 +329,19 @@ bool use_split_rows(int32_t R, int64_t H, int32_t k, bool ep, int epilogue, int6
     if (k < 1 || T < 1 || T > kSplitCapT) return false;
     {
         std::lock_guard<std::mutex> lock(g_mu);
-        load_env_table_locked();
-        for (const Rule& r : g_rules) {
-            if (r.vec >= 0 || !matches(r, H, R, k, epilogue, ep ? 1 : 0)) continue;
-            if (T >= r.tmin && T <= r.tmax) return r.vec == kSplitRule;
+        load_tables_locked();
+        bool builtin = false;
+        for (const std::vector<Rule>* table : {&g_rules, &g_tuned}) {
+            for (const Rule& r : *table) {
+                if (r.vec >= 0 || !matches(r, H, R, k, epilogue, ep ? 1 : 0)) continue;
+                if (T < r.tmin || T > r.tmax) continue;
+                if (r.vec == kBuiltinRule) {
+                    builtin = true;
+                    break;
+                }
+                return r.vec == kSplitRule;
+            }
+            if (builtin) break;
         }
     }
     return T <= builtin_split_max_t(R, H, k, ep);
@@ -312,11 +354,12 @@ int64_t split_rows_cap(int32_t R, int64_t H, int32_t k) {
     if (cap_ep > cap) cap = cap_ep;
     {
         std::lock_guard<std::mutex> lock(g_mu);
-        load_env_table_locked();
-        for (const Rule& r : g_rules)
-            if (r.vec == kSplitRule && (r.H < 0 || r.H == H) && (r.R < 0 || r.R == R) &&
-                (r.k < 0 || r.k == k) && r.tmax > cap)
-                cap = r.tmax;
+        load_tables_locked();
+        for (const std::vector<Rule>* table : {&g_rules, &g_tuned})
+            for (const Rule& r : *table)
+                if (r.vec == kSplitRule && (r.H < 0 || r.H == H) && (r.R < 0 || r.R == R) &&
+                    (r.k < 0 || r.k == k) && r.tmax > cap)
+                    cap = r.tmax;
     }
     return cap < kSplitCapT ? cap : kSplitCapT;
 }
@@ -328,17 +371,27 @@ LaunchShape choose_shape(int nvec, int fin, int64_t T, int epilogue, int R, int 
     bool pipe = false;
     {
         std::lock_guard<std::mutex> lock(g_mu);
-        load_env_table_locked();
+        load_tables_locked();
         const int64_t H = (int64_t)nvec * 8;
-        for (const Rule& r : g_rules) {
-            if (r.vec <= 0 || !matches(r, H, R, k, epilogue, ep) || T < r.tmin || T > r.tmax)
-                continue;
-            if (r.pipe ? pipe_fits(r.vec, nvec, fin, epilogue, R)
-                       : vec_fits(r.vec, nvec, finalize, epilogue)) {
-                vec = r.vec;
-                pipe = r.pipe;
-                break;
+        bool builtin = false;
+        for (const std::vector<Rule>* table : {&g_rules, &g_tuned}) {
+            for (const Rule& r : *table) {
+                const bool shape_rule = r.vec > 0 || r.vec == kBuiltinRule;
+                if (!shape_rule || !matches(r, H, R, k, epilogue, ep) || T < r.tmin ||
+                    T > r.tmax)
+                    continue;
+                if (r.vec == kBuiltinRule) {
+                    builtin = true;
+                    break;
+                }
+                if (r.pipe ? pipe_fits(r.vec, nvec, fin, epilogue, R)
+                           : vec_fits(r.vec, nvec, finalize, epilogue)) {
+                    vec = r.vec;
+                    pipe = r.pipe;
+                    break;
+                }
             }
+            if (vec != 0 || builtin) break;
         }
     }
     if (vec == 0) {

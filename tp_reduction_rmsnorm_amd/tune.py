@@ -3,6 +3,10 @@
     python tp_reduction_rmsnorm_amd/tune.py --out frn_launch_table.txt \\
         [--shape H R k epilogue ...] [--tokens T ...] [--calls 20]
 
+With ``--out tp_reduction_rmsnorm_amd/csrc/frn_tuned_mi355x.inc`` it writes
+the table the library compiles in as its default tuned rules (rebuild to
+use it); any other name gets the plain table text.
+
 For every shape and token count, each launch choice that fits is forced
 through ``set_launch_table`` -- the one-row kernel with 1, 2 or 4 vectors
 per lane, and for calls without finalize the row-pipelined kernel with 1 or
@@ -226,6 +230,22 @@ def rules_for(H, R, k, epi, rows, last="*"):
     return [f"{H} {R} {k} {epi} {a} {b} {v}" for a, b, v in out]
 
 
+INC_HEADER = """\
+// frn_tuned_mi355x.inc -- the launch table measured on MI355X (gfx950, 256
+// CUs) by tune.py, compiled into the library as its default tuned rules:
+// they decide every shape they cover unless a caller's table
+// (frn_set_launch_table, FRN_LAUNCH_TABLE) has a rule for it first.  Shapes
+// they do not cover take the hand-fitted rule in frn_shapes.hip.  Written
+// by `python tp_reduction_rmsnorm_amd/tune.py --out <this file>`; the text
+// between the delimiters is the table format of frn_set_launch_table.
+"""
+
+
+def as_inc(text: str) -> str:
+    """The table as the C++ raw string literal frn_shapes.hip includes."""
+    return INC_HEADER + 'R"FRN_TABLE(\n' + text + ')FRN_TABLE"\n'
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--out", required=True)
@@ -244,16 +264,18 @@ def main():
     lines = ["# fused_reduce_norm launch table: H R k epilogue Tmin Tmax vec",
              f"# measured on a {props.gcnArchName.split(':')[0]} GPU with {props.multi_processor_count} CUs"
              f" with: python tp_reduction_rmsnorm_amd/tune.py {' '.join(sys.argv[1:])}",
-             f"# graph replay of {args.calls} calls, median of 5.  Load with FRN_LAUNCH_TABLE=<file>."]
+             f"# graph replay of {args.calls} calls, median of 5 after 100 ms of replays."]
     for H, R, k, epi in shapes:
         rows = tune_shape(H, R, k, epi, sorted(set(args.tokens)), args.calls, dev)
         lines += rules_for(H, R, k, epi, rows)
         if k > 0 and epi != "sum" and split_tokens:
             rows = tune_split(H, R, k, epi, split_tokens, args.calls, dev)
             lines += rules_for(H, R, k, epi, rows, last="256")
+    text = "\n".join(lines) + "\n"
+    frn.set_launch_table(text)  # validates the table
+    frn.set_launch_table(None)
     with open(args.out, "w") as f:
-        f.write("\n".join(lines) + "\n")
-    frn.set_launch_table(open(args.out).read())  # validates the file
+        f.write(as_inc(text) if args.out.endswith(".inc") else text)
     print(f"wrote {args.out}", flush=True)
 
 
