@@ -20,11 +20,18 @@ Printed: ONE JSON line with the contract fields plus
   * ``sweep``: µs/call and GB/s over T = 1..4096 at H=5120 (R=4) and H=8192
     (R=8), each the median of 5 replays of a HIP graph holding 20 calls (the
     measuring method of the pages' microbenchmark table, vLLM PR #62366);
-  * ``cpu_baseline``: the CPU oracle timed on the host cores (and on one)
-    on a bounded sample of the same workload, with the largest BF16 ulp
-    distance between its rows and the GPU's timed outputs of those rows;
-  * ``roofline.measured_copy_GBps``: a plain 1 GiB device copy on the same
-    GPU, the practical streaming rate, as a second reference line.
+  * ``other_configs``: the other workloads at their gated sizes -- the tiny
+    call at T=8, the MoE finalize at T=1, 8 and 64, the large-batch MoE call
+    fused against the split path at T=4096, the expert-parallel finalize at
+    T=4096 -- and eager (not graph-captured) µs per call at T=1 and 8;
+  * ``cpu_baseline``: the CPU oracle timed on every core of the host's
+    affinity mask (and on one) on a bounded sample of the same workload,
+    with the largest BF16 ulp distance between its rows and the GPU's timed
+    outputs of those rows;
+  * ``roofline.access_pattern``: the headline call's access pattern alone
+    (bench_probe.hip: the same rows read and written, the same launch
+    pattern, no arithmetic) on the same buffers, the practical ceiling of
+    this access mix on this GPU, and the call's fraction of it.
 
 The GPU runs one process on one device; ``--gpus N`` with N > 1 exits with a
 message (the library runs on one GPU only).
@@ -242,6 +249,8 @@ class Runner:
         self.bytes = workloads.algorithmic_bytes(w.R, T, w.H, epilogue=w.epilogue, k=w.k,
                                                  shared=w.shared, ep=w.ep)
         n = max(1, min(32, -(-COLD_BYTES // self.bytes))) if cold else 1
+        # the inputs the graph's calls rotate over exceed the Infinity Cache
+        self.cold = cold and n * self.bytes >= COLD_BYTES
         self.sets = [workloads.make_workload(cid, T, device=dev, salt=i) for i in range(n)]
         self.outs = [(torch.empty(T, w.H, dtype=torch.bfloat16, device=dev),
                       torch.empty(T, w.H, dtype=torch.bfloat16, device=dev)) for _ in range(n)]
@@ -326,23 +335,28 @@ def sweep(dev, cids=(2, 3), Ts=SWEEP_T):
             gbs = r.bytes / us / 1e3
             rows.append(dict(workload=r.w.name, T=T, us_per_call=round(us, 3),
                              GBps=round(gbs, 1), frac_of_peak=round(gbs / PEAK_GBS, 4),
-                             cold=len(r.sets) > 1))
+                             cold=r.cold))
             print(json.dumps(dict(sweep=rows[-1])), file=sys.stderr, flush=True)
             del r
     return rows
 
 
-def extra_configs(dev):
-    """The other workloads.  Where two paths compute the same call (MoE fused
-    against finalize-then-reduce; fused against split), they share one set of
-    inputs and are timed in the order A, B, B, A, each reported as the mean of
-    its two medians, so that neither gains from running second."""
+def extra_configs(dev, full=False):
+    """The other workloads at their gated sizes: the tiny call at T=8, the
+    MoE finalize at T=1, 8, 64, the expert-parallel finalize at T=4096, and
+    the large-batch MoE call fused against the split path at T=4096
+    (``full``: more T, and the MoE finalize fused against the standalone
+    finalize followed by the plain reduction).  Where two paths compute the
+    same call they share one set of inputs and are timed in the order A, B,
+    B, A, each reported as the mean of its two medians, so that neither
+    gains from running second."""
     rows = []
 
     def add(r, T, tag, us):
         rows.append(dict(workload=r.w.name + (f"_{tag}" if tag else ""), T=T,
                          us_per_call=round(us, 3), GBps=round(r.bytes / us / 1e3, 1),
-                         frac_of_peak=round(r.bytes / us / 1e3 / PEAK_GBS, 4)))
+                         frac_of_peak=round(r.bytes / us / 1e3 / PEAK_GBS, 4),
+                         cold=r.cold))
         print(json.dumps(dict(extra=rows[-1])), file=sys.stderr, flush=True)
 
     def pair(r, attr):
@@ -353,19 +367,24 @@ def extra_configs(dev):
         setattr(r, attr, False)
         return sum(t[False]) / 2, sum(t[True]) / 2
 
-    for cid, Ts in ((1, (8,)), (4, (2, 4, 16, 32)), (6, (1, 8, 64, 1024, 4096))):
+    if full:
+        singles = ((1, (8,)), (4, (2, 4, 16, 32)), (6, (1, 8, 64, 1024, 4096)))
+    else:
+        singles = ((1, (8,)), (4, (1, 8, 64)), (6, (4096,)))
+    for cid, Ts in singles:
         for T in Ts:
             r = Runner(cid, T, dev, cold=T >= 256)
             add(r, T, "", r.graph_us())
             del r
-    for T in (1, 8, 64):
-        r = Runner(4, T, dev, cold=False, unfused=True)
-        fused, unfused = pair(r, "unfused")
-        add(r, T, "", fused)
-        add(r, T, "unfused", unfused)
-        rows[-1]["unfused_over_fused"] = round(unfused / fused, 3)
-        del r
-    for T in (4096, 16384):
+    if full:
+        for T in (1, 8, 64):
+            r = Runner(4, T, dev, cold=False, unfused=True)
+            fused, unfused = pair(r, "unfused")
+            add(r, T, "", fused)
+            add(r, T, "unfused", unfused)
+            rows[-1]["unfused_over_fused"] = round(unfused / fused, 3)
+            del r
+    for T in ((4096, 16384) if full else (4096,)):
         r = Runner(5, T, dev, cold=True, split=True)
         fused, split = pair(r, "split")
         add(r, T, "", fused)
@@ -375,24 +394,29 @@ def extra_configs(dev):
     return rows
 
 
-def copy_reference(dev, nbytes=1 << 30):
-    """GB/s of a plain device-to-device copy of `nbytes` (torch ``copy_``),
-    counted as bytes read + bytes written; median of 5 after 2 warm-up."""
+def eager_rows(dev, cases=((2, 1), (2, 8), (1, 8), (4, 1), (4, 8)), calls=1000):
+    """µs per call of eager calls through the Python binding (no graph), the
+    outputs given: the wall time of `calls` back-to-back calls, after a
+    warm-up, divided by their number.  At these sizes the host's time per
+    call, not the kernel, sets the rate."""
     import torch
-    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-    dst = torch.empty_like(src)
-    for _ in range(2):
-        dst.copy_(src)
-    ts = []
-    for _ in range(5):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        dst.copy_(src)
-        e1.record()
+    rows = []
+    for cid, T in cases:
+        r = Runner(cid, T, dev, cold=False)
+        t_warm = time.perf_counter()
+        while (time.perf_counter() - t_warm) * 1e3 < SETTLE_MS:
+            for i in range(50):
+                r.call(i)
+            torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(calls):
+            r.call(i)
         torch.cuda.synchronize()
-        ts.append(e0.elapsed_time(e1) * 1e-3)
-    return 2 * nbytes / sorted(ts)[2] / 1e9
+        us = (time.perf_counter() - t0) / calls * 1e6
+        rows.append(dict(workload=r.w.name, T=T, eager_us_per_call=round(us, 2)))
+        print(json.dumps(dict(eager=rows[-1])), file=sys.stderr, flush=True)
+        del r
+    return rows
 
 
 def _ordered(bits):
@@ -416,9 +440,10 @@ def cpu_model() -> str:
 def cpu_baseline(runner, seconds=10.0, single_seconds=5.0):
     """The CPU oracle, as it is, on a bounded sample of the timed workload:
     the first 256 token rows of its first input set, repeated for about
-    `seconds` on the host's threads (up to 16) and `single_seconds` on one.
-    The oracle's rows are also compared with the GPU's outputs of those rows
-    from the timed calls (the last timed call on that set)."""
+    `seconds` with one thread per core of the process's affinity mask and
+    `single_seconds` on one.  The oracle's rows are also compared with the
+    GPU's outputs of those rows from the timed calls (the last timed call on
+    that set)."""
     import numpy as np
     import oracle
     import workloads
@@ -429,7 +454,7 @@ def cpu_baseline(runner, seconds=10.0, single_seconds=5.0):
     kw = dict(residual=workloads.bits(d.residual[:rows]), gamma1=workloads.f32(d.gamma1),
               gamma2=workloads.f32(d.gamma2), eps=d.eps,
               epilogue=oracle.EPI_SANDWICH if w.epilogue == "sandwich" else oracle.EPI_RMSNORM)
-    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    cores = max(1, len(os.sched_getaffinity(0)))
     byts = workloads.algorithmic_bytes(w.R, rows, w.H, epilogue=w.epilogue)
 
     def rate(threads, budget):
@@ -448,7 +473,8 @@ def cpu_baseline(runner, seconds=10.0, single_seconds=5.0):
     ulp = max(int(np.abs(_ordered(res.y) - _ordered(y_gpu)).max()),
               int(np.abs(_ordered(res.xout) - _ordered(x_gpu)).max()))
     return dict(value=round(byts * reps / el / 1e9, 3), unit="GB/s", cores=cores, kind="oracle",
-                cpu=cpu_model(),
+                cpu=cpu_model(), affinity_cores=len(os.sched_getaffinity(0)),
+                online_cpus=os.cpu_count(),
                 sample=f"{rows} of {runner.T} token rows of {w.name} (R={w.R}, H={w.H}), "
                        f"{reps} repetitions in {el:.1f} s, {cores} threads; "
                        f"{el / reps * 1e6 / rows:.1f} us per row",
@@ -466,7 +492,13 @@ def main():
                     help="time the K steps as eager calls through the Python binding "
                          "instead of one HIP graph replay (host-bound when a call's "
                          "Python work outlasts the kernel)")
-    ap.add_argument("--all", action="store_true", help="also time the MoE and split workloads")
+    ap.add_argument("--all", action="store_true",
+                    help="more sizes of the other workloads, and the MoE finalize fused "
+                         "against finalize-then-reduce")
+    ap.add_argument("--no-other", action="store_true",
+                    help="skip the other workloads and the eager rows")
+    ap.add_argument("--no-pattern", action="store_true",
+                    help="skip the access-pattern reference of the headline call")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -600,14 +632,24 @@ def main():
         out["cpu_baseline"] = cpu_baseline(run)
     del run
     torch.cuda.empty_cache()
-    if args.workload is None:
-        copy_gbs = copy_reference(dev)
-        out["roofline"]["measured_copy_GBps"] = round(copy_gbs, 1)
-        out["roofline"]["frac_of_measured_copy"] = round(achieved / copy_gbs, 4)
+    if args.workload is None and not args.no_pattern:
+        # the access pattern alone on the same kind of buffers: the practical
+        # ceiling of this read/write mix and launch pattern on this GPU
+        pat = pattern_probe(dev, cid, (T,))[0]
+        pat_us = pat.get("pipelined_pattern_us", pat["pattern_us"])
+        pat_bytes = T * out["config"]["H"] * 2 * (out["config"]["R"] + 3)
+        out["roofline"]["access_pattern"] = dict(
+            kernel=pat["kernel"], pattern_us=pat_us,
+            pattern_GBps=round(pat_bytes / pat_us / 1e3, 1),
+            pattern_frac_of_peak=round(pat_bytes / pat_us / 1e3 / PEAK_GBS, 4),
+            call_frac_of_pattern=round(pat_us / ev_us, 4),
+            source="bench_probe.hip: the call's rows read and written with its launch "
+                   "pattern, no arithmetic")
     if not args.no_sweep:
         out["sweep"] = sweep(dev)
-    if args.all:
-        out["other_configs"] = extra_configs(dev)
+    if not args.no_other and args.workload is None:
+        out["other_configs"] = extra_configs(dev, full=args.all)
+        out["eager"] = eager_rows(dev)
     if args.pattern_probe:
         out["pattern_probe"] = (pattern_probe(dev, cid, (T,)) if args.workload is not None
                                 else pattern_probe(dev))

@@ -39,6 +39,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import threading
 from typing import Optional, Sequence, Tuple, Union
 
 import torch
@@ -167,6 +168,7 @@ def set_launch_table(text: Optional[str]) -> None:
     """Load tuned launch rules ('H R k epilogue Tmin Tmax vec' per line, vec
     1 | 2 | 4 | split | fused), or None to restore the built-in rules.
     Raises ValueError on bad text."""
+    _WS_NEED.clear()
     _check(_c_set_table(None if text is None else text.encode()))
 
 
@@ -241,6 +243,139 @@ def _stream(stream, device) -> int:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+# ------------------------------------------------- the eager call's fast path --- #
+# An eager call of a few tokens takes a few microseconds on the GPU, so the
+# binding's own host time matters there.  The hot entry points first run one
+# cheap test per tensor (the same conditions as _need, read without building
+# device or shape objects); only if a test fails do they take the detailed
+# checks, which raise with the reason.  Pointer arrays go into a per-thread
+# C array that the library copies during the call, and the current stream's
+# handle is read directly.
+
+_BF16, _FP32, _INT32 = torch.bfloat16, torch.float32, torch.int32
+
+try:
+    _raw_current_stream = torch._C._cuda_getCurrentRawStream
+except AttributeError:  # a torch without it: the public (slower) route
+    def _raw_current_stream(index):
+        return torch.cuda.current_stream(index).cuda_stream
+
+
+def _stream_handle(stream, index: int) -> int:
+    if stream is None:
+        return _raw_current_stream(index)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _fits(t, dtype, index: int, shape) -> bool:
+    """What _need checks, plus the shape, for a tensor expected on device
+    `index`."""
+    return (isinstance(t, torch.Tensor) and t.dtype is dtype and t.is_cuda and
+            t.get_device() == index and t.shape == shape and t.is_contiguous())
+
+
+_TLS = threading.local()
+
+
+def _host_ptrs(ptrs, slot: int) -> int:
+    """Address of a C array holding the device pointers `ptrs`: one of the
+    calling thread's own arrays (slot 0, 1, 2), valid until the thread's
+    next call; the library copies the pointers during the call."""
+    arrs = getattr(_TLS, "arrs", None)
+    if arrs is None:
+        arrs = _TLS.arrs = [(ctypes.c_void_p * MAX_R)() for _ in range(3)]
+    if len(ptrs) > MAX_R:  # declined by the library; pass them all the same
+        a = (ctypes.c_void_p * len(ptrs))(*ptrs)
+        _TLS.big = a
+    else:
+        a = arrs[slot]
+        a[:len(ptrs)] = ptrs
+    return ctypes.addressof(a)
+
+
+def _fast_outputs(out, residual_out, shape, index, device_of):
+    """(out, residual_out) when given ones fit or none are given (allocated
+    like the first partial), else None."""
+    if out is None:
+        out = torch.empty(shape, dtype=_BF16, device=device_of.device)
+    elif not _fits(out, _BF16, index, shape):
+        return None
+    if residual_out is None:
+        residual_out = torch.empty(shape, dtype=_BF16, device=device_of.device)
+    elif not _fits(residual_out, _BF16, index, shape):
+        return None
+    return out, residual_out
+
+
+def _fast_reduce(ps, residual, gammas, out, residual_out):
+    """(index, T, H, out, residual_out) if the operands of a reduction pass
+    the cheap tests, else None."""
+    if not ps or not isinstance(ps[0], torch.Tensor):
+        return None
+    p0 = ps[0]
+    index = p0.get_device()
+    shape = p0.shape
+    if index < 0 or len(shape) != 2:
+        return None
+    for p in ps:
+        if not _fits(p, _BF16, index, shape):
+            return None
+    if not _fits(residual, _BF16, index, shape):
+        return None
+    gshape = shape[1:]
+    for g in gammas:
+        if not _fits(g, _FP32, index, gshape):
+            return None
+    outs = _fast_outputs(out, residual_out, shape, index, p0)
+    if outs is None:
+        return None
+    return (index, shape[0], shape[1]) + outs
+
+
+def _fast_moe(es, topk_weights, topk_rows, residual, gamma1, gamma2, epilogue, shared, out,
+              residual_out):
+    """(index, T, H, k, num_rows, out, residual_out) if the operands of a
+    finalize call pass the cheap tests, else None."""
+    if not es or not isinstance(es[0], torch.Tensor) or not isinstance(residual, torch.Tensor):
+        return None
+    e0 = es[0]
+    index = e0.get_device()
+    eshape = e0.shape
+    shape = residual.shape
+    if index < 0 or len(eshape) != 2 or len(shape) != 2 or eshape[1] != shape[1]:
+        return None
+    for e in es:
+        if not _fits(e, _BF16, index, eshape):
+            return None
+    if not _fits(residual, _BF16, index, shape):
+        return None
+    if not isinstance(topk_weights, torch.Tensor) or topk_weights.dim() != 2:
+        return None
+    kshape = topk_weights.shape
+    if kshape[0] != shape[0] or not _fits(topk_weights, _FP32, index, kshape) or \
+            not _fits(topk_rows, _INT32, index, kshape):
+        return None
+    gshape = shape[1:]
+    if not _fits(gamma1, _FP32, index, gshape):
+        return None
+    if epilogue == EPI_SANDWICH and not _fits(gamma2, _FP32, index, gshape):
+        return None
+    if shared is not None:
+        if len(shared) != len(es):
+            return None
+        for t in shared:
+            if not _fits(t, _BF16, index, shape):
+                return None
+    outs = _fast_outputs(out, residual_out, shape, index, e0)
+    if outs is None:
+        return None
+    return (index, shape[0], shape[1], kshape[1], eshape[0]) + outs
+
+
+def _listed(x):
+    return x if type(x) in (list, tuple) else _as_list(x, "tensors")
+
+
 def _outputs(T, H, device, out, residual_out):
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=device)
@@ -261,6 +396,10 @@ def _outputs(T, H, device, out, residual_out):
 # one, so there are few) instead of freeing the old.
 _AUTO_WS = {}
 
+# Automatic workspace bytes per call shape (0: the call takes no split-row
+# finalize); cleared whenever set_launch_table loads a table.
+_WS_NEED = {}
+
 
 def _workspace(workspace, T=0, H=0, R=0, k=0, device=None, stream=None,
                epilogue=EPI_RMSNORM, ep=False):
@@ -275,11 +414,15 @@ def _workspace(workspace, T=0, H=0, R=0, k=0, device=None, stream=None,
     if isinstance(workspace, str):
         if workspace != "auto":
             raise ValueError("workspace must be a tensor, None or 'auto'")
-        use = k > 0 and split_rows(R, k, T, H, epilogue, ep=ep)
-        need = workspace_bytes(T, H, R, k) if use else 0
+        key = (R, k, T, H, epilogue, ep)
+        need = _WS_NEED.get(key)
+        if need is None:
+            use = k > 0 and split_rows(R, k, T, H, epilogue, ep=ep)
+            need = _WS_NEED[key] = workspace_bytes(T, H, R, k) if use else 0
         if need == 0:
             return None, 0
-        kept = _AUTO_WS.setdefault((device.index, stream), [])
+        index = device if isinstance(device, int) else device.index
+        kept = _AUTO_WS.setdefault((index, stream), [])
         if not kept or kept[-1].numel() < need:
             size = max(need, 2 * kept[-1].numel()) if kept else need
             kept.append(torch.empty(size, dtype=torch.uint8, device=device))
@@ -349,13 +492,19 @@ def reduce_residual_rmsnorm(partials: TensorList, residual: torch.Tensor, gamma:
     Pass ``residual_out=residual`` to update the residual stream in place."""
     if residual is None:
         raise ValueError("residual is required: this boundary always adds the residual")
-    ps, T, H, device = _check_partials(partials, residual)
-    _check_gamma(gamma, H, device, "gamma")
-    out, residual_out = _outputs(T, H, device, out, residual_out)
+    ps = _listed(partials)
+    fast = _fast_reduce(ps, residual, (gamma,), out, residual_out)
+    if fast is None:  # the detailed checks: they raise, or allocate what is missing
+        ps, T, H, device = _check_partials(partials, residual)
+        _check_gamma(gamma, H, device, "gamma")
+        out, residual_out = _outputs(T, H, device, out, residual_out)
+        index = device.index
+    else:
+        index, T, H, out, residual_out = fast
     ws, wsb = _workspace(workspace)
-    arr = _ptr_array(ps)
-    _check(_c_rms(ctypes.cast(arr, _P), len(ps), residual.data_ptr(), gamma.data_ptr(), eps,
-                  T, H, out.data_ptr(), residual_out.data_ptr(), ws, wsb, _stream(stream, device)))
+    _check(_c_rms(_host_ptrs([p.data_ptr() for p in ps], 0), len(ps), residual.data_ptr(),
+                  gamma.data_ptr(), eps, T, H, out.data_ptr(), residual_out.data_ptr(), ws, wsb,
+                  _stream_handle(stream, index)))
     return out, residual_out
 
 
@@ -367,15 +516,20 @@ def reduce_sandwich_norm(partials: TensorList, residual: torch.Tensor, gamma1: t
     returns (bf16(norm(h) * gamma2), bf16(h))."""
     if residual is None:
         raise ValueError("residual is required: this boundary always adds the residual")
-    ps, T, H, device = _check_partials(partials, residual)
-    _check_gamma(gamma1, H, device, "gamma1")
-    _check_gamma(gamma2, H, device, "gamma2")
-    out, residual_out = _outputs(T, H, device, out, residual_out)
+    ps = _listed(partials)
+    fast = _fast_reduce(ps, residual, (gamma1, gamma2), out, residual_out)
+    if fast is None:  # the detailed checks: they raise, or allocate what is missing
+        ps, T, H, device = _check_partials(partials, residual)
+        _check_gamma(gamma1, H, device, "gamma1")
+        _check_gamma(gamma2, H, device, "gamma2")
+        out, residual_out = _outputs(T, H, device, out, residual_out)
+        index = device.index
+    else:
+        index, T, H, out, residual_out = fast
     ws, wsb = _workspace(workspace)
-    arr = _ptr_array(ps)
-    _check(_c_sandwich(ctypes.cast(arr, _P), len(ps), residual.data_ptr(), gamma1.data_ptr(),
-                       gamma2.data_ptr(), eps, T, H, out.data_ptr(), residual_out.data_ptr(),
-                       ws, wsb, _stream(stream, device)))
+    _check(_c_sandwich(_host_ptrs([p.data_ptr() for p in ps], 0), len(ps), residual.data_ptr(),
+                       gamma1.data_ptr(), gamma2.data_ptr(), eps, T, H, out.data_ptr(),
+                       residual_out.data_ptr(), ws, wsb, _stream_handle(stream, index)))
     return out, residual_out
 
 
@@ -405,15 +559,22 @@ def moe_finalize_reduce_norm(expert_rows: TensorList, topk_weights: torch.Tensor
     ``workspace_bytes(T, H, R, k)`` bytes, 256-byte aligned."""
     if residual is None:
         raise ValueError("residual is required: this boundary always adds the residual")
-    es, sh, T, H, k, num_rows, device = _check_finalize(expert_rows, topk_weights, topk_rows,
-                                                        shared)
-    _check_moe_epilogue(residual, gamma1, gamma2, epilogue, T, H, device)
-    out, residual_out = _outputs(T, H, device, out, residual_out)
-    st = _stream(stream, device)
-    ws, wsb = _workspace(workspace, T, H, len(es), k, device, st, epilogue)
-    earr = _ptr_array(es)
-    sarr = _ptr_array(sh) if sh is not None else None
-    _check(_c_moe(ctypes.cast(earr, _P), ctypes.cast(sarr, _P) if sarr is not None else None,
+    es = _listed(expert_rows)
+    sh = _listed(shared) if shared is not None else None
+    fast = _fast_moe(es, topk_weights, topk_rows, residual, gamma1, gamma2, epilogue, sh, out,
+                     residual_out)
+    if fast is None:  # the detailed checks: they raise, or allocate what is missing
+        es, sh, T, H, k, num_rows, device = _check_finalize(expert_rows, topk_weights,
+                                                            topk_rows, shared)
+        _check_moe_epilogue(residual, gamma1, gamma2, epilogue, T, H, device)
+        out, residual_out = _outputs(T, H, device, out, residual_out)
+        index = device.index
+    else:
+        index, T, H, k, num_rows, out, residual_out = fast
+    st = _stream_handle(stream, index)
+    ws, wsb = _workspace(workspace, T, H, len(es), k, index, st, epilogue)
+    _check(_c_moe(_host_ptrs([e.data_ptr() for e in es], 0),
+                  _host_ptrs([t.data_ptr() for t in sh], 1) if sh is not None else None,
                   len(es), topk_weights.data_ptr(), topk_rows.data_ptr(), k, num_rows, epilogue,
                   residual.data_ptr(), gamma1.data_ptr(),
                   gamma2.data_ptr() if gamma2 is not None else None, eps, T, H,
@@ -436,20 +597,27 @@ def moe_finalize_reduce_norm_noalloc(expert_rows: TensorList, topk_weights: torc
     C call allocates.  A call whose split-row finalize needs more scratch
     raises ``FusedReduceNormUnsupported``.  Calls that may overlap in time
     on one GPU share that array and race: serialise them."""
-    es, sh, T, H, k, num_rows, device = _check_finalize(expert_rows, topk_weights, topk_rows,
-                                                        shared)
-    _check_moe_epilogue(residual, gamma1, gamma2, epilogue, T, H, device)
     if out is None or residual_out is None:
         raise ValueError("out and residual_out are required: this call allocates nothing")
-    out, residual_out = _outputs(T, H, device, out, residual_out)
-    earr = _ptr_array(es)
-    sarr = _ptr_array(sh) if sh is not None else None
-    _check(_c_moe_noalloc(ctypes.cast(earr, _P),
-                          ctypes.cast(sarr, _P) if sarr is not None else None, len(es),
-                          topk_weights.data_ptr(), topk_rows.data_ptr(), k, num_rows, epilogue,
-                          residual.data_ptr(), gamma1.data_ptr(),
+    es = _listed(expert_rows)
+    sh = _listed(shared) if shared is not None else None
+    fast = _fast_moe(es, topk_weights, topk_rows, residual, gamma1, gamma2, epilogue, sh, out,
+                     residual_out)
+    if fast is None:  # the detailed checks: they raise
+        es, sh, T, H, k, num_rows, device = _check_finalize(expert_rows, topk_weights,
+                                                            topk_rows, shared)
+        _check_moe_epilogue(residual, gamma1, gamma2, epilogue, T, H, device)
+        out, residual_out = _outputs(T, H, device, out, residual_out)
+        index = device.index
+    else:
+        index, T, H, k, num_rows, out, residual_out = fast
+    _check(_c_moe_noalloc(_host_ptrs([e.data_ptr() for e in es], 0),
+                          _host_ptrs([t.data_ptr() for t in sh], 1) if sh is not None else None,
+                          len(es), topk_weights.data_ptr(), topk_rows.data_ptr(), k, num_rows,
+                          epilogue, residual.data_ptr(), gamma1.data_ptr(),
                           gamma2.data_ptr() if gamma2 is not None else None, eps, T, H,
-                          out.data_ptr(), residual_out.data_ptr(), _stream(stream, device)))
+                          out.data_ptr(), residual_out.data_ptr(),
+                          _stream_handle(stream, index)))
     return out, residual_out
 
 
