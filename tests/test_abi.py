@@ -538,6 +538,49 @@ def test_python_layer_raises_on_decline_and_never_returns_inputs(monkeypatch):
     frn._check(OK)
 
 
+def test_boundary_materializes_a_declined_finalize_or_raises(monkeypatch):
+    """boundary()'s decline policy, with stand-ins for the library calls:
+    'raise' re-raises; 'materialize' runs the standalone finalize and reduces
+    its R partials; a decline the materialized path makes too still raises,
+    so no unreduced data is ever returned."""
+    import torch
+    import tp_reduction_rmsnorm_amd as frn
+    calls = []
+
+    def fused_declines(*a, **k):
+        calls.append("fused")
+        raise frn.FusedReduceNormUnsupported("workspace is not 256-byte aligned")
+
+    def finalize(src, w, rows, shared=None, stream=None):
+        calls.append(("finalize", tuple(src), shared))
+        return ["P0", "P1"]
+
+    def reduce(parts, residual, gamma, eps, out=None, residual_out=None, stream=None):
+        calls.append(("reduce", tuple(parts), residual))
+        return "y", "x"
+
+    monkeypatch.setattr(frn, "moe_finalize_reduce_norm", fused_declines)
+    monkeypatch.setattr(frn, "moe_finalize", finalize)
+    monkeypatch.setattr(frn, "reduce_residual_rmsnorm", reduce)
+    w = torch.zeros(3, 2)
+    args = (["E0", "E1"], "res", "g")
+    kw = dict(topk_weights=w, topk_rows="idx", shared=["S0", "S1"])
+    with pytest.raises(frn.FusedReduceNormUnsupported):
+        frn.boundary(*args, **kw)
+    assert frn.boundary(*args, **kw, on_decline="materialize") == ("y", "x")
+    assert calls == ["fused", "fused", ("finalize", ("E0", "E1"), ["S0", "S1"]),
+                     ("reduce", ("P0", "P1"), "res")]
+
+    def finalize_declines(*a, **k):
+        raise frn.FusedReduceNormUnsupported("R=17 exceeds 16")
+
+    monkeypatch.setattr(frn, "moe_finalize", finalize_declines)
+    with pytest.raises(frn.FusedReduceNormUnsupported, match="exceeds"):
+        frn.boundary(*args, **kw, on_decline="materialize")
+    with pytest.raises(ValueError):
+        frn.boundary(*args, **kw, on_decline="skip")
+
+
 def test_python_layer_requires_gpu_tensors():
     import torch
     import tp_reduction_rmsnorm_amd as frn

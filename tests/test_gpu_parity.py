@@ -516,6 +516,37 @@ def test_split_row_small_or_misaligned_workspace():
         gpu_fused(d, workspace=big[16:])                      # 16-byte, not 256-byte aligned
 
 
+@pytest.mark.parametrize("epi", ["rmsnorm", "sandwich"])
+def test_boundary_materializes_a_declined_finalize(epi):
+    """A fused finalize call declined for its workspace (too small): with
+    on_decline='raise' the layer boundary raises and leaves the outputs
+    alone; with 'materialize' it finalizes each rank alone and reduces the
+    partials -- bit for bit the fused call's result, and the oracle's."""
+    m = frn()
+    R, T, H, k = 4, 8, 2048, 3
+    assert m.split_rows(R, k, T, H, m.EPI_SANDWICH if epi == "sandwich" else m.EPI_RMSNORM)
+    inp = workloads.make(R, T, H, k=k, shared=True, epilogue=epi, seed=58)
+    d = to_dev(inp)
+    e = m.EPI_SANDWICH if epi == "sandwich" else m.EPI_RMSNORM
+    small = torch.zeros(64, dtype=torch.uint8, device=DEV)
+    out = torch.full((T, H), 3.0, dtype=torch.bfloat16, device=DEV)
+    rout = torch.full((T, H), 5.0, dtype=torch.bfloat16, device=DEV)
+    kw = dict(topk_weights=d.topk_w, topk_rows=d.topk_idx, shared=d.shared, epilogue=e,
+              workspace=small)
+    with pytest.raises(m.FusedReduceNormUnsupported, match="smaller than"):
+        m.boundary(d.expert_rows, d.residual, d.gamma1, d.gamma2, d.eps, out=out,
+                   residual_out=rout, **kw)
+    torch.cuda.synchronize()
+    assert bool((out == 3.0).all()) and bool((rout == 5.0).all())
+    y, x = m.boundary(d.expert_rows, d.residual, d.gamma1, d.gamma2, d.eps,
+                      on_decline="materialize", out=out, residual_out=rout, **kw)
+    yf, xf = gpu_fused(d)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), yf.view(torch.int16))
+    assert torch.equal(x.view(torch.int16), xf.view(torch.int16))
+    check(f"boundary materialized after a decline {epi}", y, x, oracle_ref(inp))
+
+
 def test_split_row_graph_replay():
     """Graph-captured split-row finalize (two kernels through the workspace):
     every replay, with new data, matches the oracle."""

@@ -836,7 +836,8 @@ def split_reduce_norm(src: TensorList, residual: torch.Tensor, gamma1: torch.Ten
 def boundary(src: TensorList, residual: torch.Tensor, gamma1: torch.Tensor,
              gamma2: Optional[torch.Tensor] = None, eps: float = 1e-6, *,
              topk_weights=None, topk_rows=None, shared=None, epilogue: int = EPI_RMSNORM,
-             max_fused_tokens: Optional[int] = None, out=None, residual_out=None,
+             max_fused_tokens: Optional[int] = None, workspace="auto",
+             on_decline: str = "raise", out=None, residual_out=None,
              stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """The layer boundary with a large-batch threshold, the analogue of the
     pages' maximum fused batch size (SGLang PR #34134, first commit message:
@@ -847,7 +848,20 @@ def boundary(src: TensorList, residual: torch.Tensor, gamma1: torch.Tensor,
     which rounds the sum to BF16 once more.  Measured on MI355X the fused
     kernel is the faster one at every size tried (split/fused 1.05 at
     H=7168, T=4096 and 16384), hence the default.  src: partials, or the
-    expert-row buffers when topk_weights/topk_rows are given."""
+    expert-row buffers when topk_weights/topk_rows are given.
+
+    ``on_decline``: what a declined fused finalize call does.  "raise"
+    raises ``FusedReduceNormUnsupported``.  "materialize" follows the pages'
+    rule that a deferred finalize reaching a path that does not fuse it is
+    materialized in place (SGLang PR #34134, first and second commit
+    messages): the per-rank finalize runs alone (``moe_finalize``) and the R
+    BF16 partials take the plain reduction and epilogue -- the same result,
+    bit for bit, as the fused call.  That serves declines the fused call
+    alone makes (a workspace that is misaligned or too small); if the
+    materialized path declines too, it raises.  Never returns unreduced
+    data."""
+    if on_decline not in ("raise", "materialize"):
+        raise ValueError("on_decline must be 'raise' or 'materialize'")
     T = (topk_weights.shape[0] if topk_weights is not None
          else _as_list(src, "src")[0].shape[0])
     if max_fused_tokens is not None and T > max_fused_tokens:
@@ -855,9 +869,16 @@ def boundary(src: TensorList, residual: torch.Tensor, gamma1: torch.Tensor,
                                  topk_rows=topk_rows, shared=shared, epilogue=epilogue,
                                  out=out, residual_out=residual_out, stream=stream)
     if topk_weights is not None:
-        return moe_finalize_reduce_norm(src, topk_weights, topk_rows, residual, gamma1, gamma2,
-                                        eps, shared=shared, epilogue=epilogue, out=out,
-                                        residual_out=residual_out, stream=stream)
+        try:
+            return moe_finalize_reduce_norm(src, topk_weights, topk_rows, residual, gamma1,
+                                            gamma2, eps, shared=shared, epilogue=epilogue,
+                                            out=out, residual_out=residual_out,
+                                            workspace=workspace, stream=stream)
+        except FusedReduceNormUnsupported:
+            if on_decline != "materialize":
+                raise
+        parts = moe_finalize(src, topk_weights, topk_rows, shared=shared, stream=stream)
+        src = parts
     if epilogue == EPI_SANDWICH:
         return reduce_sandwich_norm(src, residual, gamma1, gamma2, eps, out=out,
                                     residual_out=residual_out, stream=stream)
