@@ -55,6 +55,7 @@ PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 HEADLINE = (2, 4096)       # sandwich H=5120 R=4, T=4096
 SWEEP_T = (1, 8, 64, 256, 1024, 4096)
 COLD_BYTES = 1 << 30       # rotate inputs over > 1 GiB where bandwidth is measured
+INFINITY_CACHE_BYTES = 256 << 20  # MI355X's last-level cache
 # Warm-up before every timed region lasts at least this long.  After idle
 # time (input generation, another workload's set-up) MI355X runs the first
 # ~10 ms of sustained memory traffic slow: the same graph of 20 sandwich
@@ -250,7 +251,7 @@ class Runner:
                                                  shared=w.shared, ep=w.ep)
         n = max(1, min(32, -(-COLD_BYTES // self.bytes))) if cold else 1
         # the inputs the graph's calls rotate over exceed the Infinity Cache
-        self.cold = cold and n * self.bytes >= COLD_BYTES
+        self.cold = cold and n * self.bytes > INFINITY_CACHE_BYTES
         self.sets = [workloads.make_workload(cid, T, device=dev, salt=i) for i in range(n)]
         self.outs = [(torch.empty(T, w.H, dtype=torch.bfloat16, device=dev),
                       torch.empty(T, w.H, dtype=torch.bfloat16, device=dev)) for _ in range(n)]
