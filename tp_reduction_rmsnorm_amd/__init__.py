@@ -27,8 +27,10 @@ Function names are the C entry points without their ``frn_`` prefix:
   ``launch_pipelined``           tuned launch shapes, the split-row finalize
                                  choice and the row-pipelined kernel choice
                                  (tune.py)
-* ``boundary``                   fused or split by a token threshold (a
-                                 Python-side policy over the calls above)
+* ``boundary``                   fused or split by a token threshold, and
+                                 the materialized finalize when a fused
+                                 finalize call declines (Python-side
+                                 policies over the calls above)
 
 Every call returns its outputs.  A declined call raises
 ``FusedReduceNormUnsupported``; it never returns unreduced data.  (The pages
