@@ -1,6 +1,8 @@
 """Seeded random shapes across the supported range, each call checked
 against the oracle: plain, sandwich, TP and expert-parallel finalize, split
-path, with and without the split-row workspace.  The shapes are drawn from
+path, with and without the split-row workspace (every other TP finalize
+case given one goes through the no-allocation entry point instead, whose
+scratch array then holds the partials).  The shapes are drawn from
 a fixed seed, so the set is the same on every run: 48 of them by default;
 FRN_RANDOM_SHAPES=<n> and FRN_RANDOM_SEED=<s> draw a larger or another
 set."""
@@ -67,6 +69,20 @@ def test_random_shape_matches_oracle(case):
         if kind == "split":
             y, x = P.gpu_split(d)
             ref = P.oracle_ref(inp, split=True)
+        elif kind == "tp" and ws and (i // 4) % 2 == 1:
+            e = m.EPI_SANDWICH if epi == "sandwich" else m.EPI_RMSNORM
+            y = torch.empty(T, H, dtype=torch.bfloat16, device=P.DEV)
+            x = torch.empty(T, H, dtype=torch.bfloat16, device=P.DEV)
+            if m.split_rows(R, k, T, H, e) and R * T * H * 2 > m.NOALLOC_SCRATCH_BYTES:
+                with pytest.raises(m.FusedReduceNormUnsupported, match="scratch"):
+                    m.moe_finalize_reduce_norm_noalloc(
+                        d.expert_rows, d.topk_w, d.topk_idx, d.residual, d.gamma1, d.gamma2,
+                        d.eps, out=y, residual_out=x, shared=d.shared, epilogue=e)
+                return
+            m.moe_finalize_reduce_norm_noalloc(d.expert_rows, d.topk_w, d.topk_idx, d.residual,
+                                               d.gamma1, d.gamma2, d.eps, out=y, residual_out=x,
+                                               shared=d.shared, epilogue=e)
+            ref = P.oracle_ref(inp)
         else:
             y, x = P.gpu_fused(d, workspace="auto" if (ws and k) else None)
             ref = P.oracle_ref(inp)
