@@ -14,7 +14,7 @@
 
 namespace {
 
-constexpr int kMaxSrc = 17;
+constexpr int kMaxSrc = 24;
 constexpr int kMaxDst = 2;
 
 struct ProbeArgs {

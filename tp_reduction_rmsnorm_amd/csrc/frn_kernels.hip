@@ -893,9 +893,15 @@ hipError_t launch(const RowArgs& a, int64_t T, int threads, hipStream_t stream) 
 }
 
 // Ranks (or top-k slots, or live rows) per load chunk: at most 64 VGPRs of
-// loads in flight per lane (32 for a two-vector finalize and for the
-// expert-parallel work list, which hold more live state and would otherwise
-// spill or lose occupancy).
+// loads in flight per lane (32 for a two-vector finalize, which holds more
+// live state and would otherwise spill or lose occupancy).  The
+// expert-parallel work list takes five live rows a chunk: 62 VGPRs, eight
+// waves per SIMD, where eight rows take 74 and six waves -- one workgroup
+// fewer per CU at 512 and 896 lanes.  Measured on MI355X against eight
+// (graph replay, R=8 H=6144 k=10 of 256 experts): 2-5% faster at T=64 to
+// 256, 1-2% at T=1024 to 16384; 8% faster at R=4 H=4096 k=8 T=1024 and 6%
+// at R=16 H=7168 k=8 T=1024; at most 1% slower over k=2 to 16 at
+// H=6144 R=8.
 template <int EPI, int FIN, int V>
 hipError_t launch_c(const RowArgs& a, int64_t T, int threads, hipStream_t stream) {
     constexpr int CMAX = 16 / V;
@@ -911,7 +917,7 @@ hipError_t launch_c(const RowArgs& a, int64_t T, int threads, hipStream_t stream
             return launch<EPI, FIN, V, (V == 1 ? 16 : 4)>(a, T, threads, stream);
         }
     } else if constexpr (FIN == kFinEp) {
-        return launch<EPI, FIN, V, (V == 1 ? 8 : 4)>(a, T, threads, stream);
+        return launch<EPI, FIN, V, (V == 1 ? 5 : 4)>(a, T, threads, stream);
     } else {
         if (a.R <= 2) return launch<EPI, FIN, V, 2>(a, T, threads, stream);
         if (a.R <= 4) return launch<EPI, FIN, V, 4>(a, T, threads, stream);
