@@ -151,15 +151,15 @@ frn_status frn_moe_finalize_reduce_norm(const void* const* expert_rows,
  * serving loops, harnesses that forbid allocation.  Same arguments, results
  * and checks as frn_moe_finalize_reduce_norm, without workspace and
  * workspace_bytes: where that call would take the split-row finalize (see
- * frn_split_rows), this one writes its R x T x H BF16 partials to a scratch
+ * frn_split_rows), this one writes its T x H FP32 rank sums to a scratch
  * array that the library holds in device memory, FRN_NOALLOC_SCRATCH_BYTES
  * per GPU, kept until the process ends; elsewhere it runs the one-row kernel
- * and uses no scratch.  It calls no allocation routine.  A call whose
- * split-row finalize needs more than FRN_NOALLOC_SCRATCH_BYTES (R * T * H *
- * 2 bytes; e.g. R = 8, H = 6144 fits up to T = 170) returns
- * FRN_ERR_UNSUPPORTED without launching, and frn_last_error() states both
- * sizes.  The scratch needs no initialisation and its contents from the
- * previous call are never read.  Every call on one GPU shares that GPU's
+ * and uses no scratch.  It calls no allocation routine.  The array covers
+ * the largest call any launch table can route to the split-row finalize
+ * (T = 256 at H = 16384: T * H * 4 bytes); a larger need would return
+ * FRN_ERR_UNSUPPORTED without launching, with both sizes in
+ * frn_last_error().  The scratch needs no initialisation and its contents
+ * from the previous call are never read.  Every call on one GPU shares that GPU's
  * array: calls that may overlap in time on one GPU (different streams,
  * concurrent graph replays) race and give wrong results; serialise them.
  * The first call on each GPU looks up the array's device address
@@ -348,24 +348,25 @@ frn_status frn_launch_shape(int32_t R, int32_t k, int64_t T, int64_t H, int32_t 
 /*
  * Bytes of the optional workspace argument of the fused calls for calls of
  * up to max_T tokens (0: no call of these sizes uses one).  Only the MoE
- * finalize (k > 0) uses it, at small T: the finalize of each (token, rank,
- * 2048-column slice) then runs in a workgroup of its own and writes its
- * BF16 partial to the workspace, and a second kernel on the same stream
- * reduces the R partials and runs the epilogue.  This spreads a token's row
- * over many workgroups at small batch, the analogue of the pages' row
- * spread over several blocks (SGLang PR #34134, the publish-granularity
- * discussion).  Which calls take it is frn_split_rows; the size returned
- * covers both routings and every epilogue under the current launch table.
- * Results are bit-identical with and without it (the partials are the same
- * BF16 values, summed in the same order).  Layout: R x T x H BF16.  The
- * caller allocates it (256-byte aligned); it needs no initialisation and
- * holds nothing between calls.  Calls that share one workspace must not run
- * concurrently.  A workspace that is NULL, or given to a call that does not
- * take the split-row finalize, is ignored (the call then uses the
+ * finalize (k > 0) uses it, at small T: each (token, 512-column slice) then
+ * runs in a workgroup of its own with one wave per rank, the R finalized
+ * BF16 partials are summed in LDS, and the FP32 sum goes to the workspace;
+ * a second kernel on the same stream reads it back and runs the epilogue.
+ * This spreads a token's row over many workgroups at small batch, the
+ * analogue of the pages' row spread over several blocks (SGLang PR #34134,
+ * the publish-granularity discussion).  Which calls take it is
+ * frn_split_rows; the size returned covers both routings and every
+ * epilogue under the current launch table.  Results are bit-identical with
+ * and without it (the same BF16 partials, summed in the same order, and the
+ * FP32 sum stored exactly).  Layout: T x H FP32.  The caller allocates it
+ * (256-byte aligned); it needs no initialisation and holds nothing between
+ * calls.  Calls that share one workspace must not run concurrently.  A
+ * workspace that is NULL, or given to a call that does not take the
+ * split-row finalize, is ignored (the call then uses the
  * one-row-per-workgroup kernel).  A workspace given to a call that takes it
- * must cover that call (R * T * H * 2 bytes) and be 256-byte aligned, else
- * the call returns FRN_ERR_UNSUPPORTED without launching; it must not
- * overlap any other argument (FRN_ERR_INVALID).
+ * must cover that call (T * H * 4 bytes) and be 256-byte aligned, else the
+ * call returns FRN_ERR_UNSUPPORTED without launching; it must not overlap
+ * any other argument (FRN_ERR_INVALID).
  */
 size_t frn_workspace_bytes(int64_t max_T, int64_t H, int32_t R, int32_t k);
 
@@ -375,11 +376,12 @@ size_t frn_workspace_bytes(int64_t max_T, int64_t H, int32_t R, int32_t k);
  * sizes outside what the library serves).  epilogue: FRN_EPI_RMSNORM or
  * FRN_EPI_SANDWICH, OR'ed with FRN_SHAPE_EP for a call of
  * frn_ep_moe_finalize_reduce_norm.  The split-row finalize writes and
- * re-reads R partial rows per token, so it pays only while the one-row
- * kernel is bound by its memory round trips.  The compiled-in measured
- * table decides the shapes it covers; the hand-fitted rule, measured on
- * MI355X, takes it up to 8 to 192 tokens depending on R, H and the routing;
- * a caller's split / fused rules override both (see frn_set_launch_table).
+ * re-reads one FP32 row per token and adds a second launch, so it pays only
+ * while the one-row kernel is bound by its memory round trips.  The
+ * compiled-in measured table decides the shapes it covers; the hand-fitted
+ * rule, measured on MI355X, takes it up to 8 to 224 tokens depending on R,
+ * H, k and the routing (never at R = 1 under TP routing); a caller's split /
+ * fused rules override both (see frn_set_launch_table).
  */
 int32_t frn_split_rows(int32_t R, int32_t k, int64_t T, int64_t H, int32_t epilogue);
 

@@ -253,22 +253,21 @@ def test_noalloc_zero_tokens_is_a_no_op(lib):
     assert call_moe_noalloc(lib, T=0) == OK
 
 
-def test_noalloc_declines_beyond_its_scratch(lib):
-    """Where the split-row finalize is chosen and its partials (R*T*H*2
-    bytes) exceed the library's scratch array, the call is declined before
-    any HIP call, and the message gives both sizes."""
+def test_noalloc_scratch_covers_every_split_row_call(lib):
+    """The scratch array holds the FP32 rank sums of the largest call the
+    split-row finalize takes (256 tokens of H=16384: T*H*4 bytes), so the
+    no-allocation entry point never declines for its size."""
     import tp_reduction_rmsnorm_amd as frn
     cap = noalloc_scratch_bytes()
     assert cap == frn.NOALLOC_SCRATCH_BYTES == 16 << 20
-    R, k, H, T = 16, 16, 16384, 64
-    assert frn.split_rows(R, k, T, H)
-    need = R * T * H * 2
-    assert need > cap
-    assert call_moe_noalloc(lib, R=R, k=k, T=T, H=H, num_rows=T * k) == UNSUPPORTED
-    msg = lib.frn_last_error().decode()
-    assert "scratch" in msg and str(need) in msg and str(cap) in msg
-    # R = 8, H = 6144 fits up to 170 tokens, which the built-in rule never splits at
-    assert 8 * 170 * 6144 * 2 <= cap < 8 * 171 * 6144 * 2
+    assert 256 * 16384 * 4 == cap
+    frn.set_launch_table("* * * * 0 * split\n")   # split wherever the library allows
+    try:
+        R, k, H, T = 16, 16, 16384, 256
+        assert frn.split_rows(R, k, T, H) and not frn.split_rows(R, k, T + 1, H)
+        assert lib.frn_workspace_bytes(100000, H, R, k) == T * H * 4 == cap
+    finally:
+        frn.set_launch_table(None)
     assert lib.frn_workspace_bytes(100000, 6144, 8, 10) <= cap
 
 
@@ -354,18 +353,18 @@ def test_workspace_bytes(lib):
     lib.frn_set_launch_table.argtypes = [ctypes.c_char_p]
     assert lib.frn_set_launch_table(HAND_FITTED.encode()) == OK
     try:
-        assert lib.frn_workspace_bytes(8, 6144, 8, 10) == 8 * 8 * 6144 * 2
-        # covers the largest T either routing splits at: R=8 H=6144 -> 96 (TP)
-        assert lib.frn_workspace_bytes(5000, 6144, 8, 10) == 96 * 8 * 6144 * 2
-        assert lib.frn_workspace_bytes(5000, 4096, 2, 4) == 8 * 2 * 4096 * 2   # EP only
+        assert lib.frn_workspace_bytes(8, 6144, 8, 10) == 8 * 6144 * 4   # FP32 rank sums
+        # covers the largest T either routing splits at: R=8 H=6144 -> 128 (TP)
+        assert lib.frn_workspace_bytes(5000, 6144, 8, 10) == 128 * 6144 * 4
+        assert lib.frn_workspace_bytes(5000, 4096, 2, 4) == 8 * 4096 * 4   # EP only
         assert lib.frn_workspace_bytes(64, 5120, 4, 0) == 0      # no finalize: none used
         assert lib.frn_workspace_bytes(64, 5124, 4, 2) == 0      # unsupported H
         assert lib.frn_workspace_bytes(0, 5120, 4, 2) == 0
         assert lib.frn_workspace_bytes(8, 5120, 4, 17) == 0      # k beyond FRN_MAX_K
         # the size covers the compiled-in table's split rules too
         assert lib.frn_workspace_bytes(5000, 7168, 2, 8) == max(
-            [32] + [int(r[5]) for r in tuned_rules()
-                    if r[:3] == ["7168", "2", "8"] and r[6] == "split"]) * 2 * 7168 * 2
+            [48] + [int(r[5]) for r in tuned_rules()
+                    if r[:3] == ["7168", "2", "8"] and r[6] == "split"]) * 7168 * 4
     finally:
         lib.frn_set_launch_table(None)
 
@@ -377,19 +376,27 @@ def test_split_rows_builtin_rule():
     S, EP = frn.EPI_SANDWICH, True
     frn.set_launch_table(HAND_FITTED)
     cases = [  # R, k, H, ep, T, expected
-        (8, 10, 6144, False, 1, True), (8, 10, 6144, False, 96, True),
-        (8, 10, 6144, False, 97, False), (8, 10, 6144, False, 256, False),
-        (2, 8, 7168, False, 32, True), (2, 8, 7168, False, 33, False),
-        (2, 4, 4096, False, 1, False), (4, 8, 2048, False, 192, True),
-        (4, 8, 2048, False, 193, False), (16, 8, 4096, False, 128, True),
-        (8, 10, 6144, EP, 16, True), (8, 10, 6144, EP, 17, False),
+        (8, 10, 6144, False, 1, True), (8, 10, 6144, False, 128, True),
+        (8, 10, 6144, False, 129, False), (8, 10, 6144, False, 256, False),
+        (1, 8, 7168, False, 1, False),
+        (2, 8, 7168, False, 48, True), (2, 8, 7168, False, 49, False),
+        (2, 16, 5120, False, 64, True), (2, 16, 5120, False, 65, False),
+        (2, 4, 4096, False, 1, False), (4, 8, 2048, False, 224, True),
+        (4, 8, 2048, False, 225, False), (16, 8, 4096, False, 192, True),
+        (16, 8, 4096, False, 193, False), (3, 8, 7168, False, 64, True),
+        (3, 8, 7168, False, 65, False), (4, 8, 5120, False, 96, True),
+        (4, 8, 5120, False, 97, False),
+        (8, 10, 6144, EP, 64, True), (8, 10, 6144, EP, 65, False),
+        (8, 4, 6144, EP, 16, True), (8, 4, 6144, EP, 17, False),
         (2, 10, 6144, EP, 8, True), (2, 10, 6144, EP, 9, False),
-        (16, 8, 4096, EP, 48, True), (16, 8, 4096, EP, 49, False),
-        (8, 8, 2048, EP, 48, True),
-        (16, 8, 7168, False, 96, True), (16, 8, 7168, False, 97, False),
-        (8, 6, 3072, False, 192, True), (8, 6, 3072, False, 193, False),
-        (8, 10, 5120, False, 96, True), (8, 10, 5120, False, 97, False),
-        (16, 6, 3072, EP, 32, True), (16, 6, 3072, EP, 33, False),
+        (4, 8, 7168, EP, 32, True), (4, 8, 7168, EP, 33, False),
+        (16, 8, 4096, EP, 96, True), (16, 8, 4096, EP, 97, False),
+        (16, 8, 7168, EP, 64, True), (16, 8, 7168, EP, 65, False),
+        (8, 8, 2048, EP, 160, True), (8, 8, 2048, EP, 161, False),
+        (16, 8, 7168, False, 128, True), (16, 8, 7168, False, 129, False),
+        (8, 6, 3072, False, 224, True), (8, 6, 3072, False, 225, False),
+        (8, 10, 5120, False, 128, True), (8, 10, 5120, False, 129, False),
+        (16, 6, 3072, EP, 96, True), (16, 6, 3072, EP, 97, False),
     ]
     try:
         for R, k, H, ep, T, want in cases:
@@ -420,7 +427,7 @@ def test_split_rows_is_covered_by_workspace_bytes(lib):
                         assert not (split and seen_fused), (R, H, k, ep, T)
                         seen_fused |= not split
                         if split:
-                            assert T * R * H * 2 <= cap_bytes, (R, H, k, ep, T)
+                            assert T * H * 4 <= cap_bytes, (R, H, k, ep, T)
 
 
 def test_launch_table_split_and_fused_rules(lib):
@@ -440,11 +447,11 @@ def test_launch_table_split_and_fused_rules(lib):
         assert frn.split_rows(8, 10, 8, 6144, frn.EPI_SANDWICH)         # sandwich: '*' rule
         assert not frn.split_rows(8, 10, 257, 6144, ep=True)            # never above 256
         assert frn.launch_shape(8, 10, 200, 6144, ep=True) == base      # vec rules untouched
-        assert lib.frn_workspace_bytes(5000, 6144, 8, 10) == 256 * 8 * 6144 * 2
+        assert lib.frn_workspace_bytes(5000, 6144, 8, 10) == 256 * 6144 * 4
         frn.set_launch_table("6144 8 10 * 0 * fused\n")
         assert not frn.split_rows(8, 10, 1, 6144)
         assert not frn.split_rows(8, 10, 1, 6144, ep=True)
-        assert lib.frn_workspace_bytes(5000, 6144, 8, 10) == 96 * 8 * 6144 * 2  # built-in bound
+        assert lib.frn_workspace_bytes(5000, 6144, 8, 10) == 128 * 6144 * 4  # built-in bound
         for bad in ("6144 8 10 rmsnorm 0 * splits", "6144 8 10 rmsnorm 0 * 3"):
             with pytest.raises(ValueError):
                 frn.set_launch_table(bad)
@@ -660,6 +667,8 @@ def test_launch_table_pipelined_rules():
     import tp_reduction_rmsnorm_amd as frn
     S, N = frn.EPI_SANDWICH, frn.EPI_RMSNORM
     try:
+        frn.set_launch_table(None)
+        base = frn.launch_shape(8, 0, 4096, 8192, S)
         frn.set_launch_table("5120 4 0 sandwich 0 * p1\n")
         assert frn.launch_pipelined(4, 0, 8, 5120, S)
         assert frn.launch_shape(4, 0, 8, 5120, S) == (640, 1)
@@ -669,8 +678,8 @@ def test_launch_table_pipelined_rules():
         frn.set_launch_table("* * * * 0 * p2\n")
         assert frn.launch_pipelined(2, 0, 8, 1024, N)              # 128 vectors: 64 lanes
         assert frn.launch_shape(2, 0, 8, 1024, N) == (64, 2)
-        assert not frn.launch_pipelined(8, 0, 4096, 8192, S)       # does not fit: built-in
-        assert frn.launch_shape(8, 0, 4096, 8192, S) == (256, 4)
+        assert not frn.launch_pipelined(8, 0, 4096, 8192, S)       # does not fit: skipped
+        assert frn.launch_shape(8, 0, 4096, 8192, S) == base        # the compiled-in rule
         assert not frn.launch_pipelined(2, 0, 8, 520, N)           # 65 vectors: skipped
         assert not frn.launch_pipelined(4, 10, 8, 6144, N)         # finalize: skipped
         for bad in ("5120 4 0 sandwich 0 * p3\n", "5120 4 0 sandwich 0 * p\n",
@@ -904,7 +913,7 @@ def test_caller_table_and_builtin_rule_override_the_compiled_in_table():
         assert not frn.launch_pipelined(4, 0, 1100, 5120, S)      # hand-fitted: not below 1536
         assert frn.launch_pipelined(4, 0, 1300, 5120, S)          # the table again
         frn.set_launch_table("6144 8 10 rmsnorm 0 256 builtin\n")
-        assert frn.split_rows(8, 10, 96, 6144) and not frn.split_rows(8, 10, 97, 6144)
+        assert frn.split_rows(8, 10, 128, 6144) and not frn.split_rows(8, 10, 129, 6144)
     finally:
         frn.set_launch_table(None)
 

@@ -24,13 +24,13 @@ int main(void) {
     EXPECT(frn_query(FRN_MAX_R + 1, 0, 8, 512, FRN_EPI_RMSNORM) == FRN_ERR_UNSUPPORTED);
     EXPECT(frn_query(2, 0, FRN_MAX_T + 1LL, 512, FRN_EPI_RMSNORM) == FRN_ERR_UNSUPPORTED);
     EXPECT(frn_query(0, 0, 8, 512, FRN_EPI_RMSNORM) == FRN_ERR_INVALID);
-    EXPECT(frn_workspace_bytes(64, 6144, 8, 10) == (size_t)64 * 8 * 6144 * 2);
+    EXPECT(frn_workspace_bytes(64, 6144, 8, 10) == (size_t)64 * 6144 * 4);
     EXPECT(frn_workspace_bytes(64, 6144, 8, 0) == 0);
     EXPECT(frn_launch_shape(8, 10, 1024, 6144, FRN_EPI_RMSNORM | FRN_SHAPE_EP, &th, &vec) == FRN_OK);
     EXPECT(th == 768 && vec == 1);
     EXPECT(frn_split_rows(8, 10, 16, 6144, FRN_EPI_RMSNORM | FRN_SHAPE_EP) == 1);
-    EXPECT(frn_split_rows(8, 10, 64, 6144, FRN_EPI_RMSNORM | FRN_SHAPE_EP) == 0);
-    EXPECT(frn_split_rows(8, 10, 64, 6144, FRN_EPI_RMSNORM) == 1);
+    EXPECT(frn_split_rows(8, 10, 96, 6144, FRN_EPI_RMSNORM | FRN_SHAPE_EP) == 0);
+    EXPECT(frn_split_rows(8, 10, 96, 6144, FRN_EPI_RMSNORM) == 1);
     /* a rejected call names its reason and launches nothing */
     EXPECT(frn_reduce_residual_rmsnorm(parts, 2, NULL, NULL, 1e-6f, 4, 64, NULL, NULL, NULL, 0,
                                        NULL) == FRN_ERR_INVALID);

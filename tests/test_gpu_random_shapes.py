@@ -73,12 +73,6 @@ def test_random_shape_matches_oracle(case):
             e = m.EPI_SANDWICH if epi == "sandwich" else m.EPI_RMSNORM
             y = torch.empty(T, H, dtype=torch.bfloat16, device=P.DEV)
             x = torch.empty(T, H, dtype=torch.bfloat16, device=P.DEV)
-            if m.split_rows(R, k, T, H, e) and R * T * H * 2 > m.NOALLOC_SCRATCH_BYTES:
-                with pytest.raises(m.FusedReduceNormUnsupported, match="scratch"):
-                    m.moe_finalize_reduce_norm_noalloc(
-                        d.expert_rows, d.topk_w, d.topk_idx, d.residual, d.gamma1, d.gamma2,
-                        d.eps, out=y, residual_out=x, shared=d.shared, epilogue=e)
-                return
             m.moe_finalize_reduce_norm_noalloc(d.expert_rows, d.topk_w, d.topk_idx, d.residual,
                                                d.gamma1, d.gamma2, d.eps, out=y, residual_out=x,
                                                shared=d.shared, epilogue=e)

@@ -160,6 +160,9 @@ def query(R: int, k: int, T: int, H: int, epilogue: int = EPI_RMSNORM) -> bool:
 
 
 def workspace_bytes(max_T: int, H: int, R: int, k: int = 0) -> int:
+    """Bytes of the optional workspace of the finalize calls for up to max_T
+    tokens: T x H FP32 rank sums of the split-row finalize, for the largest
+    T it is taken at (0: never)."""
     return int(_c_ws(max_T, H, R, k))
 
 
@@ -594,11 +597,11 @@ def moe_finalize_reduce_norm_noalloc(expert_rows: TensorList, topk_weights: torc
                                      stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """``moe_finalize_reduce_norm`` for callers that cannot allocate: the
     outputs are the caller's (``out`` and ``residual_out`` are required) and
-    the split-row finalize's partials go to the library's own scratch array
-    on the GPU (``NOALLOC_SCRATCH_BYTES``), so neither this function nor the
-    C call allocates.  A call whose split-row finalize needs more scratch
-    raises ``FusedReduceNormUnsupported``.  Calls that may overlap in time
-    on one GPU share that array and race: serialise them."""
+    the split-row finalize's FP32 rank sums go to the library's own scratch
+    array on the GPU (``NOALLOC_SCRATCH_BYTES``, enough for the largest
+    split-row call), so neither this function nor the C call allocates.
+    Calls that may overlap in time on one GPU share that array and race:
+    serialise them."""
     if out is None or residual_out is None:
         raise ValueError("out and residual_out are required: this call allocates nothing")
     es = _listed(expert_rows)

@@ -251,10 +251,10 @@ frn_status run(const Call& c, int32_t epilogue, int64_t T, void* stream) {
 // chosen mode declines the call, as a misaligned one does.
 frn_status set_workspace(Call& c, void* workspace, size_t workspace_bytes, int32_t k, int64_t T,
                          int64_t H, int32_t R, int32_t epilogue) {
-    c.a.ws_p = nullptr;
+    c.a.ws_sum = nullptr;
     if (k == 0 || workspace == nullptr) return FRN_OK;
     if (!frn::use_split_rows(R, H, k, c.a.ep != 0, epilogue, T)) return FRN_OK;
-    const size_t need = frn::split_workspace_bytes(T, H, R);
+    const size_t need = frn::split_workspace_bytes(T, H);
     if (workspace_bytes < need)
         return fail(FRN_ERR_UNSUPPORTED,
                     "workspace of %zu bytes is smaller than the %zu bytes the split-row "
@@ -264,7 +264,7 @@ frn_status set_workspace(Call& c, void* workspace, size_t workspace_bytes, int32
         return fail(FRN_ERR_UNSUPPORTED, "workspace is not 256-byte aligned");
     frn_status st = add_out(c, "workspace", workspace, need);
     if (st != FRN_OK) return st;
-    c.a.ws_p = static_cast<uint4*>(workspace);
+    c.a.ws_sum = static_cast<float4*>(workspace);
     return FRN_OK;
 }
 
@@ -410,9 +410,9 @@ FRN_API frn_status frn_moe_finalize_reduce_norm_noalloc(
                            residual_out)) != FRN_OK)
         return st;
     if ((st = check_alias(c)) != FRN_OK) return st;
-    c.a.ws_p = nullptr;
+    c.a.ws_sum = nullptr;
     if (frn::use_split_rows(R, H, k, false, epilogue, T)) {
-        const size_t need = frn::split_workspace_bytes(T, H, R);
+        const size_t need = frn::split_workspace_bytes(T, H);
         if (need > (size_t)FRN_NOALLOC_SCRATCH_BYTES)
             return fail(FRN_ERR_UNSUPPORTED,
                         "the split-row finalize needs %zu bytes of scratch at R=%d T=%lld "
@@ -421,7 +421,7 @@ FRN_API frn_status frn_moe_finalize_reduce_norm_noalloc(
                         (size_t)FRN_NOALLOC_SCRATCH_BYTES);
         void* p = nullptr;
         if ((st = scratch_address(stream, &p)) != FRN_OK) return st;
-        c.a.ws_p = static_cast<uint4*>(p);
+        c.a.ws_sum = static_cast<float4*>(p);
     }
     return run(c, epilogue, T, stream);
 }
@@ -586,7 +586,7 @@ FRN_API size_t frn_workspace_bytes(int64_t max_T, int64_t H, int32_t R, int32_t 
         return 0;
     const int64_t cap = frn::split_rows_cap(R, H, k);
     const int64_t t = max_T < cap ? max_T : cap;
-    return t < 1 ? 0 : frn::split_workspace_bytes(t, H, R);
+    return t < 1 ? 0 : frn::split_workspace_bytes(t, H);
 }
 
 FRN_API int32_t frn_split_rows(int32_t R, int32_t k, int64_t T, int64_t H, int32_t epilogue) {

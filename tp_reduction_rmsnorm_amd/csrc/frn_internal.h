@@ -33,7 +33,7 @@ struct RowArgs {
     uint4* residual_out;             // [T,H]
     int64_t num_rows[FRN_MAX_R];     // rows in each rank's expert buffer
     int64_t T;                       // token rows of the call
-    uint4* ws_p;                     // split-row finalize: R x T x nvec BF16 partials, or null
+    float4* ws_sum;                  // split-row finalize: [T,H] FP32 rank sums, or null
     uint4* part_out[FRN_MAX_R];      // finalize_slices_kernel: [T,H] BF16 output per rank
     int32_t R;                       // ranks
     int32_t k;                       // top-k slots (0: no finalize)
@@ -44,17 +44,17 @@ struct RowArgs {
                                      // marks a slot of another rank's expert
 };
 
-// Split-row finalize (small T): workgroup size, the largest T any call may
-// take it at, and its workspace, R x T x H BF16 finalized partials (no other
+// Standalone finalize: workgroup size (one slice of one rank's row).
+constexpr int kSplitThreads = 256;
+
+// Split-row finalize (small T): the largest T any call may take it at, and
+// its workspace, the T x H FP32 sums of the R finalized partials (no other
 // state: the workspace needs no initialisation and keeps nothing between
 // calls).
-constexpr int kSplitThreads = 256;
 constexpr int64_t kSplitCapT = 256;
 
 // Workspace bytes the split-row finalize needs for T rows.
-inline size_t split_workspace_bytes(int64_t T, int64_t H, int32_t R) {
-    return (size_t)T * (size_t)R * (size_t)H * 2;
-}
+inline size_t split_workspace_bytes(int64_t T, int64_t H) { return (size_t)T * (size_t)H * 4; }
 
 // Whether a finalize call (k >= 1) that is given a large enough workspace
 // takes the split-row finalize: the first matching split/fused rule of the
@@ -67,7 +67,7 @@ bool use_split_rows(int32_t R, int64_t H, int32_t k, bool ep, int epilogue, int6
 // must cover.  Thread-safe.
 int64_t split_rows_cap(int32_t R, int64_t H, int32_t k);
 
-// Column slices of one row in the split-row finalize.
+// Column slices of one row in the standalone finalize.
 int split_slices(int nvec);
 
 // Launch shape of one call: `threads` lanes per row, each lane owning `vec`

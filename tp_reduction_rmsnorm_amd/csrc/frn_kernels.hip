@@ -1,8 +1,8 @@
 // frn_kernels.hip -- gfx950 kernels of the fused reduce + norm boundary.
 //
-// Three kernels (row_kernel, rows_pipelined_kernel and
-// finalize_slices_kernel, each in several instantiations) share the per-row
-// building blocks below.
+// Four kernels (row_kernel, rows_pipelined_kernel,
+// finalize_sum_slices_kernel and finalize_slices_kernel, each in several
+// instantiations) share the per-row building blocks below.
 //
 // row_kernel: one token row per workgroup.  Each lane owns V 16-byte vectors
 // of the row (8 BF16 values each), placed `threads` vectors apart so every
@@ -18,15 +18,20 @@
 // and partials are in flight while the current row runs its epilogue, so
 // every CU keeps reading while it writes.
 //
-// finalize_slices_kernel: for the MoE finalize at small T, where one
+// finalize_sum_slices_kernel: for the MoE finalize at small T, where one
 // workgroup per token would walk the R ranks one memory round trip after
-// another.  Workgroup (t, r, c) finalizes slice c of rank r of token t and
-// stores the BF16 partial into the caller's workspace -- the per-rank
-// finalize materialized -- and row_kernel then reduces those R partials in
-// rank order and runs the epilogue.  The kernel boundary orders the two, so
-// no workgroup waits for another and no cross-XCD cache maintenance is
-// issued inside a kernel (a device-scope fence per workgroup writes back and
-// invalidates the whole L2 of its XCD, which measured far slower).
+// another.  Workgroup (t, c) takes a 64-vector slice of token t with one
+// wave per rank: each wave finalizes its rank's slice, the R BF16 partials
+// meet in LDS and are summed in rank order, and the FP32 sum goes to the
+// caller's workspace; row_kernel then reads it back and runs the epilogue.
+// The kernel boundary orders the two, so no workgroup waits for another and
+// no cross-XCD cache maintenance is issued inside a kernel (a device-scope
+// fence per workgroup writes back and invalidates the whole L2 of its XCD,
+// which measured far slower).
+//
+// finalize_slices_kernel: the standalone per-rank finalize.  Workgroup
+// (t, r, c) finalizes slice c of rank r of token t and stores the BF16
+// partial to rank r's output.
 //
 // Row-wide sums of squares are FP64: per lane, then within each wave (DPP
 // swaps and four lane reads in a fixed order), then one LDS slot per wave
@@ -605,13 +610,14 @@ __device__ __forceinline__ void epilogue(const RowArgs& a, int64_t row, const La
 // ------------------------------------------------------------ kernels --- //
 
 // Finalize variants of the one-row kernel.
-enum Fin { kNoFin = 0, kFinTp = 1, kFinEp = 2 };
+enum Fin { kNoFin = 0, kFinTp = 1, kFinEp = 2, kFinSum = 3 };
 
 // One token row per workgroup.  EPI: epilogue; FIN: top-k finalize ahead of
 // the reduction (kFinTp: every rank routes every slot, one rank after the
-// other; kFinEp: expert-parallel routing, the work list across ranks); V:
-// vectors per lane; C: ranks (no finalize), top-k slots (kFinTp) or live
-// rows (kFinEp) loaded per chunk.
+// other; kFinEp: expert-parallel routing, the work list across ranks;
+// kFinSum: the rank sum already formed by finalize_sum_slices_kernel, read
+// back as FP32); V: vectors per lane; C: ranks (no finalize), top-k slots
+// (kFinTp) or live rows (kFinEp) loaded per chunk.
 template <int EPI, int FIN, int V, int C>
 __global__ __launch_bounds__(1024) void row_kernel(const RowArgs a) {
     __shared__ double slots[2][16];
@@ -631,6 +637,16 @@ __global__ __launch_bounds__(1024) void row_kernel(const RowArgs a) {
 
     if constexpr (FIN == kNoFin) {
         reduce_ranks<V, C, true>([&](int r) { return a.src[r] + row; }, a.R, L, s);
+    } else if constexpr (FIN == kFinSum) {
+#pragma unroll
+        for (int j = 0; j < V; ++j) {
+            if (!L.ok[j]) continue;
+            const float4* p = a.ws_sum + 2 * (row + L.vi[j]);
+            const float4 lo = p[0];
+            const float4 hi = p[1];
+            s[j][0] = lo.x; s[j][1] = lo.y; s[j][2] = lo.z; s[j][3] = lo.w;
+            s[j][4] = hi.x; s[j][5] = hi.y; s[j][6] = hi.z; s[j][7] = hi.w;
+        }
     } else if constexpr (FIN == kFinEp) {
         // a rank owns few of the token's slots: keep several ranks' rows in flight
         finalize_reduce<V, C>(a, t, L, s);
@@ -662,6 +678,43 @@ __global__ __launch_bounds__(kSplitThreads) void finalize_slices_kernel(const Ro
     float acc[1][8];
     finalize_rank<1, C, EARLY_SHARED>(a, r, t, L, acc);
     if (L.ok[0]) a.part_out[r][t * a.nvec + L.vi[0]] = narrow(acc[0]);
+}
+
+// Split-row finalize, first kernel: workgroup (t, c) takes vectors
+// [64c, 64c + 64) of token t, one wave per rank.  Wave r finalizes rank r's
+// slice (all of its top-k rows in one chunk of C >= k loads) and parks the
+// BF16-rounded partial in LDS; after the barrier wave 0 adds the R partials
+// in rank order and stores the FP32 sum -- bit for bit what the one-row
+// kernel holds before its epilogue, which row_kernel<EPI, kFinSum> then runs
+// from the workspace.  The R partials never reach HBM: the workspace holds
+// one FP32 row per token where a BF16 partial per rank would take R.
+template <bool EARLY_SHARED, int C>
+__global__ __launch_bounds__(64 * FRN_MAX_R) void finalize_sum_slices_kernel(const RowArgs a,
+                                                                             int S) {
+    __shared__ uint4 part[FRN_MAX_R][64];
+    const int lane = threadIdx.x & 63;
+    const int r = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int c = blockIdx.x % S;
+    const int64_t t = blockIdx.x / S;
+    Lanes<1> L(a.nvec);
+    L.vi[0] = c * 64 + lane;
+    L.ok[0] = L.vi[0] < a.nvec;
+    float acc[1][8];
+    finalize_rank<1, C, EARLY_SHARED>(a, r, t, L, acc);
+    part[r][lane] = narrow(acc[0]);
+    __syncthreads();
+    if (r != 0 || !L.ok[0]) return;
+    float sum[8];
+    widen(part[0][lane], sum);
+    for (int q = 1; q < a.R; ++q) {
+        float f[8];
+        widen(part[q][lane], f);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sum[i] = sum[i] + f[i];
+    }
+    float4* out = a.ws_sum + 2 * (t * a.nvec + L.vi[0]);
+    out[0] = make_float4(sum[0], sum[1], sum[2], sum[3]);
+    out[1] = make_float4(sum[4], sum[5], sum[6], sum[7]);
 }
 
 // Calls f(std::integral_constant<int, C>) with the top-k chunk for k slots:
@@ -942,6 +995,37 @@ hipError_t launch_fin(const RowArgs& a, int64_t T, LaunchShape sh, hipStream_t s
     return launch_v<EPI, kFinTp>(a, T, sh, stream);
 }
 
+// Split-row finalize: finalize_sum_slices_kernel forms the FP32 rank sums in
+// the workspace (a workgroup per token and 64-vector slice, a wave per rank),
+// then row_kernel<EPI, kFinSum> runs the epilogue, one workgroup per token
+// (one vector per lane up to 1024 lanes, two above).  The caller keeps T at
+// or below kSplitCapT, so the first grid stays far below its limit.
+template <int EPI>
+hipError_t launch_split_rows(const RowArgs& a, int64_t T, hipStream_t stream) {
+    if (T > kSplitCapT) return hipErrorInvalidValue;
+    const int S = (a.nvec + 63) / 64;
+    const dim3 grid((unsigned)(T * S));
+    const dim3 block((unsigned)(64 * a.R));
+    // Under expert-parallel routing most ranks hold no shared row, and the
+    // registers of an early shared load would cost occupancy for nothing.
+    with_topk_chunk(a.k, [&](auto c) {
+        constexpr int C = decltype(c)::value;
+        if (a.ep)
+            hipLaunchKernelGGL((finalize_sum_slices_kernel<false, C>), grid, block, 0, stream, a,
+                               S);
+        else
+            hipLaunchKernelGGL((finalize_sum_slices_kernel<true, C>), grid, block, 0, stream, a,
+                               S);
+        return 0;
+    });
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int vec = a.nvec > 1024 ? 2 : 1;
+    const int threads = ((a.nvec + vec - 1) / vec + 63) / 64 * 64;
+    if (vec == 1) return launch<EPI, kFinSum, 1, 1>(a, T, threads, stream);
+    return launch<EPI, kFinSum, 2, 1>(a, T, threads, stream);
+}
+
 }  // namespace
 
 int split_slices(int nvec) { return (nvec + kSplitThreads - 1) / kSplitThreads; }
@@ -972,20 +1056,13 @@ hipError_t launch_finalize(const RowArgs& a, int64_t T, hipStream_t stream) {
     return hipSuccess;
 }
 
-hipError_t launch_rows(const RowArgs& a_in, int epilogue, int64_t T, hipStream_t stream) {
-    RowArgs a = a_in;
-    if (a.k > 0 && a.ws_p != nullptr) {
-        // Split-row finalize: materialize the R finalized partials into the
-        // workspace, then reduce them like ordinary partials.
-        for (int r = 0; r < a.R; ++r) a.part_out[r] = a.ws_p + (int64_t)r * T * a.nvec;
-        const hipError_t e = launch_finalize(a, T, stream);
-        if (e != hipSuccess) return e;
-        for (int r = 0; r < a.R; ++r) {
-            a.src[r] = a.part_out[r];
-            a.shared[r] = nullptr;
+hipError_t launch_rows(const RowArgs& a, int epilogue, int64_t T, hipStream_t stream) {
+    if (a.k > 0 && a.ws_sum != nullptr) {
+        switch (epilogue) {
+            case kRmsNorm: return launch_split_rows<kRmsNorm>(a, T, stream);
+            case kSandwich: return launch_split_rows<kSandwich>(a, T, stream);
+            default: return hipErrorInvalidValue;
         }
-        a.k = 0;
-        a.ep = 0;
     }
     const int fin = a.k == 0 ? kNoFinalize : (a.ep ? kEpFinalize : kTpFinalize);
     const LaunchShape sh = choose_shape(a.nvec, fin, T, epilogue, a.R, a.k);

@@ -282,40 +282,55 @@ int builtin_pipe_vec(int nvec, int fin, int64_t T, int epilogue, int R) {
     return 0;
 }
 
-// The built-in choice of the split-row finalize (a workgroup per (token,
-// rank, 2048-column slice), then the reduction pass) over the one-row
-// finalize, from graph-replay sweeps on MI355X with inputs rotated over
-// 1 GiB.  With one workgroup per token, all R * (k + 1) rows of a token pass
-// through one CU, whose throughput bounds the one-row kernel at small T
+// The built-in choice of the split-row finalize (a workgroup per token and
+// 512-column slice with a wave per rank, summing the R rounded partials in
+// LDS into one FP32 row of the workspace, then the epilogue kernel) over the
+// one-row finalize, from graph-replay sweeps on MI355X with inputs rotated
+// over 1 GiB.  With one workgroup per token, all R * (k + 1) rows of a token
+// pass through one CU, whose throughput bounds the one-row kernel at small T
 // (about 37 GB/s per CU at T=16, R=8, k=10), so its time is nearly flat in
 // T; the split-row finalize spreads a token over many workgroups but writes
-// and re-reads R partial rows per token, so its time grows with T from a
-// lower start.
-// Largest T at which the split-row finalize still won (25 shapes):
-//  - TP routing, R <= 2: 32 at H*k >= 32768 (H=7168 k=8: 9.1 against 9.8
-//    us at T=32, 10.0 against 9.9 at T=48; H=5120 k=16 the same); none
-//    below (H=4096 k=4 and H=2048 k=8 are within 5% either way);
-//  - TP routing, 3 <= R <= 8: 96 at H > 4096 (H=6144 R=8 k=10: 28.1 against
-//    33.0 us at T=96, 35.9 against 33.2 at T=128; the same at H=5120 R=4,
-//    H=7168 R=8, H=8192 R=4 and H=16384 R=8); 192 at H <= 4096 (H=4096 R=8
-//    k=8: 25.9 against 26.9 us at T=192; H=3072 R=8, H=2048 R=4 and R=8);
-//  - TP routing, R=16: 128 at H <= 4096, 96 above (H=7168: 66.9 against
-//    57.4 us at T=128);
+// and re-reads one FP32 row per token and adds a second launch, so its time
+// grows with T from a lower start.
+// Largest T at which the split-row finalize still won (25 shapes, T = 1, 8,
+// 16, 32, 48, 64, 96, 128, 160, 192, 224, 256):
+//  - TP routing, R = 1: none (H=7168 k=8: 6.4 against 6.3 us at T=1);
+//  - TP routing, R = 2: 48 at H*k >= 32768 (H=7168 k=8: 9.4 against 9.7 us
+//    at T=48, 10.5 against 9.8 at T=64), 64 at H*k >= 65536 (H=5120 k=16:
+//    11.0 against 12.4 us at T=64, 12.7 each at T=96); none below (H=4096
+//    k=4: 5.5 against 5.3 us at T=1; H=2048 k=8 within 5% either way);
+//  - TP routing, 3 <= R: 224 at H <= 3072 (H=3072 R=8 k=8: 23.0 against
+//    24.0 us at T=224; H=2048 R=4 12.8 against 12.6 at T=256), 192 at
+//    H <= 4096 (H=4096 R=8 k=8: 24.6 against 24.9 us at T=192, 28.0 against
+//    26.2 at T=224; H=4096 R=16 the same); above, 128 at R >= 5 (H=6144
+//    R=8 k=10: 28.9 against 30.5 us at T=128, 35.6 against 32.2 at T=160;
+//    the same at k=2 and 4, H=7168 R=8 and R=16, H=16384 R=8) and 96 at
+//    R <= 4 (H=5120 R=4 k=8: 12.6 against 13.9 us at T=96, 14.6 against
+//    14.3 at T=128; H=8192 R=4 the same), R=3 taken as 64;
 //  - expert-parallel routing, where the one-row kernel already keeps
-//    several ranks' rows in flight: 8 at R <= 2, 16 at R <= 8 (H=6144 R=8
-//    k=10: 9.8 against 10.9 us at T=16, 11.0 each at T=32, 13.8 against
-//    11.2 at T=64), 48 at H <= 2048, and at R=16 48 for k >= 8 and 32 below
-//    (H=3072 k=6: 11.6 against 10.7 us at T=48).
+//    several ranks' rows in flight and the split kernel's waves of ranks
+//    without a live slot idle: 8 at R <= 2 (H=6144 k=8: 7.2 against 7.4 us
+//    at T=8, 7.7 each at T=16); 16 at k <= 4 (H=6144 R=8 k=4: 7.1 against
+//    7.3 at T=16, 8.2 against 7.3 at T=32); 160 at H <= 2048 (R=8 k=8: 8.8
+//    against 9.1 us at T=160); 96 at R >= 16 and H <= 4096 (H=4096 k=8: 12.2
+//    against 13.8 us at T=96, 14.2 against 13.9 at T=128; H=3072 k=6 10.8
+//    against 11.0), 64 above; else 32 at R <= 4 (H=7168 R=4 k=8: 8.8
+//    against 9.1 us at T=32, 9.2 each at T=48) and 64 (H=6144 R=8 k=10:
+//    10.1 against 11.0 us at T=64, 13.3 against 11.1 at T=96).
 int64_t builtin_split_max_t(int32_t R, int64_t H, int32_t k, bool ep) {
     if (ep) {
         if (R <= 2) return 8;
-        if (H <= 2048) return 48;
-        if (R >= 16) return k >= 8 ? 48 : 32;
-        return 16;
+        if (k <= 4) return 16;
+        if (H <= 2048) return 160;
+        if (R >= 16) return H <= 4096 ? 96 : 64;
+        return R <= 4 ? 32 : 64;
     }
-    if (R <= 2) return H * k >= 32768 ? 32 : 0;
-    if (R >= 16) return H <= 4096 ? 128 : 96;
-    return H <= 4096 ? 192 : 96;
+    if (R == 1) return 0;
+    if (R == 2) return H * k >= 65536 ? 64 : H * k >= 32768 ? 48 : 0;
+    if (H <= 3072) return 224;
+    if (H <= 4096) return 192;
+    if (R == 3) return 64;
+    return R <= 4 ? 96 : 128;
 }
 
 bool matches(const Rule& r, int64_t H, int64_t R, int64_t k, int64_t epilogue, int64_t ep) {

@@ -22,8 +22,8 @@ Shapes with a finalize (k > 0, not ``sum``) are also timed at
 ``--split-tokens`` (T <= 256) with the split-row finalize forced (a
 workspace and a ``split`` rule) against the one-row kernel (no workspace);
 the winner per T becomes ``split`` / ``fused`` rules.  The vec rules of a
-finalize shape describe the one-row kernel; where the split-row finalize
-runs, its reduction pass is a k = 0 call of the same H and R.  An epilogue
+finalize shape describe the one-row kernel; the split-row finalize's two
+kernels take fixed shapes (a wave per rank, then one workgroup per token).  An epilogue
 named ``ep-rmsnorm`` or ``ep-sandwich`` tunes the expert-parallel finalize
 (``ep_moe_finalize_reduce_norm``): each of the R ranks owns an equal share
 of 4R experts (at least k), and each token picks k distinct ones at random.
@@ -48,7 +48,7 @@ DEFAULT_SHAPES = [(5120, 4, 0, "sandwich"), (8192, 8, 0, "sandwich"), (512, 2, 0
                   (6144, 8, 0, "rmsnorm"), (6144, 8, 10, "rmsnorm"), (7168, 2, 8, "rmsnorm"),
                   (7168, 2, 0, "rmsnorm"), (7168, 2, 8, "sum"), (6144, 8, 10, "ep-rmsnorm")]
 DEFAULT_TOKENS = [1, 8, 64, 256, 512, 1024, 2048, 4096, 16384]
-DEFAULT_SPLIT_TOKENS = [1, 8, 16, 32, 48, 64, 96, 128, 192, 256]
+DEFAULT_SPLIT_TOKENS = [1, 8, 16, 32, 48, 64, 96, 128, 160, 192, 224, 256]
 
 
 def _bf16(shape, dev, g):
