@@ -67,8 +67,8 @@ extern "C" {
 #define FRN_MAX_H 16384  /* hidden size */
 #define FRN_MAX_T 4194303 /* token rows per call (a row's workgroup has up to
                              1024 lanes, and a dispatch holds < 2^32 lanes) */
-#define FRN_NOALLOC_SCRATCH_BYTES (16u << 20) /* scratch per GPU of
-                             frn_moe_finalize_reduce_norm_noalloc (16 MiB) */
+#define FRN_NOALLOC_SCRATCH_BYTES (17u << 20) /* scratch per GPU of
+                             frn_moe_finalize_reduce_norm_noalloc (17 MiB) */
 
 typedef enum frn_status {
     FRN_OK = 0,

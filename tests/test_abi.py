@@ -112,6 +112,12 @@ TUNED_INC = os.path.join(ROOT, "tp_reduction_rmsnorm_amd", "csrc", "frn_tuned_mi
 HAND_FITTED = "* * * * 0 * builtin\n"   # every call: the hand-fitted rule
 
 
+def split_ws(T, H):
+    """The split-row finalize's workspace: T x H FP32 rows, then T x S FP64
+    sums of squares (S = 64-vector slices of a row)."""
+    return T * H * 4 + T * (-(-(H // 8) // 64)) * 8
+
+
 @pytest.fixture
 def hand_fitted():
     """Every call under the hand-fitted rule for the test's duration."""
@@ -254,18 +260,19 @@ def test_noalloc_zero_tokens_is_a_no_op(lib):
 
 
 def test_noalloc_scratch_covers_every_split_row_call(lib):
-    """The scratch array holds the FP32 rank sums of the largest call the
-    split-row finalize takes (256 tokens of H=16384: T*H*4 bytes), so the
-    no-allocation entry point never declines for its size."""
+    """The scratch array holds the workspace of the largest call the
+    split-row finalize takes (256 tokens of H=16384: FP32 rows and FP64
+    slice sums), so the no-allocation entry point never declines for its
+    size."""
     import tp_reduction_rmsnorm_amd as frn
     cap = noalloc_scratch_bytes()
-    assert cap == frn.NOALLOC_SCRATCH_BYTES == 16 << 20
-    assert 256 * 16384 * 4 == cap
+    assert cap == frn.NOALLOC_SCRATCH_BYTES == 17 << 20
+    assert split_ws(256, 16384) == 256 * 16384 * 4 + 256 * 32 * 8 <= cap
     frn.set_launch_table("* * * * 0 * split\n")   # split wherever the library allows
     try:
         R, k, H, T = 16, 16, 16384, 256
         assert frn.split_rows(R, k, T, H) and not frn.split_rows(R, k, T + 1, H)
-        assert lib.frn_workspace_bytes(100000, H, R, k) == T * H * 4 == cap
+        assert lib.frn_workspace_bytes(100000, H, R, k) == split_ws(T, H) <= cap
     finally:
         frn.set_launch_table(None)
     assert lib.frn_workspace_bytes(100000, 6144, 8, 10) <= cap
@@ -353,18 +360,18 @@ def test_workspace_bytes(lib):
     lib.frn_set_launch_table.argtypes = [ctypes.c_char_p]
     assert lib.frn_set_launch_table(HAND_FITTED.encode()) == OK
     try:
-        assert lib.frn_workspace_bytes(8, 6144, 8, 10) == 8 * 6144 * 4   # FP32 rank sums
+        assert lib.frn_workspace_bytes(8, 6144, 8, 10) == split_ws(8, 6144)   # FP32 sums
         # covers the largest T either routing splits at: R=8 H=6144 -> 128 (TP)
-        assert lib.frn_workspace_bytes(5000, 6144, 8, 10) == 128 * 6144 * 4
-        assert lib.frn_workspace_bytes(5000, 4096, 2, 4) == 8 * 4096 * 4   # EP only
+        assert lib.frn_workspace_bytes(5000, 6144, 8, 10) == split_ws(128, 6144)
+        assert lib.frn_workspace_bytes(5000, 4096, 2, 4) == split_ws(8, 4096)   # EP only
         assert lib.frn_workspace_bytes(64, 5120, 4, 0) == 0      # no finalize: none used
         assert lib.frn_workspace_bytes(64, 5124, 4, 2) == 0      # unsupported H
         assert lib.frn_workspace_bytes(0, 5120, 4, 2) == 0
         assert lib.frn_workspace_bytes(8, 5120, 4, 17) == 0      # k beyond FRN_MAX_K
         # the size covers the compiled-in table's split rules too
-        assert lib.frn_workspace_bytes(5000, 7168, 2, 8) == max(
+        assert lib.frn_workspace_bytes(5000, 7168, 2, 8) == split_ws(max(
             [48] + [int(r[5]) for r in tuned_rules()
-                    if r[:3] == ["7168", "2", "8"] and r[6] == "split"]) * 7168 * 4
+                    if r[:3] == ["7168", "2", "8"] and r[6] == "split"]), 7168)
     finally:
         lib.frn_set_launch_table(None)
 
@@ -427,7 +434,7 @@ def test_split_rows_is_covered_by_workspace_bytes(lib):
                         assert not (split and seen_fused), (R, H, k, ep, T)
                         seen_fused |= not split
                         if split:
-                            assert T * H * 4 <= cap_bytes, (R, H, k, ep, T)
+                            assert split_ws(T, H) <= cap_bytes, (R, H, k, ep, T)
 
 
 def test_launch_table_split_and_fused_rules(lib):
@@ -447,11 +454,11 @@ def test_launch_table_split_and_fused_rules(lib):
         assert frn.split_rows(8, 10, 8, 6144, frn.EPI_SANDWICH)         # sandwich: '*' rule
         assert not frn.split_rows(8, 10, 257, 6144, ep=True)            # never above 256
         assert frn.launch_shape(8, 10, 200, 6144, ep=True) == base      # vec rules untouched
-        assert lib.frn_workspace_bytes(5000, 6144, 8, 10) == 256 * 6144 * 4
+        assert lib.frn_workspace_bytes(5000, 6144, 8, 10) == split_ws(256, 6144)
         frn.set_launch_table("6144 8 10 * 0 * fused\n")
         assert not frn.split_rows(8, 10, 1, 6144)
         assert not frn.split_rows(8, 10, 1, 6144, ep=True)
-        assert lib.frn_workspace_bytes(5000, 6144, 8, 10) == 128 * 6144 * 4  # built-in bound
+        assert lib.frn_workspace_bytes(5000, 6144, 8, 10) == split_ws(128, 6144)  # built-in
         for bad in ("6144 8 10 rmsnorm 0 * splits", "6144 8 10 rmsnorm 0 * 3"):
             with pytest.raises(ValueError):
                 frn.set_launch_table(bad)

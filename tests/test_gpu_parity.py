@@ -486,7 +486,7 @@ def test_split_row_workspace_explicit_and_reused():
     m = frn()
     R, H, k = 8, 6144, 10
     need = m.workspace_bytes(128, H, R, k)
-    assert need == 128 * H * 4  # the FP32 rank sums of 128 tokens
+    assert need == 128 * H * 4 + 128 * 12 * 8  # FP32 rows and FP64 slice sums, 128 tokens
     assert m.workspace_bytes(1000, H, R, k) == need  # the largest T that splits here
     assert m.workspace_bytes(64, H, R, 0) == 0
     ws = torch.full((need,), 0xA5, dtype=torch.uint8, device=DEV)  # no initialisation needed

@@ -60,7 +60,7 @@ EPI_SANDWICH = 1
 MAX_R = 16
 MAX_K = 16
 MAX_H = 16384
-NOALLOC_SCRATCH_BYTES = 16 << 20  # FRN_NOALLOC_SCRATCH_BYTES
+NOALLOC_SCRATCH_BYTES = 17 << 20  # FRN_NOALLOC_SCRATCH_BYTES
 
 
 class FusedReduceNormError(RuntimeError):
@@ -161,8 +161,8 @@ def query(R: int, k: int, T: int, H: int, epilogue: int = EPI_RMSNORM) -> bool:
 
 def workspace_bytes(max_T: int, H: int, R: int, k: int = 0) -> int:
     """Bytes of the optional workspace of the finalize calls for up to max_T
-    tokens: T x H FP32 rank sums of the split-row finalize, for the largest
-    T it is taken at (0: never)."""
+    tokens: the split-row finalize's T x H FP32 rows and T x ceil(H / 512)
+    FP64 sums of squares, for the largest T it is taken at (0: never)."""
     return int(_c_ws(max_T, H, R, k))
 
 

@@ -265,6 +265,8 @@ frn_status set_workspace(Call& c, void* workspace, size_t workspace_bytes, int32
     frn_status st = add_out(c, "workspace", workspace, need);
     if (st != FRN_OK) return st;
     c.a.ws_sum = static_cast<float4*>(workspace);
+    c.a.ws_ss = reinterpret_cast<double*>(static_cast<char*>(workspace) +
+                                          frn::split_ss_offset(T, H));
     return FRN_OK;
 }
 
@@ -422,6 +424,7 @@ FRN_API frn_status frn_moe_finalize_reduce_norm_noalloc(
         void* p = nullptr;
         if ((st = scratch_address(stream, &p)) != FRN_OK) return st;
         c.a.ws_sum = static_cast<float4*>(p);
+        c.a.ws_ss = reinterpret_cast<double*>(static_cast<char*>(p) + frn::split_ss_offset(T, H));
     }
     return run(c, epilogue, T, stream);
 }

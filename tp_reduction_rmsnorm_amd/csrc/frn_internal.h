@@ -33,7 +33,9 @@ struct RowArgs {
     uint4* residual_out;             // [T,H]
     int64_t num_rows[FRN_MAX_R];     // rows in each rank's expert buffer
     int64_t T;                       // token rows of the call
-    float4* ws_sum;                  // split-row finalize: [T,H] FP32 rank sums, or null
+    float4* ws_sum;                  // split-row finalize: [T,H] FP32 rank sums (residual +
+                                     // RMSNorm: the row h), or null
+    double* ws_ss;                   // split-row finalize: [T,S] slice sums of squares
     uint4* part_out[FRN_MAX_R];      // finalize_slices_kernel: [T,H] BF16 output per rank
     int32_t R;                       // ranks
     int32_t k;                       // top-k slots (0: no finalize)
@@ -47,14 +49,21 @@ struct RowArgs {
 // Standalone finalize: workgroup size (one slice of one rank's row).
 constexpr int kSplitThreads = 256;
 
-// Split-row finalize (small T): the largest T any call may take it at, and
-// its workspace, the T x H FP32 sums of the R finalized partials (no other
-// state: the workspace needs no initialisation and keeps nothing between
-// calls).
+// Split-row finalize (small T): the largest T any call may take it at, the
+// 64-vector column slices of a row, and its workspace: the T x H FP32 sums
+// of the R finalized partials, then T x S FP64 slice sums of squares (no
+// other state: the workspace needs no initialisation and keeps nothing
+// between calls).
 constexpr int64_t kSplitCapT = 256;
 
-// Workspace bytes the split-row finalize needs for T rows.
-inline size_t split_workspace_bytes(int64_t T, int64_t H) { return (size_t)T * (size_t)H * 4; }
+inline int split_row_slices(int nvec) { return (nvec + 63) / 64; }
+
+// Workspace bytes the split-row finalize needs for T rows, and where its
+// sums of squares start.
+inline size_t split_ss_offset(int64_t T, int64_t H) { return (size_t)T * (size_t)H * 4; }
+inline size_t split_workspace_bytes(int64_t T, int64_t H) {
+    return split_ss_offset(T, H) + (size_t)T * (size_t)split_row_slices((int)(H / 8)) * 8;
+}
 
 // Whether a finalize call (k >= 1) that is given a large enough workspace
 // takes the split-row finalize: the first matching split/fused rule of the

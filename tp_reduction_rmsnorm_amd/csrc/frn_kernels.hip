@@ -132,18 +132,22 @@ __device__ __forceinline__ double readlane_f64(double v, int lane) {
     return __hiloint2double(hi, lo);
 }
 
-// Sum of one double per lane over the workgroup, the same bits in every lane.
-// Within a 16-lane row: DPP swaps (lane ^ 1, ^ 2, then the half-row and row
-// mirrors), each step adding two equal partial sums in either order, so all
-// 16 lanes hold identical bits; the four row sums are then read out and
-// added in row order; the waves' sums meet in LDS and are added in wave order.
-// nw: waves in the workgroup.
-__device__ __forceinline__ double block_sum(double v, double* slots, int nw) {
+// Sum of one double per lane over the wave (wave_sum) or the workgroup
+// (block_sum), the same bits in every lane.  Within a 16-lane row: DPP swaps
+// (lane ^ 1, ^ 2, then the half-row and row mirrors), each step adding two
+// equal partial sums in either order, so all 16 lanes hold identical bits;
+// the four row sums are then read out and added in row order; the waves'
+// sums meet in LDS and are added in wave order.  nw: waves in the workgroup.
+__device__ __forceinline__ double wave_sum(double v) {
     v = v + dpp_f64<0xB1>(v);   // quad_perm [1,0,3,2]
     v = v + dpp_f64<0x4E>(v);   // quad_perm [2,3,0,1]
     v = v + dpp_f64<0x141>(v);  // row_half_mirror
     v = v + dpp_f64<0x140>(v);  // row_mirror
-    v = ((readlane_f64(v, 0) + readlane_f64(v, 16)) + readlane_f64(v, 32)) + readlane_f64(v, 48);
+    return ((readlane_f64(v, 0) + readlane_f64(v, 16)) + readlane_f64(v, 32)) + readlane_f64(v, 48);
+}
+
+__device__ __forceinline__ double block_sum(double v, double* slots, int nw) {
+    v = wave_sum(v);
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     if (lane == 0) slots[wave] = v;
@@ -684,11 +688,17 @@ __global__ __launch_bounds__(kSplitThreads) void finalize_slices_kernel(const Ro
 // [64c, 64c + 64) of token t, one wave per rank.  Wave r finalizes rank r's
 // slice (all of its top-k rows in one chunk of C >= k loads) and parks the
 // BF16-rounded partial in LDS; after the barrier wave 0 adds the R partials
-// in rank order and stores the FP32 sum -- bit for bit what the one-row
-// kernel holds before its epilogue, which row_kernel<EPI, kFinSum> then runs
-// from the workspace.  The R partials never reach HBM: the workspace holds
-// one FP32 row per token where a BF16 partial per rank would take R.
-template <bool EARLY_SHARED, int C>
+// in rank order -- bit for bit the sum the one-row kernel holds before its
+// epilogue.  The R partials never reach HBM.
+//  - Residual + RMSNorm: wave 0 also adds the residual (loaded before the
+//    finalize), stores residual_out, the FP32 row h to the workspace and
+//    its slice's sum of squares (per lane, then wave_sum: exactly the wave
+//    term the one-row kernel with one vector per lane forms for these 64
+//    vectors); norm_slices_kernel finishes the row.
+//  - Sandwich: wave 0 stores the FP32 sum s; row_kernel<kSandwich, kFinSum>
+//    runs the epilogue, one workgroup per token (its two row-wide sums need
+//    the whole row).
+template <int EPI, bool EARLY_SHARED, int C>
 __global__ __launch_bounds__(64 * FRN_MAX_R) void finalize_sum_slices_kernel(const RowArgs a,
                                                                              int S) {
     __shared__ uint4 part[FRN_MAX_R][64];
@@ -699,22 +709,79 @@ __global__ __launch_bounds__(64 * FRN_MAX_R) void finalize_sum_slices_kernel(con
     Lanes<1> L(a.nvec);
     L.vi[0] = c * 64 + lane;
     L.ok[0] = L.vi[0] < a.nvec;
+    const int64_t v = t * a.nvec + L.vi[0];
+    uint4 xr = make_uint4(0, 0, 0, 0);
+    if (EPI == kRmsNorm && r == 0 && L.ok[0]) xr = ld_stream(a.residual + v);
     float acc[1][8];
     finalize_rank<1, C, EARLY_SHARED>(a, r, t, L, acc);
     part[r][lane] = narrow(acc[0]);
     __syncthreads();
-    if (r != 0 || !L.ok[0]) return;
-    float sum[8];
-    widen(part[0][lane], sum);
+    if (r != 0) return;
+    float h[8];
+    widen(part[0][lane], h);
     for (int q = 1; q < a.R; ++q) {
         float f[8];
         widen(part[q][lane], f);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) sum[i] = sum[i] + f[i];
+        for (int i = 0; i < 8; ++i) h[i] = h[i] + f[i];
     }
-    float4* out = a.ws_sum + 2 * (t * a.nvec + L.vi[0]);
-    out[0] = make_float4(sum[0], sum[1], sum[2], sum[3]);
-    out[1] = make_float4(sum[4], sum[5], sum[6], sum[7]);
+    if constexpr (EPI == kRmsNorm) {
+        float x[8];
+        widen(xr, x);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) h[i] = h[i] + x[i];
+        double ss = 0.0;
+        if (L.ok[0]) {
+            st_stream(a.residual_out + v, narrow(h));
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const double d = (double)h[i];
+                ss = __fma_rn(d, d, ss);
+            }
+        }
+        ss = wave_sum(ss);
+        if (lane == 0) a.ws_ss[t * S + c] = ss;
+    }
+    if (!L.ok[0]) return;
+    float4* out = a.ws_sum + 2 * v;
+    out[0] = make_float4(h[0], h[1], h[2], h[3]);
+    out[1] = make_float4(h[4], h[5], h[6], h[7]);
+}
+
+// Split-row finalize, second kernel (residual + RMSNorm): workgroup (t, c)
+// adds token t's S slice sums of squares in slice order -- the one-row
+// kernel's wave order -- and normalizes its 64 vectors of h.  Lane q < S
+// loads slice q's sum, so all S arrive in one memory round trip, together
+// with the lane's h and gamma.
+__global__ __launch_bounds__(64) void norm_slices_kernel(const RowArgs a, int S) {
+    const int lane = threadIdx.x;
+    const int c = blockIdx.x % S;
+    const int64_t t = blockIdx.x / S;
+    const int vi = c * 64 + lane;
+    const bool ok = vi < a.nvec;
+    const int64_t v = t * a.nvec + vi;
+    float4 lo = make_float4(0.0f, 0.0f, 0.0f, 0.0f), hi = lo;
+    float g[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) g[i] = 0.0f;
+    if (ok) {
+        lo = a.ws_sum[2 * v];
+        hi = a.ws_sum[2 * v + 1];
+        load_gamma(a.gamma1, vi, g);
+    }
+    const double mine = lane < S ? a.ws_ss[t * S + lane] : 0.0;
+    double ss = readlane_f64(mine, 0);
+    for (int q = 1; q < S; ++q) ss += readlane_f64(mine, q);
+    const float rinv = inv_rms(ss, a.H, a.eps);
+    if (!ok) return;
+    const float h[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    float y[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float n = h[i] * rinv;
+        y[i] = n * g[i];
+    }
+    st_stream(a.out + v, narrow(y));
 }
 
 // Calls f(std::integral_constant<int, C>) with the top-k chunk for k slots:
@@ -995,15 +1062,16 @@ hipError_t launch_fin(const RowArgs& a, int64_t T, LaunchShape sh, hipStream_t s
     return launch_v<EPI, kFinTp>(a, T, sh, stream);
 }
 
-// Split-row finalize: finalize_sum_slices_kernel forms the FP32 rank sums in
-// the workspace (a workgroup per token and 64-vector slice, a wave per rank),
-// then row_kernel<EPI, kFinSum> runs the epilogue, one workgroup per token
-// (one vector per lane up to 1024 lanes, two above).  The caller keeps T at
-// or below kSplitCapT, so the first grid stays far below its limit.
+// Split-row finalize: finalize_sum_slices_kernel (a workgroup per token and
+// 64-vector slice, a wave per rank), then the epilogue: norm_slices_kernel
+// (residual + RMSNorm, a workgroup per token and slice) or row_kernel<EPI,
+// kFinSum> (sandwich, one workgroup per token; one vector per lane up to
+// 1024 lanes, two above).  The caller keeps T at or below kSplitCapT, so
+// the grids stay far below their limit.
 template <int EPI>
 hipError_t launch_split_rows(const RowArgs& a, int64_t T, hipStream_t stream) {
     if (T > kSplitCapT) return hipErrorInvalidValue;
-    const int S = (a.nvec + 63) / 64;
+    const int S = split_row_slices(a.nvec);
     const dim3 grid((unsigned)(T * S));
     const dim3 block((unsigned)(64 * a.R));
     // Under expert-parallel routing most ranks hold no shared row, and the
@@ -1011,19 +1079,24 @@ hipError_t launch_split_rows(const RowArgs& a, int64_t T, hipStream_t stream) {
     with_topk_chunk(a.k, [&](auto c) {
         constexpr int C = decltype(c)::value;
         if (a.ep)
-            hipLaunchKernelGGL((finalize_sum_slices_kernel<false, C>), grid, block, 0, stream, a,
-                               S);
+            hipLaunchKernelGGL((finalize_sum_slices_kernel<EPI, false, C>), grid, block, 0,
+                               stream, a, S);
         else
-            hipLaunchKernelGGL((finalize_sum_slices_kernel<true, C>), grid, block, 0, stream, a,
-                               S);
+            hipLaunchKernelGGL((finalize_sum_slices_kernel<EPI, true, C>), grid, block, 0,
+                               stream, a, S);
         return 0;
     });
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int vec = a.nvec > 1024 ? 2 : 1;
-    const int threads = ((a.nvec + vec - 1) / vec + 63) / 64 * 64;
-    if (vec == 1) return launch<EPI, kFinSum, 1, 1>(a, T, threads, stream);
-    return launch<EPI, kFinSum, 2, 1>(a, T, threads, stream);
+    if constexpr (EPI == kRmsNorm) {
+        hipLaunchKernelGGL(norm_slices_kernel, grid, dim3(64), 0, stream, a, S);
+        return hipGetLastError();
+    } else {
+        const int vec = a.nvec > 1024 ? 2 : 1;
+        const int threads = ((a.nvec + vec - 1) / vec + 63) / 64 * 64;
+        if (vec == 1) return launch<EPI, kFinSum, 1, 1>(a, T, threads, stream);
+        return launch<EPI, kFinSum, 2, 1>(a, T, threads, stream);
+    }
 }
 
 }  // namespace
