@@ -151,14 +151,14 @@ frn_status frn_moe_finalize_reduce_norm(const void* const* expert_rows,
  * serving loops, harnesses that forbid allocation.  Same arguments, results
  * and checks as frn_moe_finalize_reduce_norm, without workspace and
  * workspace_bytes: where that call would take the split-row finalize (see
- * frn_split_rows), this one writes its T x H FP32 rank sums to a scratch
- * array that the library holds in device memory, FRN_NOALLOC_SCRATCH_BYTES
- * per GPU, kept until the process ends; elsewhere it runs the one-row kernel
- * and uses no scratch.  It calls no allocation routine.  The array covers
- * the largest call any launch table can route to the split-row finalize
- * (T = 256 at H = 16384: T * H * 4 bytes); a larger need would return
- * FRN_ERR_UNSUPPORTED without launching, with both sizes in
- * frn_last_error().  The scratch needs no initialisation and its contents
+ * frn_split_rows), this one puts that call's workspace (see
+ * frn_workspace_bytes) in a scratch array that the library holds in device
+ * memory, FRN_NOALLOC_SCRATCH_BYTES per GPU, kept until the process ends;
+ * elsewhere it runs the one-row kernel and uses no scratch.  It calls no
+ * allocation routine.  The array covers the largest call any launch table
+ * can route to the split-row finalize (T = 256 at H = 16384: 16 MiB of FP32
+ * rows and 64 KiB of sums); a larger need would return FRN_ERR_UNSUPPORTED
+ * without launching, with both sizes in frn_last_error().  The scratch needs no initialisation and its contents
  * from the previous call are never read.  Every call on one GPU shares that GPU's
  * array: calls that may overlap in time on one GPU (different streams,
  * concurrent graph replays) race and give wrong results; serialise them.
@@ -323,8 +323,10 @@ frn_status frn_query(int32_t R, int32_t k, int64_t T, int64_t H, int32_t epilogu
  * is never split.  builtin: the calls the rule matches take the
  * hand-fitted rule for both questions, whatever later rules and the
  * compiled-in table say ("* * * * 0 * builtin" alone turns the measured
- * table off).  Results are identical for every choice; only speed
- * changes.  tp_reduction_rmsnorm_amd/tune.py measures a table.
+ * table off).  Only speed changes: the one FP64 sum of squares per row is
+ * added in an order that depends on the shape, and FP64 holds each FP32
+ * square exactly, so the FP32 mean it rounds to has not changed in any of
+ * the parity sweeps.  tp_reduction_rmsnorm_amd/tune.py measures a table.
  * frn_set_launch_table(NULL) removes the caller's table (the compiled-in
  * table and the hand-fitted rule then decide); an unparsable text returns
  * FRN_ERR_INVALID (the line is in frn_last_error) and leaves the table as
@@ -350,23 +352,29 @@ frn_status frn_launch_shape(int32_t R, int32_t k, int64_t T, int64_t H, int32_t 
  * up to max_T tokens (0: no call of these sizes uses one).  Only the MoE
  * finalize (k > 0) uses it, at small T: each (token, 512-column slice) then
  * runs in a workgroup of its own with one wave per rank, the R finalized
- * BF16 partials are summed in LDS, and the FP32 sum goes to the workspace;
- * a second kernel on the same stream reads it back and runs the epilogue.
- * This spreads a token's row over many workgroups at small batch, the
- * analogue of the pages' row spread over several blocks (SGLang PR #34134,
- * the publish-granularity discussion).  Which calls take it is
- * frn_split_rows; the size returned covers both routings and every
- * epilogue under the current launch table.  Results are bit-identical with
- * and without it (the same BF16 partials, summed in the same order, and the
- * FP32 sum stored exactly).  Layout: T x H FP32.  The caller allocates it
+ * BF16 partials are summed in LDS, and the FP32 sum goes to the workspace
+ * (residual + RMSNorm: the residual is added there too, residual_out
+ * written, and the slice's FP64 sum of squares kept); a second kernel on the
+ * same stream reads it back and runs the rest of the epilogue, per slice
+ * (residual + RMSNorm) or per token (sandwich).  This spreads a token's row
+ * over many workgroups at small batch, the analogue of the pages' row
+ * spread over several blocks (SGLang PR #34134, the publish-granularity
+ * discussion).  Which calls take it is frn_split_rows; the size returned
+ * covers both routings and every epilogue under the current launch table.
+ * Results are the same as without it: the same BF16 partials summed in the
+ * same order, the FP32 sums stored exactly, and the slice sums of squares
+ * added in slice order, which is the one-row kernel's order when it runs
+ * one vector per lane (other shapes add the same FP64 terms in another
+ * order, as launch shapes do; see frn_set_launch_table).  Layout: T x H
+ * FP32 rows, then T x ceil(H / 512) FP64 sums.  The caller allocates it
  * (256-byte aligned); it needs no initialisation and holds nothing between
  * calls.  Calls that share one workspace must not run concurrently.  A
  * workspace that is NULL, or given to a call that does not take the
  * split-row finalize, is ignored (the call then uses the
  * one-row-per-workgroup kernel).  A workspace given to a call that takes it
- * must cover that call (T * H * 4 bytes) and be 256-byte aligned, else the
- * call returns FRN_ERR_UNSUPPORTED without launching; it must not overlap
- * any other argument (FRN_ERR_INVALID).
+ * must cover that call (frn_workspace_bytes(T, ...)) and be 256-byte
+ * aligned, else the call returns FRN_ERR_UNSUPPORTED without launching; it
+ * must not overlap any other argument (FRN_ERR_INVALID).
  */
 size_t frn_workspace_bytes(int64_t max_T, int64_t H, int32_t R, int32_t k);
 
