@@ -155,3 +155,34 @@ def test_pipelined_loop_never_waits_for_everything(epi, vec, ranks):
     assert f.index("vmcnt(0)") < f.index("s_barrier")
     assert min(w for w in waits if w) >= 2 * vec, waits
 
+
+
+def _split_row_symbols(dis):
+    return sorted(set(re.findall(r"<(_ZN3frn12_GLOBAL__N_126finalize_sum_slices_kernel\w+)>:", dis)))
+
+
+def test_split_row_first_kernel_one_barrier_and_no_flat_rank_selection():
+    """finalize_sum_slices_kernel (every instance): one barrier, after which
+    wave 0 reads the R parked partials; the wave's rank is a scalar
+    (readfirstlane), so the per-rank kernel arguments are picked with
+    scalar loads, never with a per-lane index."""
+    dis = _disassembly()
+    syms = _split_row_symbols(dis)
+    assert len(syms) == 16, syms
+    for sym in syms:
+        f = _function(dis, sym)
+        assert f.count("s_barrier") == 1, sym
+        assert "v_readfirstlane_b32" in f, sym
+        assert "scratch_" not in f, sym
+
+
+def test_sliced_epilogue_loads_the_slice_sums_in_one_round_trip():
+    """norm_slices_kernel: the S slice sums of squares come in as one vector
+    load (lane q takes sum q), not as S dependent scalar loads, and the
+    kernel waits on the vector memory counter once before the rows' norm."""
+    f = _function(_disassembly(), "_ZN3frn12_GLOBAL__N_118norm_slices_kernelENS_7RowArgsEi")
+    assert len(re.findall(r"global_load_dwordx2 ", f)) == 1
+    assert len(re.findall(r"s_waitcnt vmcnt\(0\)", f)) == 1
+    loop = f[f.index("vmcnt(0)"):]
+    assert "v_readlane_b32" in loop
+    assert not re.search(r"s_load_dwordx2 s\[\d+:\d+\], s\[\d+:\d+\], 0x0\b", loop)
