@@ -15,8 +15,8 @@ Printed: ONE JSON line with the contract fields plus
   * ``roofline``: the fused kernel's achieved algorithmic GB/s (bytes per
     launch / average launch time from HIP events on the launch stream)
     against MI355X's 8 TB/s HBM peak, and the HBM traffic measured with
-    rocprofv3 counters when the stored counter summary matches the current
-    kernel source;
+    rocprofv3 counters when the stored counter summary was taken on the
+    current kernel machine code;
   * ``sweep``: µs/call and GB/s over T = 1..4096 at H=5120 (R=4) and H=8192
     (R=8), each the median of 5 replays of a HIP graph holding 20 calls (the
     measuring method of the pages' microbenchmark table, vLLM PR #62366);
@@ -39,8 +39,8 @@ message (the library runs on one GPU only).
 from __future__ import annotations
 
 import argparse
-import glob
 import hashlib
+import struct
 import json
 import os
 import re
@@ -203,20 +203,45 @@ def pattern_probe(dev, cid=2, Ts=(1024, 4096)):
     return rows
 
 
-def kernel_source_digest() -> str:
-    """SHA-256 over the kernel sources, the public header and the code
-    generation flags: counter data taken for another version of the kernels
-    is not reported."""
-    B = hip_build_module()
-    h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(B.CSRC, "*"))):
-        with open(f, "rb") as fh:
-            h.update(os.path.basename(f).encode())
-            h.update(fh.read())
-    with open(os.path.join(ROOT, "include", "fused_reduce_norm.h"), "rb") as fh:
-        h.update(fh.read())
-    h.update(" ".join(B.CODEGEN_FLAGS).encode())
-    return h.hexdigest()
+def _elf_sections(b: bytes) -> dict:
+    """{name: bytes} of the sections of a 64-bit little-endian ELF image."""
+    shoff, = struct.unpack_from("<Q", b, 0x28)
+    shentsize, shnum, shstrndx = struct.unpack_from("<HHH", b, 0x3A)
+    hdrs = [struct.unpack_from("<IIQQQQ", b, shoff + i * shentsize) for i in range(shnum)]
+    strtab = hdrs[shstrndx][4]
+    out = {}
+    for name, typ, _flags, _addr, off, size in hdrs:
+        n = b[strtab + name:b.index(b"\0", strtab + name)].decode()
+        out[n] = b"" if typ == 8 else b[off:off + size]  # SHT_NOBITS holds no bytes
+    return out
+
+
+def kernel_code_digest(lib: str = None) -> str:
+    """SHA-256 of the kernels' machine code: the gfx950 code object inside
+    the built library (its .hip_fatbin section, a clang offload bundle),
+    over the sections that hold the instructions, the kernel descriptors
+    and the kernel metadata (.text, .rodata, .note).  Symbol-name tables are
+    left out: they carry per-build identifiers.  Comments and documentation
+    do not change it; any change to the generated code does, so counter data
+    taken on other code is not reported."""
+    lib = lib or os.path.join(ROOT, "tp_reduction_rmsnorm_amd", "libfused_reduce_norm.so")
+    fat = _elf_sections(open(lib, "rb").read())[".hip_fatbin"]
+    if fat[:24] != b"__CLANG_OFFLOAD_BUNDLE__":
+        raise RuntimeError("unexpected .hip_fatbin layout")
+    n, = struct.unpack_from("<Q", fat, 24)
+    p = 32
+    for _ in range(n):
+        off, size, tlen = struct.unpack_from("<QQQ", fat, p)
+        triple = fat[p + 24:p + 24 + tlen].decode()
+        p += 24 + tlen
+        if triple.endswith("gfx950"):
+            secs = _elf_sections(fat[off:off + size])
+            h = hashlib.sha256()
+            for name in (".text", ".rodata", ".note"):
+                h.update(name.encode())
+                h.update(secs[name])
+            return h.hexdigest()
+    raise RuntimeError("no gfx950 code object in the library")
 
 
 def stored_traffic(workload: str, T: int, digest: str):
@@ -226,7 +251,7 @@ def stored_traffic(workload: str, T: int, digest: str):
     if not os.path.exists(path):
         return None
     text = open(path).read()
-    m = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    m = re.search(r"kernel_code_sha256:\s*([0-9a-f]{64})", text)
     f = re.search(r"fetch_bytes_per_launch:\s*([0-9.eE+]+)", text)
     w = re.search(r"write_bytes_per_launch:\s*([0-9.eE+]+)", text)
     if not (m and f and w) or m.group(1) != digest:
@@ -599,7 +624,7 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
 
-    digest = kernel_source_digest()
+    digest = kernel_code_digest()
     traffic = stored_traffic(run.w.name + ("_split" if args.split else ""), T, digest)
     out = {
         "metric": METRIC,
@@ -627,7 +652,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4),
                      "traffic": traffic, "kernel_us": round(ev_us, 3),
-                     "kernel_source_sha256": digest},
+                     "kernel_code_sha256": digest},
     }
     if not args.no_cpu and args.workload is None:
         out["cpu_baseline"] = cpu_baseline(run)

@@ -33,7 +33,7 @@ def test_algorithmic_bytes_of_the_headline_workload():
 def test_kernel_digest_is_stable_and_matches_stored_traffic_format():
     sys.path.insert(0, ROOT)
     import bench
-    d1, d2 = bench.kernel_source_digest(), bench.kernel_source_digest()
+    d1, d2 = bench.kernel_code_digest(), bench.kernel_code_digest()
     assert d1 == d2 and len(d1) == 64
-    # a stored summary for other sources must read as unknown traffic
+    # a stored summary for other machine code must read as unknown traffic
     assert bench.stored_traffic("sandwich_h5120_r4", 4096, "0" * 64) is None

@@ -350,7 +350,8 @@ FRN_API frn_status frn_moe_finalize_reduce_norm(
 // ------------------------------------------- the no-allocation entry point --- //
 
 // Scratch memory of frn_moe_finalize_reduce_norm_noalloc: the split-row
-// finalize's R x T x H BF16 partials, for callers that cannot allocate.
+// finalize's workspace (T x H FP32 rows, then the FP64 slice sums), for
+// callers that cannot allocate.
 // Each GPU the library runs on holds its own copy of this array until the
 // process ends.  Host code never uses the array's name as an address (on
 // the host it is a stand-in, not device memory): it uses the address that

@@ -1,8 +1,8 @@
 // frn_kernels.hip -- gfx950 kernels of the fused reduce + norm boundary.
 //
-// Four kernels (row_kernel, rows_pipelined_kernel,
-// finalize_sum_slices_kernel and finalize_slices_kernel, each in several
-// instantiations) share the per-row building blocks below.
+// Five kernels (row_kernel, rows_pipelined_kernel,
+// finalize_sum_slices_kernel, norm_slices_kernel and finalize_slices_kernel,
+// most in several instantiations) share the per-row building blocks below.
 //
 // row_kernel: one token row per workgroup.  Each lane owns V 16-byte vectors
 // of the row (8 BF16 values each), placed `threads` vectors apart so every
@@ -23,11 +23,12 @@
 // another.  Workgroup (t, c) takes a 64-vector slice of token t with one
 // wave per rank: each wave finalizes its rank's slice, the R BF16 partials
 // meet in LDS and are summed in rank order, and the FP32 sum goes to the
-// caller's workspace; row_kernel then reads it back and runs the epilogue.
-// The kernel boundary orders the two, so no workgroup waits for another and
-// no cross-XCD cache maintenance is issued inside a kernel (a device-scope
-// fence per workgroup writes back and invalidates the whole L2 of its XCD,
-// which measured far slower).
+// caller's workspace.  norm_slices_kernel (residual + RMSNorm, from the
+// slices' sums of squares) or row_kernel (sandwich) then reads it back and
+// finishes the epilogue.  The kernel boundary orders the two, so no
+// workgroup waits for another and no cross-XCD cache maintenance is issued
+// inside a kernel (a device-scope fence per workgroup writes back and
+// invalidates the whole L2 of its XCD, which measured far slower).
 //
 // finalize_slices_kernel: the standalone per-rank finalize.  Workgroup
 // (t, r, c) finalizes slice c of rank r of token t and stores the BF16
