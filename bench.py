@@ -77,6 +77,7 @@ def hip_build_module():
 
 
 PROBE_SRC = os.path.join(ROOT, "bench_probe.hip")
+PROBE_MAX_SRC = 24  # kMaxSrc of bench_probe.hip
 PROBE_LIB = os.path.join(ROOT, "bench_probe.so")
 
 
@@ -102,7 +103,9 @@ def pattern_probe(dev, cid=2, Ts=(1024, 4096)):
     the current row's stores) is timed as well.  Reduction workloads: on the call's own rotating
     buffers.  Expert-parallel workload: its k routed rows, the shared row and
     the residual of each token read as k + 2 contiguous [T,H] streams of
-    their own (the same bytes without the gather, indices or weights)."""
+    their own (the same bytes without the gather, indices or weights); TP
+    finalize workloads the same way, R (k + 1) + 1 streams (at most
+    PROBE_MAX_SRC)."""
     import ctypes
     import torch
     import tp_reduction_rmsnorm_amd as frn
@@ -123,17 +126,19 @@ def pattern_probe(dev, cid=2, Ts=(1024, 4096)):
         r = Runner(cid, T, dev, cold=True)
         w = r.w
         arrays, keep = [], []
-        if w.ep:
-            nsrc = w.k + 2
-            vec = frn.launch_shape(w.R, w.k, T, w.H, r.epi, ep=True)[1]
+        if w.ep or w.k:
+            # expert-parallel: k routed rows + the shared row + the residual;
+            # TP finalize: R (k + shared) rows + the residual
+            nsrc = w.k + 2 if w.ep else w.R * (w.k + (1 if w.shared else 0)) + 1
+            if nsrc > PROBE_MAX_SRC:
+                raise ValueError(f"the pattern probe reads at most {PROBE_MAX_SRC} rows per token")
+            vec = frn.launch_shape(w.R, w.k, T, w.H, r.epi, ep=w.ep)[1]
             for o, ro in r.outs:
                 bufs = [torch.empty(T, w.H, dtype=torch.bfloat16, device=dev) for _ in range(nsrc)]
                 keep.append(bufs)
                 arrays.append(((ctypes.c_void_p * nsrc)(*[b.data_ptr() for b in bufs]),
                                (ctypes.c_void_p * 2)(o.data_ptr(), ro.data_ptr())))
         else:
-            if w.k:
-                raise ValueError("the pattern probe covers reductions and the expert-parallel call")
             nsrc = w.R + 1
             vec = frn.launch_shape(w.R, 0, T, w.H, r.epi)[1]
             for d, (o, ro) in zip(r.sets, r.outs):
@@ -163,7 +168,7 @@ def pattern_probe(dev, cid=2, Ts=(1024, 4096)):
             if st != 0:
                 raise RuntimeError(f"probe_rows_pipelined failed ({st})")
 
-        pipelined = not w.ep and frn.launch_pipelined(w.R, 0, T, w.H, r.epi)
+        pipelined = not w.k and frn.launch_pipelined(w.R, 0, T, w.H, r.epi)
         kernel_us = r.graph_us()
         call = r.call
         r.call = probe
