@@ -7,7 +7,8 @@ test asserts that the kernels
 * never write through the scalar data cache (no scalar stores, scalar
   atomics or scalar-cache write-back): every store is a vector store;
 * contain no packed FP32 arithmetic (the build disables it);
-* never spill to scratch memory;
+* never spill to scratch memory, and keep the register budgets their launch
+  shapes were measured at;
 * narrow FP32 to BF16 with the hardware round-to-nearest-even conversion.
 """
 import os
@@ -24,21 +25,43 @@ LLVM = "/opt/rocm/llvm/bin"
 _DIS = {}
 
 
+def _code_object(d):
+    """Write the library's gfx950 code object into directory d; its path."""
+    if not os.path.exists(LIB):
+        import __graft_entry__
+        __graft_entry__.hip_build_module().build()
+    fatbin, co = os.path.join(d, "fatbin.bin"), os.path.join(d, "gfx950.co")
+    subprocess.run([f"{LLVM}/llvm-objcopy", f"--dump-section=.hip_fatbin={fatbin}", LIB,
+                    os.path.join(d, "copy.so")], check=True)
+    subprocess.run([f"{LLVM}/clang-offload-bundler", "--unbundle", "--type=o",
+                    f"--input={fatbin}", "--targets=hipv4-amdgcn-amd-amdhsa--gfx950",
+                    f"--output={co}"], check=True)
+    return co
+
+
+def _vgpr_counts():
+    """{kernel symbol: VGPRs per lane} from the code object's metadata (cached)."""
+    if "vgprs" in _DIS:
+        return _DIS["vgprs"]
+    import tempfile
+    with tempfile.TemporaryDirectory() as d:
+        notes = subprocess.run([f"{LLVM}/llvm-readelf", "--notes", _code_object(d)],
+                               capture_output=True, text=True, check=True).stdout
+    out = {}
+    for block in notes.split("- .agpr_count")[1:]:
+        name = re.search(r"\.name:\s+(\S+)", block).group(1)
+        out[name] = int(re.search(r"\.vgpr_count:\s+(\d+)", block).group(1))
+    _DIS["vgprs"] = out
+    return out
+
+
 def _disassembly():
     """llvm-objdump of the library's gfx950 code object (cached)."""
     if "text" in _DIS:
         return _DIS["text"]
-    if not os.path.exists(LIB):
-        import __graft_entry__
-        __graft_entry__.hip_build_module().build()
     import tempfile
     with tempfile.TemporaryDirectory() as d:
-        fatbin, co = os.path.join(d, "fatbin.bin"), os.path.join(d, "gfx950.co")
-        subprocess.run([f"{LLVM}/llvm-objcopy", f"--dump-section=.hip_fatbin={fatbin}", LIB,
-                        os.path.join(d, "copy.so")], check=True)
-        subprocess.run([f"{LLVM}/clang-offload-bundler", "--unbundle", "--type=o",
-                        f"--input={fatbin}", "--targets=hipv4-amdgcn-amd-amdhsa--gfx950",
-                        f"--output={co}"], check=True)
+        co = _code_object(d)
         _DIS["text"] = subprocess.run([f"{LLVM}/llvm-objdump", "-d", "--mcpu=gfx950", co],
                                       capture_output=True, text=True, check=True).stdout
     return _DIS["text"]
@@ -186,3 +209,27 @@ def test_sliced_epilogue_loads_the_slice_sums_in_one_round_trip():
     loop = f[f.index("vmcnt(0)"):]
     assert "v_readlane_b32" in loop
     assert not re.search(r"s_load_dwordx2 s\[\d+:\d+\], s\[\d+:\d+\], 0x0\b", loop)
+
+
+# Register budgets the launch shapes were measured at: a SIMD holds
+# floor(512 / VGPRs) waves (VGPRs allocated in steps of 8), and a CU four
+# SIMDs.  (kernel symbol pattern, most VGPRs, why)
+OCCUPANCY = [
+    (r"row_kernelILi[01]ELi2ELi1ELi5E", 64,
+     "expert-parallel work list: 8 waves per SIMD (two 768-lane or four 512-lane tokens per CU)"),
+    (r"row_kernelILi[01]ELi1ELi1ELi8E", 72,
+     "TP finalize, k <= 8: 7 waves per SIMD (two 896-lane tokens per CU at H=7168)"),
+    (r"finalize_sum_slices_kernelILi[01]ELb1ELi12E", 80,
+     "split-row finalize, k <= 12: 6 waves per SIMD (three 8-wave workgroups per CU at R=8)"),
+    (r"rows_pipelined_kernelILi1ELi2ELi4E", 128,
+     "headline kernel: one 320-lane workgroup per CU needs 2 waves per SIMD"),
+    (r"norm_slices_kernel", 64, "sliced epilogue: one wave per workgroup, 8 per SIMD"),
+]
+
+
+@pytest.mark.parametrize("pattern,limit,why", OCCUPANCY, ids=[o[0] for o in OCCUPANCY])
+def test_measured_kernels_keep_their_register_budget(pattern, limit, why):
+    hits = {k: v for k, v in _vgpr_counts().items() if re.search(pattern, k)}
+    assert hits, f"no kernel matches {pattern}"
+    over = {k: v for k, v in hits.items() if v > limit}
+    assert not over, f"{why}: {over} exceed {limit} VGPRs"
