@@ -23,7 +23,7 @@ Printed: ONE JSON line with the contract fields plus
   * ``other_configs``: the other workloads at their gated sizes -- the tiny
     call at T=8, the MoE finalize at T=1, 8 and 64, the large-batch MoE call
     fused against the split path at T=4096, the expert-parallel finalize at
-    T=4096 -- and eager (not graph-captured) µs per call at T=1 and 8;
+    T=8, 64, 1024 and 4096 -- and eager (not graph-captured) µs per call at T=1 and 8;
   * ``cpu_baseline``: the CPU oracle timed on every core of the host's
     affinity mask (and on one) on a bounded sample of the same workload,
     with the largest BF16 ulp distance between its rows and the GPU's timed
@@ -374,7 +374,8 @@ def sweep(dev, cids=(2, 3), Ts=SWEEP_T):
 
 def extra_configs(dev, full=False):
     """The other workloads at their gated sizes: the tiny call at T=8, the
-    MoE finalize at T=1, 8, 64, the expert-parallel finalize at T=4096, and
+    MoE finalize at T=1, 8, 64, the expert-parallel finalize at T=8, 64,
+    1024 and 4096, and
     the large-batch MoE call fused against the split path at T=4096
     (``full``: more T, and the MoE finalize fused against the standalone
     finalize followed by the plain reduction).  Where two paths compute the
@@ -401,7 +402,7 @@ def extra_configs(dev, full=False):
     if full:
         singles = ((1, (8,)), (4, (2, 4, 16, 32)), (6, (1, 8, 64, 1024, 4096)))
     else:
-        singles = ((1, (8,)), (4, (1, 8, 64)), (6, (4096,)))
+        singles = ((1, (8,)), (4, (1, 8, 64)), (6, (8, 64, 1024, 4096)))
     for cid, Ts in singles:
         for T in Ts:
             r = Runner(cid, T, dev, cold=T >= 256)
