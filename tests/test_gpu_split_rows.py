@@ -107,3 +107,35 @@ def test_split_rows_ep(case, split_everywhere):
     parity.compare(f"split-row EP {case} residual_out", workloads.bits(x), ref.xout)
     _same("split-row EP out vs one-row kernel", y, yf)
     _same("split-row EP residual_out vs one-row kernel", x, xf)
+
+
+@pytest.mark.parametrize("epi", ["rmsnorm", "sandwich"])
+def test_split_rows_out_of_range_and_non_finite(epi, split_everywhere):
+    """Through the split-row finalize: an index past the expert buffer (or
+    negative, under TP routing) reads as a NaN row without a fault, and inf
+    or NaN in expert and shared rows propagate as IEEE arithmetic dictates;
+    the oracle and the one-row kernel agree element for element (NaN
+    positions included)."""
+    m = split_everywhere
+    R, T, H, k = 3, 6, 1024, 3
+    assert m.split_rows(R, k, T, H)
+    log(f"split-row non-finite {epi}")
+    inp = workloads.make(R, T, H, k=k, shared=True, epilogue=epi, seed=3500)
+    nr = inp.expert_rows[0].shape[0]
+    inf, nan = torch.tensor(float("inf")), torch.tensor(float("nan"))
+    inp.topk_idx[2, 1] = nr                                       # row 2: past the buffer
+    inp.topk_idx[4, 0] = -5                                       # row 4: negative
+    inp.expert_rows[1][int(inp.topk_idx[1, 2]), 17] = inf.to(torch.bfloat16)  # row 1: inf
+    inp.shared[2][3, 40] = nan.to(torch.bfloat16)                 # row 3: NaN shared
+    inp.expert_rows[0][int(inp.topk_idx[5, 0]), 3] = inf.to(torch.bfloat16)   # row 5: inf - inf
+    inp.expert_rows[1][int(inp.topk_idx[5, 0]), 3] = (-inf).to(torch.bfloat16)
+    d = to_dev(inp)
+    y, x = gpu_fused(d, workspace="auto")
+    yf, xf = gpu_fused(d, workspace=None)
+    ref = oracle_ref(inp)
+    torch.cuda.synchronize()
+    parity.compare(f"split-row non-finite {epi} out", workloads.bits(y), ref.y)
+    parity.compare(f"split-row non-finite {epi} residual_out", workloads.bits(x), ref.xout)
+    _same("split-row non-finite out vs one-row kernel", y, yf)
+    _same("split-row non-finite residual_out vs one-row kernel", x, xf)
+    assert torch.isnan(y[2].float()).all() and torch.isnan(y[4].float()).all()
