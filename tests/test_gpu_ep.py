@@ -229,7 +229,7 @@ def _sub_ep(d, rows):
     return sub
 
 
-@pytest.mark.parametrize("T", [64, 4096])
+@pytest.mark.parametrize("T", [64, 1024, 4096, 16384])
 def test_ep_full_size_sampled_rows(T):
     log(f"ep full size T={T}")
     d = workloads.make_workload(6, T, device=DEV)
