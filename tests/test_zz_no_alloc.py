@@ -6,8 +6,9 @@ Two calls in a row, the second with a smaller input, both taking the
 split-row finalize (so both use the array, and the second runs on what the
 first left there): each output equals, bit for bit, that of the workspace
 entry point frn_moe_finalize_reduce_norm on the same inputs, and both equal
-the oracle.  A call above the split-row range (no scratch used) and the
-largest split-row call at the largest H (R=16, H=16384) are checked too.
+the oracle.  A call above the split-row range (no scratch used), the
+largest split-row call at the largest H (R=16, H=16384), and the call
+captured in a HIP graph and replayed with new data are checked too.
 """
 import pytest
 import torch
@@ -99,3 +100,50 @@ def test_noalloc_without_split_rows_and_at_the_largest_h():
     ref = oracle_ref(inp)
     parity.compare("noalloc R=16 H=16384 out vs oracle", workloads.bits(y), ref.y)
     parity.compare("noalloc R=16 H=16384 residual_out vs oracle", workloads.bits(x), ref.xout)
+
+
+def test_noalloc_under_graph_capture():
+    """The callers this entry point is for: a HIP graph captures it (after
+    one eager call on the device, which looks up the array's address) and is
+    replayed four times with new data copied into the captured inputs and
+    eager work between the replays; every replay matches the oracle, and
+    the workspace entry point bit for bit."""
+    m = frn()
+    R, T, H, k = 8, 16, 6144, 10
+    assert m.split_rows(R, k, T, H)
+    base = to_dev(workloads.make(R, T, H, k=k, shared=True, seed=1200))
+    out = torch.empty(T, H, dtype=torch.bfloat16, device=DEV)
+    rout = torch.empty(T, H, dtype=torch.bfloat16, device=DEV)
+
+    def call():
+        m.moe_finalize_reduce_norm_noalloc(base.expert_rows, base.topk_w, base.topk_idx,
+                                           base.residual, base.gamma1, None, base.eps,
+                                           out=out, residual_out=rout, shared=base.shared)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    log("noalloc graph capture")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for rep in range(4):
+        new = workloads.make(R, T, H, k=k, shared=True, seed=1300 + rep)
+        for dst, src in zip(base.expert_rows + base.shared, new.expert_rows + new.shared):
+            dst.copy_(src.to(DEV))
+        base.topk_w.copy_(new.topk_w.to(DEV))
+        base.topk_idx.copy_(new.topk_idx.to(DEV))
+        base.residual.copy_(new.residual.to(DEV))
+        base.gamma1.copy_(new.gamma1.to(DEV))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref = oracle_ref(new)
+        parity.compare(f"noalloc graph replay {rep} out", workloads.bits(out), ref.y)
+        parity.compare(f"noalloc graph replay {rep} residual_out", workloads.bits(rout),
+                       ref.xout)
+        yw, xw = _with_workspace(to_dev(new))
+        _same(f"noalloc graph replay {rep} out vs workspace call", out, yw)
+        _same(f"noalloc graph replay {rep} residual_out vs workspace call", rout, xw)
