@@ -387,7 +387,7 @@ size_t frn_workspace_bytes(int64_t max_T, int64_t H, int32_t R, int32_t k);
  * re-reads one FP32 row per token and adds a second launch, so it pays only
  * while the one-row kernel is bound by its memory round trips.  The
  * compiled-in measured table decides the shapes it covers; the hand-fitted
- * rule, measured on MI355X, takes it up to 8 to 224 tokens depending on R,
+ * rule, measured on MI355X, takes it up to 32 to 256 tokens depending on R,
  * H, k and the routing (never at R = 1 under TP routing); a caller's split /
  * fused rules override both (see frn_set_launch_table).
  */

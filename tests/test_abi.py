@@ -363,14 +363,14 @@ def test_workspace_bytes(lib):
         assert lib.frn_workspace_bytes(8, 6144, 8, 10) == split_ws(8, 6144)   # FP32 sums
         # covers the largest T either routing splits at: R=8 H=6144 -> 128 (TP)
         assert lib.frn_workspace_bytes(5000, 6144, 8, 10) == split_ws(128, 6144)
-        assert lib.frn_workspace_bytes(5000, 4096, 2, 4) == split_ws(8, 4096)   # EP only
+        assert lib.frn_workspace_bytes(5000, 4096, 2, 4) == split_ws(64, 4096)   # EP only
         assert lib.frn_workspace_bytes(64, 5120, 4, 0) == 0      # no finalize: none used
         assert lib.frn_workspace_bytes(64, 5124, 4, 2) == 0      # unsupported H
         assert lib.frn_workspace_bytes(0, 5120, 4, 2) == 0
         assert lib.frn_workspace_bytes(8, 5120, 4, 17) == 0      # k beyond FRN_MAX_K
         # the size covers the compiled-in table's split rules too
         assert lib.frn_workspace_bytes(5000, 7168, 2, 8) == split_ws(max(
-            [48] + [int(r[5]) for r in tuned_rules()
+            [64] + [int(r[5]) for r in tuned_rules()
                     if r[:3] == ["7168", "2", "8"] and r[6] == "split"]), 7168)
     finally:
         lib.frn_set_launch_table(None)
@@ -386,24 +386,26 @@ def test_split_rows_builtin_rule():
         (8, 10, 6144, False, 1, True), (8, 10, 6144, False, 128, True),
         (8, 10, 6144, False, 129, False), (8, 10, 6144, False, 256, False),
         (1, 8, 7168, False, 1, False),
-        (2, 8, 7168, False, 48, True), (2, 8, 7168, False, 49, False),
-        (2, 16, 5120, False, 64, True), (2, 16, 5120, False, 65, False),
-        (2, 4, 4096, False, 1, False), (4, 8, 2048, False, 224, True),
-        (4, 8, 2048, False, 225, False), (16, 8, 4096, False, 192, True),
-        (16, 8, 4096, False, 193, False), (3, 8, 7168, False, 64, True),
-        (3, 8, 7168, False, 65, False), (4, 8, 5120, False, 96, True),
-        (4, 8, 5120, False, 97, False),
+        (2, 8, 7168, False, 64, True), (2, 8, 7168, False, 65, False),
+        (2, 16, 5120, False, 96, True), (2, 16, 5120, False, 97, False),
+        (2, 4, 4096, False, 1, False), (4, 8, 2048, False, 256, True),
+        (4, 8, 2048, False, 257, False), (16, 8, 4096, False, 192, True),
+        (16, 8, 4096, False, 193, False), (3, 8, 7168, False, 96, True),
+        (3, 8, 7168, False, 97, False), (4, 8, 5120, False, 128, True),
+        (4, 8, 5120, False, 129, False), (4, 8, 8192, False, 96, True),
+        (4, 8, 8192, False, 97, False), (8, 2, 6144, False, 192, True),
+        (8, 2, 6144, False, 193, False),
         (8, 10, 6144, EP, 64, True), (8, 10, 6144, EP, 65, False),
-        (8, 4, 6144, EP, 16, True), (8, 4, 6144, EP, 17, False),
-        (2, 10, 6144, EP, 8, True), (2, 10, 6144, EP, 9, False),
-        (4, 8, 7168, EP, 32, True), (4, 8, 7168, EP, 33, False),
-        (16, 8, 4096, EP, 96, True), (16, 8, 4096, EP, 97, False),
-        (16, 8, 7168, EP, 64, True), (16, 8, 7168, EP, 65, False),
-        (8, 8, 2048, EP, 160, True), (8, 8, 2048, EP, 161, False),
+        (8, 4, 6144, EP, 32, True), (8, 4, 6144, EP, 33, False),
+        (2, 10, 6144, EP, 64, True), (2, 10, 6144, EP, 65, False),
+        (4, 8, 7168, EP, 64, True), (4, 8, 7168, EP, 65, False),
+        (16, 8, 4096, EP, 128, True), (16, 8, 4096, EP, 129, False),
+        (16, 8, 7168, EP, 96, True), (16, 8, 7168, EP, 97, False),
+        (8, 8, 2048, EP, 256, True), (8, 8, 2048, EP, 257, False),
         (16, 8, 7168, False, 128, True), (16, 8, 7168, False, 129, False),
         (8, 6, 3072, False, 224, True), (8, 6, 3072, False, 225, False),
         (8, 10, 5120, False, 128, True), (8, 10, 5120, False, 129, False),
-        (16, 6, 3072, EP, 96, True), (16, 6, 3072, EP, 97, False),
+        (16, 6, 3072, EP, 128, True), (16, 6, 3072, EP, 129, False),
     ]
     try:
         for R, k, H, ep, T, want in cases:

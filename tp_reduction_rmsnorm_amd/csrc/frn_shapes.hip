@@ -294,43 +294,49 @@ int builtin_pipe_vec(int nvec, int fin, int64_t T, int epilogue, int R) {
 // grows with T from a lower start.
 // Largest T at which the split-row finalize still won (25 shapes, T = 1, 8,
 // 16, 32, 48, 64, 96, 128, 160, 192, 224, 256):
-//  - TP routing, R = 1: none (H=7168 k=8: 6.4 against 6.3 us at T=1);
-//  - TP routing, R = 2: 48 at H*k >= 32768 (H=7168 k=8: 9.4 against 9.7 us
-//    at T=48, 10.5 against 9.8 at T=64), 64 at H*k >= 65536 (H=5120 k=16:
-//    11.0 against 12.4 us at T=64, 12.7 each at T=96); none below (H=4096
-//    k=4: 5.5 against 5.3 us at T=1; H=2048 k=8 within 5% either way);
-//  - TP routing, 3 <= R: 224 at H <= 3072 (H=3072 R=8 k=8: 23.0 against
-//    24.0 us at T=224; H=2048 R=4 12.8 against 12.6 at T=256), 192 at
-//    H <= 4096 (H=4096 R=8 k=8: 24.6 against 24.9 us at T=192, 28.0 against
-//    26.2 at T=224; H=4096 R=16 the same); above, 128 at R >= 5 (H=6144
-//    R=8 k=10: 28.9 against 30.5 us at T=128, 35.6 against 32.2 at T=160;
-//    the same at k=2 and 4, H=7168 R=8 and R=16, H=16384 R=8) and 96 at
-//    R <= 4 (H=5120 R=4 k=8: 12.6 against 13.9 us at T=96, 14.6 against
-//    14.3 at T=128; H=8192 R=4 the same), R=3 taken as 64;
+//  - TP routing, R = 1: none (H=7168 k=8: 6.2 us either way at T=1);
+//  - TP routing, R = 2: 64 at H*k >= 32768 (H=7168 k=8: 8.9 against 9.9 us
+//    at T=64, 10.3 against 10.2 at T=96), 96 at H*k >= 65536 (H=5120 k=16:
+//    11.5 against 12.7 us at T=96, 13.2 against 13.1 at T=128); none below
+//    (H=4096 k=4: 5.6 against 5.4 us at T=1; H=2048 k=8 within 5% either
+//    way);
+//  - TP routing, 3 <= R: 256 at H <= 2048 (R=4 k=8: 11.7 against 12.6 us at
+//    T=256), 224 at H <= 3072 (R=8 k=8: 22.7 against 24.0 us at T=224, 24.7
+//    against 24.6 at T=256), 192 at H <= 4096 (R=8 k=8: 24.5 against 24.9 us
+//    at T=192, 27.4 against 26.2 at T=224; R=16 the same); above, 128 at
+//    R >= 5 (H=6144 R=8 k=10: 28.3 against 30.2 us at T=128, 34.8 against
+//    32.3 at T=160; k=4, H=7168 R=8 and R=16 the same, H=16384 R=8 a tie at
+//    128) and 192 for k <= 2 (H=6144 R=8 k=2: 16.4 against 16.8 us at T=192,
+//    18.3 against 17.4 at T=224); at R = 4, 128 up to H=6144 (H=5120 k=8:
+//    13.2 against 14.4 us at T=128, 15.7 against 14.8 at T=160) and 96 above
+//    (H=8192 k=8: 15.1 against 17.0 at T=96, 19.0 against 17.8 at T=128);
+//    R = 3 taken as 96;
 //  - expert-parallel routing, where the one-row kernel already keeps
 //    several ranks' rows in flight and the split kernel's waves of ranks
-//    without a live slot idle: 8 at R <= 2 (H=6144 k=8: 7.2 against 7.4 us
-//    at T=8, 7.7 each at T=16); 16 at k <= 4 (H=6144 R=8 k=4: 7.1 against
-//    7.3 at T=16, 8.2 against 7.3 at T=32); 160 at H <= 2048 (R=8 k=8: 8.8
-//    against 9.1 us at T=160); 96 at R >= 16 and H <= 4096 (H=4096 k=8: 12.2
-//    against 13.8 us at T=96, 14.2 against 13.9 at T=128; H=3072 k=6 10.8
-//    against 11.0), 64 above; else 32 at R <= 4 (H=7168 R=4 k=8: 8.8
-//    against 9.1 us at T=32, 9.2 each at T=48) and 64 (H=6144 R=8 k=10:
-//    10.1 against 11.0 us at T=64, 13.3 against 11.1 at T=96).
+//    without a live slot idle: 64 at R <= 2 (H=6144 k=8: 7.6 against 7.8 us
+//    at T=64, 8.4 against 7.9 at T=96); 32 at k <= 4 (H=6144 R=8 k=4: 6.9
+//    against 7.5 at T=32, 7.5 each at T=48); 256 at H <= 2048 (R=8 k=8: 8.8
+//    against 9.5 us at T=256); at R >= 16, 128 at H <= 4096 (H=4096 k=8:
+//    12.7 against 13.9 us at T=128, 14.5 against 14.1 at T=160; H=3072 k=6
+//    10.3 against 11.2) and 96 above; else 64 (H=6144 R=8 k=10: 8.7 against
+//    11.1 us at T=64, 11.9 against 11.1 at T=96; H=7168 R=4 k=8: 8.0
+//    against 9.2 at T=64, 9.2 each at T=96).
 int64_t builtin_split_max_t(int32_t R, int64_t H, int32_t k, bool ep) {
     if (ep) {
-        if (R <= 2) return 8;
-        if (k <= 4) return 16;
-        if (H <= 2048) return 160;
-        if (R >= 16) return H <= 4096 ? 96 : 64;
-        return R <= 4 ? 32 : 64;
+        if (R <= 2) return 64;
+        if (k <= 4) return 32;
+        if (H <= 2048) return 256;
+        if (R >= 16) return H <= 4096 ? 128 : 96;
+        return 64;
     }
     if (R == 1) return 0;
-    if (R == 2) return H * k >= 65536 ? 64 : H * k >= 32768 ? 48 : 0;
+    if (R == 2) return H * k >= 65536 ? 96 : H * k >= 32768 ? 64 : 0;
+    if (H <= 2048) return 256;
     if (H <= 3072) return 224;
     if (H <= 4096) return 192;
-    if (R == 3) return 64;
-    return R <= 4 ? 96 : 128;
+    if (R == 3) return 96;
+    if (R == 4) return H <= 6144 ? 128 : 96;
+    return k <= 2 ? 192 : 128;
 }
 
 bool matches(const Rule& r, int64_t H, int64_t R, int64_t k, int64_t epilogue, int64_t ep) {
