@@ -910,7 +910,9 @@ def test_caller_table_and_builtin_rule_override_the_compiled_in_table():
     import tp_reduction_rmsnorm_amd as frn
     S = frn.EPI_SANDWICH
     rules = tuned_rules()
-    assert ["5120", "4", "0", "sandwich", "2049", "*", "p2"] in rules
+    # the measured table sends the headline call (T=4096) to the row-pipelined kernel
+    assert any(r[:4] == ["5120", "4", "0", "sandwich"] and int(r[4]) <= 4096 and
+               (r[5] == "*" or int(r[5]) >= 4096) and r[6] in ("p1", "p2") for r in rules)
     try:
         frn.set_launch_table(None)
         assert frn.launch_pipelined(4, 0, 4096, 5120, S)

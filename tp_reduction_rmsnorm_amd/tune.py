@@ -12,7 +12,12 @@ through ``set_launch_table`` -- the one-row kernel with 1, 2 or 4 vectors
 per lane, and for calls without finalize the row-pipelined kernel with 1 or
 2 (``p1``, ``p2``) -- and timed the way the pages time this
 operation (vLLM PR #62366, kernel microbenchmark table): a HIP graph holding
-``--calls`` calls, median of 5 replays after at least 100 ms of replays.  Inputs rotate over up to 64 sets,
+``--calls`` calls, median of 5 replays after at least 100 ms of replays.
+Each choice is timed twice, the choices in order and then in reverse
+order, and the two medians are averaged, so that a drift over the run
+favours none of them.  The hand-fitted rule's own choice is kept wherever
+it is within 1% of the fastest (``TIE``), so that near-equal choices do not
+flip the table from run to run.  Inputs rotate over up to 64 sets,
 at least 1 GiB where that many sets reach it, so large calls are not served
 from the Infinity Cache.  The fastest choice per T becomes a rule covering
 the T range up to it; neighbouring ranges with the same choice merge.  Load
@@ -168,20 +173,62 @@ def fits(H, R, k, epi, T, choice):
             pipelined == choice.startswith("p"))
 
 
+# A measured winner replaces the hand-fitted rule's choice only where it is
+# faster by more than this: between near-equal choices the timing order of
+# a run, not the kernels, would decide, and the table would change from run
+# to run.
+TIE = 0.01
+
+
+def builtin_choice(H, R, k, epi, T):
+    """The rule value the hand-fitted rule gives a call ('1', '2', '4', 'p1',
+    'p2')."""
+    ep = epi.startswith("ep-")
+    frn.set_launch_table("* * * * 0 * builtin\n")
+    try:
+        vec = frn.launch_shape(R, k, T, H, EPI[epi], ep=ep)[1]
+        pipe = not ep and frn.launch_pipelined(R, k, T, H, EPI[epi])
+    finally:
+        frn.set_launch_table(None)
+    return ("p" if pipe else "") + str(vec)
+
+
+def builtin_split(H, R, k, epi, T):
+    """'split' or 'fused': the hand-fitted rule's choice for a finalize call."""
+    frn.set_launch_table("* * * * 0 * builtin\n")
+    try:
+        return "split" if frn.split_rows(R, k, T, H, EPI[epi], ep=epi.startswith("ep-")) else "fused"
+    finally:
+        frn.set_launch_table(None)
+
+
+def pick(times, default):
+    """The fastest choice, unless `default` is within TIE of it."""
+    best = min(times, key=times.get)
+    if default in times and times[default] <= times[best] * (1 + TIE):
+        return default
+    return best
+
+
 def tune_shape(H, R, k, epi, tokens, calls, dev, log=print):
     """[(T, best_choice, {choice: us})] for one shape; a choice is a rule
     value: '1', '2', '4' (one-row kernel) or 'p1', 'p2' (row-pipelined)."""
     rows = []
     for T in tokens:
         call = Call(H, R, k, epi, T, dev)
-        times = {}
+        choices = []
         for vec in ("1", "2", "4", "p1", "p2"):
             frn.set_launch_table(f"{H} {R} {k} {epi} {T} {T} {vec}")
-            if not fits(H, R, k, epi, T, vec):
-                continue  # does not fit this call
-            times[vec] = graph_us(call, calls)
+            if fits(H, R, k, epi, T, vec):  # else the rule is skipped for this call
+                choices.append(vec)
+        # every choice timed twice, in order and then in reverse order, so
+        # that a drift over the run favours none of them
+        times = {vec: 0.0 for vec in choices}
+        for vec in choices + choices[::-1]:
+            frn.set_launch_table(f"{H} {R} {k} {epi} {T} {T} {vec}")
+            times[vec] += graph_us(call, calls) / 2
         frn.set_launch_table(None)
-        best = min(times, key=times.get)
+        best = pick(times, builtin_choice(H, R, k, epi, T))
         rows.append((T, best, times))
         log(f"H={H} R={R} k={k} {epi} T={T}: " +
             ", ".join(f"vec {v}: {us:.2f} us" for v, us in sorted(times.items())) + f" -> {best}")
@@ -197,16 +244,18 @@ def tune_split(H, R, k, epi, tokens, calls, dev, log=print):
     rows = []
     for T in tokens:
         call = Call(H, R, k, epi, T, dev)
-        times = {}
-        try:
-            frn.set_launch_table(f"{H} {R} {k} {epi} {T} {T} split")
-            call.workspace = "auto"
-            times["split"] = graph_us(call, calls)
-        finally:
-            frn.set_launch_table(None)
-        call.workspace = None
-        times["fused"] = graph_us(call, calls)
-        best = min(times, key=times.get)
+        times = {"split": 0.0, "fused": 0.0}
+        for choice in ("split", "fused", "fused", "split"):  # A, B, B, A
+            try:
+                if choice == "split":
+                    frn.set_launch_table(f"{H} {R} {k} {epi} {T} {T} split")
+                    call.workspace = "auto"
+                else:
+                    call.workspace = None
+                times[choice] += graph_us(call, calls) / 2
+            finally:
+                frn.set_launch_table(None)
+        best = pick(times, builtin_split(H, R, k, epi, T))
         rows.append((T, best, times))
         log(f"H={H} R={R} k={k} {epi} T={T}: split {times['split']:.2f} us, "
             f"fused {times['fused']:.2f} us -> {best}")
@@ -264,7 +313,9 @@ def main():
     lines = ["# fused_reduce_norm launch table: H R k epilogue Tmin Tmax vec",
              f"# measured on a {props.gcnArchName.split(':')[0]} GPU with {props.multi_processor_count} CUs"
              f" with: python tp_reduction_rmsnorm_amd/tune.py {' '.join(sys.argv[1:])}",
-             f"# graph replay of {args.calls} calls, median of 5 after 100 ms of replays."]
+             f"# graph replay of {args.calls} calls, median of 5 after 100 ms of replays;"
+             " each choice timed twice (in order, then in reverse order), the two averaged;"
+             " the hand-fitted choice kept where within 1% of the fastest."]
     for H, R, k, epi in shapes:
         rows = tune_shape(H, R, k, epi, sorted(set(args.tokens)), args.calls, dev)
         lines += rules_for(H, R, k, epi, rows)
