@@ -211,6 +211,38 @@ def test_sliced_epilogue_loads_the_slice_sums_in_one_round_trip():
     assert not re.search(r"s_load_dwordx2 s\[\d+:\d+\], s\[\d+:\d+\], 0x0\b", loop)
 
 
+def _row_kernel_symbols(dis):
+    """{(epilogue, finalize, vectors per lane, chunk): symbol} of every row_kernel."""
+    out = {}
+    for m in re.finditer(r"<(_ZN3frn12_GLOBAL__N_110row_kernelILi(\d)ELi(\d)ELi(\d)ELi(\d+)EEEvNS_7RowArgsE)>:", dis):
+        out[tuple(int(g) for g in m.groups()[1:])] = m.group(1)
+    return out
+
+
+def test_row_kernel_epilogue_loads_nothing_after_its_first_store():
+    """row_kernel with two or four vectors per lane and a norm epilogue: no
+    vector load follows the first store.  A wave's vector memory operations
+    complete in issue order, so a gamma load behind a store would also wait
+    for the store; every gamma load goes out before the last row sum and
+    both outputs are stored after it.  With one vector per lane the last
+    gamma load does follow the residual_out store (one such wait, measured
+    faster there), and that layout is checked too."""
+    dis = _disassembly()
+    syms = _row_kernel_symbols(dis)
+    multi = {k: v for k, v in syms.items() if k[0] in (0, 1) and k[2] >= 2}
+    assert len(multi) >= 12, sorted(syms)
+    for key, sym in multi.items():
+        f = _function(dis, sym)
+        first_store = f.index("global_store")
+        assert not re.search(r"\b(global|buffer)_load", f[first_store:]), (key, sym)
+    one = {k: v for k, v in syms.items() if k[0] in (0, 1) and k[2] == 1}
+    assert one
+    for key, sym in one.items():
+        f = _function(dis, sym)
+        after = f[f.index("global_store"):]
+        assert re.search(r"\bglobal_load_dwordx4\b", after), (key, sym)
+
+
 # Register budgets the launch shapes were measured at: a SIMD holds
 # floor(512 / VGPRs) waves (VGPRs allocated in steps of 8), and a CU four
 # SIMDs.  (kernel symbol pattern, most VGPRs, why)
