@@ -73,12 +73,14 @@ __global__ __launch_bounds__(1024) void probe_rows_kernel(const ProbeArgs a) {
                 acc[j].w ^= q[c][j].w;
             }
     }
-    for (int d = 0; d < a.ndst; ++d)
+    // both destinations of a vector, then the next vector (the store order of
+    // the one-row kernel's epilogue)
 #pragma unroll
-        for (int j = 0; j < V; ++j) {
-            const bool write = MODE != 1 || (acc[j].x == 0x9E3779B9u && acc[j].y == 0x7F4A7C15u);
+    for (int j = 0; j < V; ++j) {
+        const bool write = MODE != 1 || (acc[j].x == 0x9E3779B9u && acc[j].y == 0x7F4A7C15u);
+        for (int d = 0; d < a.ndst; ++d)
             if (ok[j] && write) st_nt(a.dst[d] + row + vi[j], acc[j]);
-        }
+    }
 }
 
 template <int MODE>
