@@ -83,3 +83,20 @@ def test_random_shape_matches_oracle(case):
         torch.cuda.synchronize()
     parity.compare(f"random {_id(case)} out", workloads.bits(y), ref.y)
     parity.compare(f"random {_id(case)} residual_out", workloads.bits(x), ref.xout)
+
+
+# The same kind of shapes with a launch table that sends every call two (or
+# four) vectors per lane where they fit: the one-row kernel's epilogue with
+# several vectors per lane (every gamma load ahead of the first store) and
+# its ragged last vectors, at many H.
+FORCED = [(v, c) for v in (2, 4) for c in _cases(24, seed=6100 + v)]
+
+
+@pytest.mark.parametrize("vec,case", FORCED, ids=[f"v{v}_{_id(c)}" for v, c in FORCED])
+def test_random_shape_forced_vectors_matches_oracle(vec, case):
+    m = P.frn()
+    m.set_launch_table(f"* * * * 0 * {vec}\n")
+    try:
+        test_random_shape_matches_oracle(case)
+    finally:
+        m.set_launch_table(None)
