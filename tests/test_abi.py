@@ -874,7 +874,7 @@ def test_compiled_in_table_decides_its_shapes_by_default():
     assert os.environ.get("FRN_LAUNCH_TABLE") is None
     epis = {"rmsnorm": frn.EPI_RMSNORM, "sandwich": frn.EPI_SANDWICH, "sum": frn.EPI_SUM}
     rules = tuned_rules()
-    assert len({tuple(r[:4]) for r in rules}) >= 9      # the nine tuned shapes
+    assert len({tuple(r[:4]) for r in rules}) >= 20     # the twenty tuned shapes
     seen = set()
     for H, R, k, epi, lo, hi, v in rules:
         H, R, k = int(H), int(R), int(k)

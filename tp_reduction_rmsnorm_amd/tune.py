@@ -51,7 +51,12 @@ EPI = {"rmsnorm": frn.EPI_RMSNORM, "sandwich": frn.EPI_SANDWICH, "sum": frn.EPI_
        "ep-rmsnorm": frn.EPI_RMSNORM, "ep-sandwich": frn.EPI_SANDWICH}
 DEFAULT_SHAPES = [(5120, 4, 0, "sandwich"), (8192, 8, 0, "sandwich"), (512, 2, 0, "rmsnorm"),
                   (6144, 8, 0, "rmsnorm"), (6144, 8, 10, "rmsnorm"), (7168, 2, 8, "rmsnorm"),
-                  (7168, 2, 0, "rmsnorm"), (7168, 2, 8, "sum"), (6144, 8, 10, "ep-rmsnorm")]
+                  (7168, 2, 0, "rmsnorm"), (7168, 2, 8, "sum"), (6144, 8, 10, "ep-rmsnorm"),
+                  # residual + RMSNorm without finalize at common hidden sizes and TP degrees
+                  (4096, 2, 0, "rmsnorm"), (4096, 4, 0, "rmsnorm"), (4096, 8, 0, "rmsnorm"),
+                  (5120, 2, 0, "rmsnorm"), (5120, 4, 0, "rmsnorm"), (5120, 8, 0, "rmsnorm"),
+                  (7168, 4, 0, "rmsnorm"), (7168, 8, 0, "rmsnorm"),
+                  (8192, 2, 0, "rmsnorm"), (8192, 4, 0, "rmsnorm"), (8192, 8, 0, "rmsnorm")]
 DEFAULT_TOKENS = [1, 8, 64, 256, 512, 1024, 2048, 4096, 16384]
 DEFAULT_SPLIT_TOKENS = [1, 8, 16, 32, 48, 64, 96, 128, 160, 192, 224, 256]
 
@@ -228,10 +233,12 @@ def tune_shape(H, R, k, epi, tokens, calls, dev, log=print):
             frn.set_launch_table(f"{H} {R} {k} {epi} {T} {T} {vec}")
             times[vec] += graph_us(call, calls) / 2
         frn.set_launch_table(None)
-        best = pick(times, builtin_choice(H, R, k, epi, T))
+        hand = builtin_choice(H, R, k, epi, T)
+        best = pick(times, hand)
         rows.append((T, best, times))
         log(f"H={H} R={R} k={k} {epi} T={T}: " +
-            ", ".join(f"vec {v}: {us:.2f} us" for v, us in sorted(times.items())) + f" -> {best}")
+            ", ".join(f"vec {v}: {us:.2f} us" for v, us in sorted(times.items())) +
+            f" -> {best} (hand-fitted rule: {hand})")
         del call
         torch.cuda.empty_cache()
     return rows
