@@ -624,7 +624,9 @@ def test_launch_shape_builtin_rule(hand_fitted):
     assert frn.launch_shape(4, 0, 1024, 5120, S) == (192, 4)   # mid T: four vectors
     assert frn.launch_shape(4, 0, 4096, 5120, S) == (320, 2)   # large T
     assert frn.launch_shape(8, 0, 4096, 8192, S) == (256, 4)   # long rows: four up to 4096
-    assert frn.launch_shape(8, 0, 16384, 8192, S) == (512, 2)
+    assert frn.launch_shape(8, 0, 16384, 8192, S) == (1024, 1)  # beyond 4096: one vector
+    assert frn.launch_shape(2, 0, 16384, 16384, 0) == (1024, 2)  # ... up to 1024 lanes
+    assert frn.launch_shape(2, 0, 16384, 7168, frn.EPI_SUM) == (448, 2)  # not split pass 1
     assert frn.launch_shape(2, 8, 4096, 7168, 0) == (896, 1)   # finalize: one vector
     assert frn.launch_shape(2, 8, 1024, 7168, 0) == (448, 2)   # ... two at mid T for R <= 2
     assert frn.launch_shape(8, 10, 512, 6144, 0) == (384, 2)   # ... and up to 512 above
@@ -657,12 +659,20 @@ def test_pipelined_builtin_rule(hand_fitted):
     assert frn.launch_shape(4, 0, 1535, 5120, S) == (320, 2)   # one-row kernel, two vectors
     assert frn.launch_pipelined(1, 0, 16384, 7168, N)          # split pass 2
     assert frn.launch_shape(1, 0, 16384, 7168, N) == (448, 2)
-    assert not frn.launch_pipelined(2, 0, 16384, 7168, N)      # residual + RMSNorm: R = 1 only
+    assert not frn.launch_pipelined(2, 0, 16384, 7168, N)      # residual + RMSNorm R = 2: T <= 4096
+    assert frn.launch_pipelined(2, 0, 4096, 7168, N)
+    assert frn.launch_shape(2, 0, 4096, 7168, N) == (896, 1)
+    assert frn.launch_pipelined(2, 0, 1536, 8192, N)           # ... 512 to 1024 vectors, one each
+    assert frn.launch_shape(2, 0, 1536, 8192, N) == (1024, 1)
+    assert not frn.launch_pipelined(2, 0, 1535, 8192, N)
+    assert not frn.launch_pipelined(2, 0, 4096, 2048, N)       # 256 vectors
+    assert not frn.launch_pipelined(3, 0, 4096, 6144, N)       # residual + RMSNorm: R <= 2
     assert frn.launch_pipelined(2, 0, 2048, 6144, S)           # the sandwich at R = 2
     assert frn.launch_pipelined(3, 0, 2048, 6144, S)           # 768 vectors, R = 3
     assert frn.launch_shape(3, 0, 2048, 6144, S) == (384, 2)
     assert not frn.launch_pipelined(4, 0, 4096, 8192, S)       # 1024 vectors: one row per group
-    assert not frn.launch_pipelined(2, 0, 4096, 4096, N)       # 512 vectors: the same
+    assert not frn.launch_pipelined(4, 0, 4096, 4096, S)       # 512 vectors: the same
+    assert frn.launch_pipelined(2, 0, 4096, 4096, N)           # except residual + RMSNorm at R = 2
     assert not frn.launch_pipelined(8, 0, 4096, 8192, S)       # R > 4
     assert not frn.launch_pipelined(4, 10, 4096, 6144, N)      # finalize
     assert not frn.launch_pipelined(4, 0, 4096, 5128, S)       # 641 vectors: idle lanes

@@ -212,6 +212,12 @@ void load_tables_locked() {
 //    lanes except two for 256 < T <= 512: its work list is short per rank,
 //    and more tokens in flight per CU matter more (H=6144 R=8 k=10: T=4096
 //    131 against 145 us with two; T=512 21.1 against 20.4).
+//  - beyond T = 4096 without finalize, one vector per lane up to 1024 lanes:
+//    with the epilogue issuing every load before its first store, tune.py
+//    over the sixteen measured shapes without finalize put one vector within
+//    1% of the fastest one-row choice at T = 16384 in 14 of them, and ahead
+//    of two vectors by 1-5% at R = 8 (H=8192 sandwich: 469.6 against 493.8
+//    us; H=8192 R=8 residual + RMSNorm: 487.7 against 501.3).
 // Four vectors are never used with the finalize (too many live registers)
 // or for split pass 1 (it spills).
 int builtin_vec(int nvec, int fin, int64_t T, int epilogue, int R) {
@@ -229,6 +235,7 @@ int builtin_vec(int nvec, int fin, int64_t T, int epilogue, int R) {
         if (T <= 512) return nvec >= 1024 ? 4 : 2;
         if (T <= 1024 || (nvec >= 768 && T <= 4096)) return 4;
     }
+    if (epilogue != kStoreSum && T > 4096) return nvec <= 1024 ? 1 : 2;
     return nvec <= 512 ? 1 : 2;
 }
 
@@ -274,8 +281,21 @@ bool pipe_fits(int vec, int nvec, int fin, int epilogue, int R) {
 // vectors per lane fit the row in few waves (H=4096 R=2 T=1536-2048: 3-7%
 // behind; H=8192 R=4: 1-3% behind).  Returns the vec, or 0 for the one-row
 // kernel.
+//  Residual + RMSNorm at R = 2 is the exception, re-measured after the
+//  one-row kernel's epilogue began issuing every load before its first
+//  store: for 1536 <= T <= 4096 the row-pipelined kernel with one vector per
+//  lane beat the one-row kernel on all four shapes measured, rows of 512 to
+//  1024 vectors included (T=2048 / 4096: H=4096 16.3 / 29.1 against 16.9 /
+//  30.1 us, H=5120 19.8 / 36.0 against 20.8 / 36.9, H=7168 26.7 / 49.1
+//  against 27.0 / 50.0, H=8192 29.9 / 55.7 against 30.1 / 56.0) and lost at
+//  T=16384 (107.5 against 110.3 us at H=4096).
 int builtin_pipe_vec(int nvec, int fin, int64_t T, int epilogue, int R) {
-    if (T < 1536 || nvec <= 512 || nvec >= 1024) return 0;
+    if (T < 1536) return 0;
+    if (epilogue == kRmsNorm && R == 2) {
+        if (T > 4096 || nvec < 512 || nvec > 1024) return 0;
+        return pipe_fits(1, nvec, fin, epilogue, R) ? 1 : 0;
+    }
+    if (nvec <= 512 || nvec >= 1024) return 0;
     if (epilogue == kRmsNorm && R != 1) return 0;
     if (pipe_fits(2, nvec, fin, epilogue, R)) return 2;
     if (pipe_fits(1, nvec, fin, epilogue, R)) return 1;
