@@ -303,8 +303,9 @@ frn_status frn_query(int32_t R, int32_t k, int64_t T, int64_t H, int32_t epilogu
  * over to another (SGLang PR #34134: the shipped H=8192 profiles misfit
  * H=6144).  Three layers of rules decide, the first with a rule for the
  * call winning: the caller's table (this call, or FRN_LAUNCH_TABLE); the
- * table measured on MI355X for the shapes of the pages' workloads, which
- * the library carries compiled in; and a hand-fitted rule, also measured on
+ * table measured on MI355X for the shapes of the pages' workloads and for
+ * residual + RMSNorm at common hidden sizes and TP degrees, which the
+ * library carries compiled in; and a hand-fitted rule, also measured on
  * MI355X, for every other shape.  Table text: one rule per line, '#'
  * starts a comment:
  *     H  R  k  epilogue  Tmin  Tmax  vec
@@ -407,8 +408,10 @@ int32_t frn_split_rows(int32_t R, int32_t k, int64_t T, int64_t H, int32_t epilo
  * 64 KiB.  The compiled-in measured table decides the shapes it covers;
  * the hand-fitted rule, measured on MI355X,
  * takes it with two vectors per lane from T = 1536 for 4096 < H < 8192,
- * for the sandwich epilogue and for residual + RMSNorm at R = 1 (where it
- * measured faster or even); a caller's p1 / p2 and numeric vec rules
+ * for the sandwich epilogue and for residual + RMSNorm at R = 1, and with
+ * one vector per lane for 1536 <= T <= 4096 and 4096 <= H <= 8192 for
+ * residual + RMSNorm at R = 2 (where it measured faster or even); a
+ * caller's p1 / p2 and numeric vec rules
  * override both.  Results are bit-identical either way: the same
  * arithmetic in the same order, row by row.
  */
