@@ -10,7 +10,8 @@
 // issues all loads of a chunk -- of ranks, of one rank's top-k slots, or
 // (expert-parallel routing) of the token's live rows across ranks -- before
 // it consumes any of them, keeps the FP32 row slice in registers through the
-// epilogue, and writes each output exactly once.
+// epilogue, and writes each output exactly once; with two or four vectors
+// per lane no load follows its first store (see epilogue).
 //
 // rows_pipelined_kernel: for calls without finalize at large T.  One
 // workgroup per compute unit walks rows b, b + G, b + 2G, ...; the gamma
