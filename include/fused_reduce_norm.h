@@ -408,7 +408,8 @@ int32_t frn_split_rows(int32_t R, int32_t k, int64_t T, int64_t H, int32_t epilo
  * 64 KiB.  The compiled-in measured table decides the shapes it covers;
  * the hand-fitted rule, measured on MI355X,
  * takes it with two vectors per lane from T = 1536 for 4096 < H < 8192,
- * for the sandwich epilogue and for residual + RMSNorm at R = 1, and with
+ * for the sandwich epilogue (at R >= 3 and H >= 6144 up to T = 4096) and
+ * for residual + RMSNorm at R = 1, and with
  * one vector per lane for 1536 <= T <= 4096 and 4096 <= H <= 8192 for
  * residual + RMSNorm at R = 2 (where it measured faster or even); a
  * caller's p1 / p2 and numeric vec rules

@@ -670,6 +670,11 @@ def test_pipelined_builtin_rule(hand_fitted):
     assert frn.launch_pipelined(2, 0, 2048, 6144, S)           # the sandwich at R = 2
     assert frn.launch_pipelined(3, 0, 2048, 6144, S)           # 768 vectors, R = 3
     assert frn.launch_shape(3, 0, 2048, 6144, S) == (384, 2)
+    assert frn.launch_pipelined(4, 0, 4096, 6144, S)           # R >= 3, 768+ vectors: up to 4096
+    assert not frn.launch_pipelined(4, 0, 4097, 6144, S)
+    assert frn.launch_shape(4, 0, 8192, 6144, S) == (768, 1)
+    assert frn.launch_pipelined(2, 0, 16384, 6144, S)          # R = 2: all T
+    assert frn.launch_pipelined(4, 0, 16384, 5120, S)          # 640 vectors: all T
     assert not frn.launch_pipelined(4, 0, 4096, 8192, S)       # 1024 vectors: one row per group
     assert not frn.launch_pipelined(4, 0, 4096, 4096, S)       # 512 vectors: the same
     assert frn.launch_pipelined(2, 0, 4096, 4096, N)           # except residual + RMSNorm at R = 2

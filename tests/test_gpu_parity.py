@@ -277,7 +277,9 @@ def test_deterministic_across_runs():
 
 
 def test_in_place_residual():
-    for cid, T in ((2, 33), (4, 5)):
+    # one, two and four vectors per lane (the last two store residual_out
+    # after every load of the row), and the split-row finalize
+    for cid, T in ((2, 33), (3, 33), (2, 600), (4, 5)):
         inp = workloads.make_workload(cid, T)
         ref = oracle_ref(inp)
         d = to_dev(inp)

@@ -289,6 +289,12 @@ bool pipe_fits(int vec, int nvec, int fin, int epilogue, int R) {
 //  30.1 us, H=5120 19.8 / 36.0 against 20.8 / 36.9, H=7168 26.7 / 49.1
 //  against 27.0 / 50.0, H=8192 29.9 / 55.7 against 30.1 / 56.0) and lost at
 //  T=16384 (107.5 against 110.3 us at H=4096).
+//  The sandwich at R >= 3 on rows of 768+ vectors stops at T = 4096: at
+//  R = 4 it lost from T = 8192 on both shapes measured (H=6144: T=8192 121.4
+//  against 116.9 us, T=16384 245.3 against 227.1; H=7168: 137.7 against
+//  135.0, 281.4 against 267.2), while at R = 2, and at H=5120 R=4, it won
+//  through T = 16384 (H=7168 R=2: 196.0 against 197.9 us; H=5120 R=4: 186.6
+//  against 190.7).
 int builtin_pipe_vec(int nvec, int fin, int64_t T, int epilogue, int R) {
     if (T < 1536) return 0;
     if (epilogue == kRmsNorm && R == 2) {
@@ -297,6 +303,7 @@ int builtin_pipe_vec(int nvec, int fin, int64_t T, int epilogue, int R) {
     }
     if (nvec <= 512 || nvec >= 1024) return 0;
     if (epilogue == kRmsNorm && R != 1) return 0;
+    if (epilogue == kSandwich && R >= 3 && nvec >= 768 && T > 4096) return 0;
     if (pipe_fits(2, nvec, fin, epilogue, R)) return 2;
     if (pipe_fits(1, nvec, fin, epilogue, R)) return 1;
     return 0;
