@@ -187,8 +187,8 @@ void load_tables_locked() {
 }
 
 // The hand-fitted rule, from graph-replay sweeps on MI355X (the sandwich
-// workloads by hand, then tune.py over nine shapes with inputs rotated over
-// 1 GiB, the disputed cells A/B/B/A-interleaved):
+// workloads by hand, then tune.py over nine and later twenty shapes with
+// inputs rotated over 1 GiB, the disputed cells A/B/B/A-interleaved):
 //  - small T (T <= 256, latency-bound): one vector per lane up to 896
 //    lanes, else two -- more lanes issue the row's loads at once (H=6144
 //    R=8 T=1: 3.8 us with one vector, 4.2 with two; H=5120 T=64: 5.0
